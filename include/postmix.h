@@ -1,0 +1,149 @@
+/*
+ * postmix.h -- C ABI of the fused inverse-RoPE + VHA postmix library for
+ * AMD Instinct MI355X (gfx950).  Library: libpostmix.so.
+ *
+ * The operation (PaddleFleet PR #1772, "Fuse HCA inverse RoPE into the VHA
+ * postmix, and the sparse-attention KV index remap", PR body item 1 and the
+ * description's part 一):  the HCA layer undoes the rotary position embedding
+ * (RoPE) on the trailing pe channels of each head of the attention output O
+ * and feeds the result to the ungrouped VHA postmix, an [nh,nh] matrix that
+ * mixes heads.  Because the rotation acts on channels only and the mix
+ * contracts heads, the channel axis is a pure N dimension and the two commute;
+ * this library never materialises inv_rope(O).
+ *
+ *   forward        Y[s,g,c]  = sum_h W[g,h] * inv_rope(O)[s,h,c]
+ *   input grad     dO[s,h,:] = rope( sum_g W[g,h] * dY[s,g,:] )
+ *   weight grad    dW[g,h]   = sum_s sum_c dY[s,g,c] * inv_rope(O)[s,h,c]
+ *                  (the pages' dM[h,h'] = sum_{t,c} dOut[t,h,c]*O_roped[t,h',c])
+ *
+ * RoPE convention (a reading; the pages name RoPE but do not print it):
+ * rotate-half pairs (nope+i, nope+pe/2+i), i < pe/2, angle
+ * phi = position * theta^(-2i/pe).  rope turns each pair by +phi:
+ *   (a, b) -> (a cos - b sin, b cos + a sin);  inv_rope turns it by -phi.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - bf16 tensors are passed as raw bfloat16 bit patterns (uint16_t).
+ *  - Activations O, Y, dY, dO: [sq, nh, nope+pe], row-major, channel fastest,
+ *    the pe channels trailing each head.  Batch is folded into sq.
+ *  - W, dW: [nh, nh] row-major, W[g,h] with g the OUTPUT head (matmul(M, X)).
+ *  - rope_cos, rope_sin: fp32 [table_rows, pe/2]; row r holds position r.
+ *  - positions: int32 [sq]; row s of O uses table row positions[s].  Values
+ *    outside [0, table_rows) are clamped on the device (never read out of
+ *    bounds); callers must not rely on clamping.
+ *  - All pointers are DEVICE pointers, owned by the caller.  The library
+ *    allocates, frees and synchronises nothing; work is enqueued on `stream`
+ *    (a hipStream_t; NULL = the null stream) and the call returns at once.
+ *  - Outputs are overwritten, never accumulated.  Inputs are not modified.
+ *    In-place operation is not supported: an output range that overlaps an
+ *    input range is rejected.
+ *  - Limits: 1 <= nh <= 128; nope >= 0 with nope % 8 == 0; pe >= 0 with
+ *    pe % 16 == 0; nope + pe > 0; sq >= 0.  sq == 0 is a successful no-op.
+ *  - Activation, table and workspace pointers must be 16-byte aligned.
+ *  - Return 0 on success, else a negative PM_ERR_* code; a thread-local
+ *    message naming the offending argument is available from
+ *    postmix_last_error().  Arguments are validated before any HIP call.
+ *  - Calls are reentrant.  Concurrent bwd_dw calls need distinct workspaces.
+ */
+#ifndef POSTMIX_H
+#define POSTMIX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t pm_bf16;
+
+enum {
+    PM_OK = 0,
+    PM_ERR_NULL = -1,      /* a required pointer is NULL                      */
+    PM_ERR_SHAPE = -2,     /* sizes outside the limits above                  */
+    PM_ERR_ALIGN = -3,     /* a pointer is not 16-byte aligned                */
+    PM_ERR_OVERLAP = -4,   /* an output overlaps an input                     */
+    PM_ERR_WORKSPACE = -5, /* workspace smaller than postmix_bwd_dw_workspace_bytes */
+    PM_ERR_DEVICE = -6,    /* current device is not gfx950                    */
+    PM_ERR_HIP = -7        /* a HIP runtime or launch error                   */
+};
+
+/*
+ * Forward.  Y = inv_rope(W . O) per token, which equals W . inv_rope(O)
+ * (PR #1772 body item 1: the nope columns are mixed directly; the pe columns
+ * are rotated after the mix, in fp32 registers).  bf16 in, fp32 accumulate,
+ * bf16 (round-to-nearest-even) out.
+ *   O         [sq, nh, nope+pe] bf16, read
+ *   W         [nh, nh] bf16, read
+ *   rope_cos, rope_sin  [table_rows, pe/2] fp32, read (may be NULL if pe == 0)
+ *   positions [sq] int32, read (may be NULL if pe == 0)
+ *   Y         [sq, nh, nope+pe] bf16, written
+ */
+int postmix_fwd(const pm_bf16 *O, const pm_bf16 *W, const float *rope_cos,
+                const float *rope_sin, int64_t table_rows,
+                const int32_t *positions, int64_t sq, int32_t nh, int32_t nope,
+                int32_t pe, pm_bf16 *Y, void *stream);
+
+/*
+ * Backward, input gradient.  dO = rope(W^T . dY) per token: the gradient of
+ * the head mix (PR #1772, follow-up commit: the backward hands the gradient
+ * through the GEMM's matmul_grad and then the RoPE backward), with the
+ * transposed (+phi) rotation applied in fp32 registers.
+ *   dY [sq, nh, nope+pe] bf16, read;  dO [sq, nh, nope+pe] bf16, written.
+ *   Other arguments as postmix_fwd.
+ */
+int postmix_bwd_dx(const pm_bf16 *dY, const pm_bf16 *W, const float *rope_cos,
+                   const float *rope_sin, int64_t table_rows,
+                   const int32_t *positions, int64_t sq, int32_t nh,
+                   int32_t nope, int32_t pe, pm_bf16 *dO, void *stream);
+
+/*
+ * Bytes of device workspace postmix_bwd_dw needs for this shape (a multiple
+ * of 256).  Depends on (sq, nh, nope, pe) only.  Returns 0 for sq == 0 and
+ * for shapes outside the limits.
+ */
+size_t postmix_bwd_dw_workspace_bytes(int64_t sq, int32_t nh, int32_t nope,
+                                      int32_t pe);
+
+/*
+ * Backward, weight gradient.  dW[g,h] = sum over tokens s and channels c of
+ * dY[s,g,c] * inv_rope(O)[s,h,c] (PR #1772 description part 一: the weight
+ * gradient contracts the full channel axis and cannot be split).
+ * Deterministic: fixed-size token blocks (a function of the shape only) each
+ * produce an fp32 partial; the partials are summed in a fixed pairwise tree.
+ * No atomics; repeated calls give bitwise-identical dW (the atomic-free
+ * principle of PaddleFleet PR #1776, "deterministic TileLang backend for
+ * absorbed-MQA sparse backward").  The rotated pe operand is split into a
+ * bf16 high part and a bf16 low correction (the compensated product of
+ * tilelang-ascend PR #1640), both accumulated in fp32.
+ *   dY, O     [sq, nh, nope+pe] bf16, read
+ *   dW        [nh, nh] fp32, written
+ *   workspace device scratch of workspace_bytes >= postmix_bwd_dw_workspace_bytes;
+ *             clobbered.  May be NULL when that size is 0.
+ */
+int postmix_bwd_dw(const pm_bf16 *dY, const pm_bf16 *O, const float *rope_cos,
+                   const float *rope_sin, int64_t table_rows,
+                   const int32_t *positions, int64_t sq, int32_t nh,
+                   int32_t nope, int32_t pe, float *dW, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/*
+ * RoPE tables from theta: row r (position r), column i < pe/2:
+ *   cos_out[r, i] = cos(r * theta^(-2i/pe)),  sin_out likewise,
+ * with the angle formed and evaluated in fp64, then rounded to fp32.
+ * cos_out, sin_out: [table_rows, pe/2] fp32 device buffers, written.
+ */
+int postmix_rope_table(double theta, int32_t pe, int64_t table_rows,
+                       float *cos_out, float *sin_out, void *stream);
+
+/* Static text for a PM_* code. */
+const char *postmix_status_string(int status);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char *postmix_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POSTMIX_H */

@@ -1,0 +1,303 @@
+// postmix_api.hip -- the C ABI declared in include/postmix.h: argument
+// validation (done before any HIP call), device checks and kernel launches on
+// the caller's stream.  The library never allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/postmix.h"
+#include "postmix_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return PM_OK;
+}
+
+// ---- per-device facts (queried once per device) ---------------------------
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_dev_cus[kMaxDevices];
+
+int check_device(int* n_cu) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PM_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(PM_ERR_DEVICE, "device index %d out of range", dev);
+    int state = g_dev_state[dev].load(std::memory_order_acquire);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(PM_ERR_HIP, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+        const bool is950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        g_dev_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1,
+                             std::memory_order_relaxed);
+        state = is950 ? 1 : 2;
+        g_dev_state[dev].store(state, std::memory_order_release);
+        if (!is950)
+            return fail(PM_ERR_DEVICE, "device %d is %s; this library is built for gfx950 only", dev,
+                        prop.gcnArchName);
+    }
+    if (state != 1) return fail(PM_ERR_DEVICE, "device %d is not gfx950", dev);
+    *n_cu = g_dev_cus[dev].load(std::memory_order_relaxed);
+    return PM_OK;
+}
+
+// ---- argument checks --------------------------------------------------------
+
+int check_shape(int64_t sq, int32_t nh, int32_t nope, int32_t pe) {
+    if (sq < 0) return fail(PM_ERR_SHAPE, "sq must be >= 0 (got %lld)", (long long)sq);
+    if (nh < 1 || nh > 128) return fail(PM_ERR_SHAPE, "nh must be in [1, 128] (got %d)", nh);
+    if (nope < 0 || nope % 8 != 0)
+        return fail(PM_ERR_SHAPE, "nope must be >= 0 and a multiple of 8 (got %d)", nope);
+    if (pe < 0 || pe % 16 != 0)
+        return fail(PM_ERR_SHAPE, "pe must be >= 0 and a multiple of 16 (got %d)", pe);
+    if (nope + pe <= 0) return fail(PM_ERR_SHAPE, "nope + pe must be > 0");
+    // element offsets stay well inside int64 and the grid inside 2^31 items
+    if (sq > ((int64_t)1 << 40) / ((int64_t)nh * (nope + pe)))
+        return fail(PM_ERR_SHAPE, "sq=%lld too large for nh=%d, d=%d", (long long)sq, nh, nope + pe);
+    return PM_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+    const char* name;
+    const void* p;
+    size_t bytes;
+};
+
+bool overlaps(const Range& a, const Range& b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + a.bytes;
+    const uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + b.bytes;
+    return a0 < b1 && b0 < a1;
+}
+
+int check_no_overlap(const Range* outs, int n_out, const Range* ins, int n_in) {
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = 0; j < n_in; ++j)
+            if (overlaps(outs[i], ins[j]))
+                return fail(PM_ERR_OVERLAP, "output %s overlaps input %s (in-place is not supported)",
+                            outs[i].name, ins[j].name);
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(PM_ERR_OVERLAP, "output %s overlaps %s", outs[i].name, outs[j].name);
+    }
+    return PM_OK;
+}
+
+// Checks shared by the forward and the input gradient.
+int check_rope_args(const float* rope_cos, const float* rope_sin, int64_t table_rows,
+                    const int32_t* positions, int32_t pe) {
+    if (pe == 0) return PM_OK;
+    if (!rope_cos) return fail(PM_ERR_NULL, "rope_cos is NULL");
+    if (!rope_sin) return fail(PM_ERR_NULL, "rope_sin is NULL");
+    if (!positions) return fail(PM_ERR_NULL, "positions is NULL");
+    if (table_rows < 1) return fail(PM_ERR_SHAPE, "table_rows must be >= 1 when pe > 0");
+    if (!aligned16(rope_cos)) return fail(PM_ERR_ALIGN, "rope_cos is not 16-byte aligned");
+    if (!aligned16(rope_sin)) return fail(PM_ERR_ALIGN, "rope_sin is not 16-byte aligned");
+    if (((uintptr_t)positions & 3u) != 0) return fail(PM_ERR_ALIGN, "positions is not 4-byte aligned");
+    return PM_OK;
+}
+
+int mix_common(const char* xname, const pm_bf16* X, const pm_bf16* W, const float* rope_cos,
+               const float* rope_sin, int64_t table_rows, const int32_t* positions, int64_t sq,
+               int32_t nh, int32_t nope, int32_t pe, const char* oname, pm_bf16* Out, void* stream,
+               bool dx) {
+    int rc = check_shape(sq, nh, nope, pe);
+    if (rc) return rc;
+    if (sq == 0) return ok();
+    if (!X) return fail(PM_ERR_NULL, "%s is NULL", xname);
+    if (!W) return fail(PM_ERR_NULL, "W is NULL");
+    if (!Out) return fail(PM_ERR_NULL, "%s is NULL", oname);
+    rc = check_rope_args(rope_cos, rope_sin, table_rows, positions, pe);
+    if (rc) return rc;
+    if (!aligned16(X)) return fail(PM_ERR_ALIGN, "%s is not 16-byte aligned", xname);
+    if (!aligned16(Out)) return fail(PM_ERR_ALIGN, "%s is not 16-byte aligned", oname);
+    if (((uintptr_t)W & 1u) != 0) return fail(PM_ERR_ALIGN, "W is not 2-byte aligned");
+    const size_t act = (size_t)sq * nh * (nope + pe) * sizeof(pm_bf16);
+    const size_t tab = pe ? (size_t)table_rows * (pe / 2) * sizeof(float) : 0;
+    const Range outs[1] = {{oname, Out, act}};
+    const Range ins[5] = {{xname, X, act},
+                          {"W", W, (size_t)nh * nh * sizeof(pm_bf16)},
+                          {"rope_cos", pe ? rope_cos : nullptr, tab},
+                          {"rope_sin", pe ? rope_sin : nullptr, tab},
+                          {"positions", pe ? positions : nullptr, (size_t)sq * sizeof(int32_t)}};
+    rc = check_no_overlap(outs, 1, ins, 5);
+    if (rc) return rc;
+    int n_cu = 0;
+    rc = check_device(&n_cu);
+    if (rc) return rc;
+    pm::MixArgs a;
+    a.X = X;
+    a.W = W;
+    a.rcos = rope_cos;
+    a.rsin = rope_sin;
+    a.table_rows = table_rows;
+    a.positions = positions;
+    a.sq = sq;
+    a.nh = nh;
+    a.nope = nope;
+    a.pe = pe;
+    a.Out = Out;
+    a.n_cu = n_cu;
+    a.waves_per_cu = 16;
+    hipError_t e = pm::launch_mix(a, dx, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+__global__ void zero_fill_kernel(float* p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int postmix_fwd(const pm_bf16* O, const pm_bf16* W, const float* rope_cos, const float* rope_sin,
+                int64_t table_rows, const int32_t* positions, int64_t sq, int32_t nh, int32_t nope,
+                int32_t pe, pm_bf16* Y, void* stream) {
+    return mix_common("O", O, W, rope_cos, rope_sin, table_rows, positions, sq, nh, nope, pe, "Y",
+                      Y, stream, false);
+}
+
+int postmix_bwd_dx(const pm_bf16* dY, const pm_bf16* W, const float* rope_cos,
+                   const float* rope_sin, int64_t table_rows, const int32_t* positions, int64_t sq,
+                   int32_t nh, int32_t nope, int32_t pe, pm_bf16* dO, void* stream) {
+    return mix_common("dY", dY, W, rope_cos, rope_sin, table_rows, positions, sq, nh, nope, pe,
+                      "dO", dO, stream, true);
+}
+
+size_t postmix_bwd_dw_workspace_bytes(int64_t sq, int32_t nh, int32_t nope, int32_t pe) {
+    char saved[sizeof g_last_error];
+    memcpy(saved, g_last_error, sizeof saved);
+    const int rc = check_shape(sq, nh, nope, pe);
+    memcpy(g_last_error, saved, sizeof saved);  // a size query leaves the message alone
+    if (rc || sq == 0) return 0;
+    const size_t bytes = (size_t)pm::dw_num_blocks(sq, nh) * nh * nh * sizeof(float);
+    return (bytes + 255) / 256 * 256;
+}
+
+int postmix_bwd_dw(const pm_bf16* dY, const pm_bf16* O, const float* rope_cos,
+                   const float* rope_sin, int64_t table_rows, const int32_t* positions, int64_t sq,
+                   int32_t nh, int32_t nope, int32_t pe, float* dW, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    int rc = check_shape(sq, nh, nope, pe);
+    if (rc) return rc;
+    if (!dW) return fail(PM_ERR_NULL, "dW is NULL");
+    if (((uintptr_t)dW & 3u) != 0) return fail(PM_ERR_ALIGN, "dW is not 4-byte aligned");
+    const size_t wbytes = (size_t)nh * nh * sizeof(float);
+    if (sq == 0) {
+        // an empty sum: dW = 0
+        int n_cu = 0;
+        rc = check_device(&n_cu);
+        if (rc) return rc;
+        const int64_t n = (int64_t)nh * nh;
+        hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                           (hipStream_t)stream, dW, n);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(PM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+        return ok();
+    }
+    if (!dY) return fail(PM_ERR_NULL, "dY is NULL");
+    if (!O) return fail(PM_ERR_NULL, "O is NULL");
+    rc = check_rope_args(rope_cos, rope_sin, table_rows, positions, pe);
+    if (rc) return rc;
+    if (!aligned16(dY)) return fail(PM_ERR_ALIGN, "dY is not 16-byte aligned");
+    if (!aligned16(O)) return fail(PM_ERR_ALIGN, "O is not 16-byte aligned");
+    const size_t need = postmix_bwd_dw_workspace_bytes(sq, nh, nope, pe);
+    if (need > 0 && !workspace) return fail(PM_ERR_NULL, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+        return fail(PM_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(PM_ERR_ALIGN, "workspace is not 16-byte aligned");
+    const size_t act = (size_t)sq * nh * (nope + pe) * sizeof(pm_bf16);
+    const size_t tab = pe ? (size_t)table_rows * (pe / 2) * sizeof(float) : 0;
+    const Range outs[2] = {{"dW", dW, wbytes}, {"workspace", workspace, need}};
+    const Range ins[5] = {{"dY", dY, act},
+                          {"O", O, act},
+                          {"rope_cos", pe ? rope_cos : nullptr, tab},
+                          {"rope_sin", pe ? rope_sin : nullptr, tab},
+                          {"positions", pe ? positions : nullptr, (size_t)sq * sizeof(int32_t)}};
+    rc = check_no_overlap(outs, 2, ins, 5);
+    if (rc) return rc;
+    int n_cu = 0;
+    rc = check_device(&n_cu);
+    if (rc) return rc;
+    pm::DwArgs a;
+    a.dY = dY;
+    a.O = O;
+    a.rcos = rope_cos;
+    a.rsin = rope_sin;
+    a.table_rows = table_rows;
+    a.positions = positions;
+    a.sq = sq;
+    a.nh = nh;
+    a.nope = nope;
+    a.pe = pe;
+    a.dW = dW;
+    a.partials = (float*)workspace;
+    hipError_t e = pm::launch_dw(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int postmix_rope_table(double theta, int32_t pe, int64_t table_rows, float* cos_out,
+                       float* sin_out, void* stream) {
+    if (!(theta > 0.0)) return fail(PM_ERR_SHAPE, "theta must be > 0");
+    if (pe <= 0 || pe % 16 != 0) return fail(PM_ERR_SHAPE, "pe must be a positive multiple of 16 (got %d)", pe);
+    if (table_rows < 0) return fail(PM_ERR_SHAPE, "table_rows must be >= 0");
+    if (table_rows == 0) return ok();
+    if (!cos_out) return fail(PM_ERR_NULL, "cos_out is NULL");
+    if (!sin_out) return fail(PM_ERR_NULL, "sin_out is NULL");
+    if (!aligned16(cos_out)) return fail(PM_ERR_ALIGN, "cos_out is not 16-byte aligned");
+    if (!aligned16(sin_out)) return fail(PM_ERR_ALIGN, "sin_out is not 16-byte aligned");
+    const size_t tab = (size_t)table_rows * (pe / 2) * sizeof(float);
+    const Range outs[2] = {{"cos_out", cos_out, tab}, {"sin_out", sin_out, tab}};
+    int rc = check_no_overlap(outs, 2, nullptr, 0);
+    if (rc) return rc;
+    int n_cu = 0;
+    rc = check_device(&n_cu);
+    if (rc) return rc;
+    hipError_t e = pm::launch_rope_table(theta, pe, table_rows, cos_out, sin_out, n_cu,
+                                         (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+const char* postmix_status_string(int status) {
+    switch (status) {
+        case PM_OK: return "ok";
+        case PM_ERR_NULL: return "null pointer";
+        case PM_ERR_SHAPE: return "bad shape";
+        case PM_ERR_ALIGN: return "misaligned pointer";
+        case PM_ERR_OVERLAP: return "output overlaps input";
+        case PM_ERR_WORKSPACE: return "workspace too small";
+        case PM_ERR_DEVICE: return "device is not gfx950";
+        case PM_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* postmix_last_error(void) { return g_last_error; }
+
+}  // extern "C"

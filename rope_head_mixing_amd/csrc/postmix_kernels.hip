@@ -1,0 +1,619 @@
+// postmix_kernels.hip -- gfx950 (MI355X) kernels for the fused inverse-RoPE +
+// VHA postmix (PaddleFleet PR #1772, "Fuse HCA inverse RoPE into the VHA
+// postmix, and the sparse-attention KV index remap", PR body item 1).
+//
+// Shapes: activations [sq, nh, d] bf16 with d = nope + pe, channel fastest;
+// W [nh, nh] bf16 with W[g,h], g the output head; RoPE tables fp32
+// [rows, pe/2]; positions int32 [sq].
+//
+// MFMA used throughout: v_mfma_f32_32x32x16_bf16 (wave64).
+//   A operand: lane l supplies row (l % 32) and 8 k-values.
+//   B operand: lane l supplies column (l % 32) and 8 k-values.
+//   D (16 fp32 per lane): register r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
+//   column l % 32.
+// The products are summed over k, so which 8 k-values sit in which lane half
+// only has to agree between A and B; the kernels assign k freely.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "postmix_launch.h"
+
+namespace pm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// scalar helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) {
+    return (lo16 & 0xffffu) | (hi16 << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ int64_t table_row(const int32_t* positions, int64_t s,
+                                             int64_t table_rows) {
+    int64_t p = positions[s];
+    p = p < 0 ? 0 : p;
+    return p >= table_rows ? table_rows - 1 : p;
+}
+
+// ---------------------------------------------------------------------------
+// channel groups
+//
+// Channels are handled in groups of 8 (one 16-byte vector).  A "unit" is two
+// groups that one MFMA lane half owns together (slot 0 and slot 1):
+//   nope units u < NU:   slot s covers channels 16u + 8s .. +8 (valid if < nope)
+//   pe units u = NU + t: slot 0 covers nope + 8t .. +8 (first rotation half),
+//                        slot 1 covers nope + pe/2 + 8t .. +8 (its partners).
+// So a rotation partner always sits in the same lane, register r <-> r + 8.
+// ---------------------------------------------------------------------------
+
+struct ChanMap {
+    int nope, h2, nu_nope, n_units;
+    __device__ __forceinline__ ChanMap(int nope_, int pe_) {
+        nope = nope_;
+        h2 = pe_ >> 1;
+        nu_nope = (nope_ + 15) >> 4;
+        n_units = nu_nope + (h2 >> 3);
+    }
+    // first channel of (unit, slot), or -1 for padding
+    __device__ __forceinline__ int base(int u, int slot) const {
+        if (u < nu_nope) {
+            int c = 16 * u + 8 * slot;
+            return c < nope ? c : -1;
+        }
+        if (u < n_units) return nope + 8 * (u - nu_nope) + slot * h2;
+        return -1;
+    }
+    __device__ __forceinline__ bool is_pe(int u) const { return u >= nu_nope && u < n_units; }
+};
+
+// ---------------------------------------------------------------------------
+// head-mix kernel (forward and input gradient)
+//
+//   forward:  Y[s,g,:]  = inv_rope( sum_h W[g,h] X[s,h,:] ),   X = O
+//   dx:       dO[s,h,:] = rope    ( sum_g W[g,h] X[s,g,:] ),   X = dY
+//
+// One wave per workgroup; the workgroup strides over work items.  A work item
+// is one token s and MPI M-blocks (each M-block = 2 units = 32 channels).  Its
+// [NHP x 32*MPI] tile of X is loaded with coalesced 16-byte loads (prefetched
+// one item ahead in registers), staged in LDS, and read back transposed into
+// MFMA A fragments (rows = channels, k = heads).  W^T (or W for dx) is the B
+// operand, held in registers for the whole kernel.  The fp32 accumulators of
+// the pe units are rotated in registers, rounded to bf16 and stored as
+// 16-byte vectors.
+// ---------------------------------------------------------------------------
+
+template <int NHP, int MPI, bool DX>
+__global__ __launch_bounds__(64) void mix_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+    const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
+    const int32_t* __restrict__ positions, int nh, int nope, int pe,
+    uint16_t* __restrict__ Out, int64_t total_items, int items_per_token) {
+    constexpr int KB = NHP / 16;            // k-blocks of 16 heads
+    constexpr int NB = (NHP + 31) / 32;     // output blocks of 32 heads
+    constexpr int GPI = 4 * MPI;            // channel groups per item
+    constexpr int PITCH = GPI * 8 + 8;      // LDS row pitch (bf16), 16 B pad
+    constexpr int LOADS = NHP * GPI / 64;   // 16-byte loads per lane per item
+    static_assert(NHP % 16 == 0 && (NHP * GPI) % 64 == 0, "tile shape");
+    __shared__ __attribute__((aligned(16))) uint16_t lds[NHP * PITCH];
+
+    const int lane = threadIdx.x;
+    const int d = nope + pe;
+    const ChanMap cm(nope, pe);
+
+    // B operand (k = contracted head, n = output head), all of W in registers.
+    bf16x8 wf[KB][NB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int n = 32 * nb + (lane & 31);
+            u32x4 v;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                uint32_t two[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int k = 16 * kb + 8 * (lane >> 5) + 2 * jj + e;
+                    const int g = DX ? k : n;  // row of W (output head of the forward)
+                    const int h = DX ? n : k;  // column of W
+                    two[e] = (g < nh && h < nh) ? (uint32_t)W[g * nh + h] : 0u;
+                }
+                v[jj] = pack2(two[0], two[1]);
+            }
+            wf[kb][nb] = as_bf16x8(v);
+        }
+
+    // A-fragment geometry: lane supplies logical row m = lane % 32, which the
+    // D layout places in lane half Q, register r; map it to (group, element).
+    const int m = lane & 31;
+    const int aQ = (m & 7) >> 2;
+    const int ar = 4 * (m >> 3) + (m & 3);
+    const int a_col = (aQ * 2 + (ar >> 3)) * 8 + (ar & 7);  // within an M-block
+    const int a_h0 = 8 * (lane >> 5);
+
+    u32x4 buf[LOADS];
+
+    auto load_item = [&](int64_t item) {
+        const int64_t s = item / items_per_token;
+        const int mb0 = (int)(item - s * items_per_token) * MPI;
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            const int idx = j * 64 + lane;
+            const int h = idx / GPI;
+            const int grp = idx % GPI;
+            const int u = 2 * (mb0 + grp / 4) + ((grp >> 1) & 1);
+            const int c = cm.base(u, grp & 1);
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (h < nh && c >= 0)
+                v = *reinterpret_cast<const u32x4*>(X + ((s * nh + h) * (int64_t)d + c));
+            buf[j] = v;
+        }
+    };
+
+    int64_t item = blockIdx.x;
+    if (item < total_items) load_item(item);
+
+    for (; item < total_items; item += gridDim.x) {
+        const int64_t s = item / items_per_token;
+        const int mb0 = (int)(item - s * items_per_token) * MPI;
+
+        __syncthreads();  // the previous item's LDS reads are complete
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            const int idx = j * 64 + lane;
+            *reinterpret_cast<u32x4*>(&lds[(idx / GPI) * PITCH + (idx % GPI) * 8]) = buf[j];
+        }
+        __syncthreads();
+
+        const int64_t next = item + gridDim.x;
+        if (next < total_items) load_item(next);  // in flight during the compute
+
+        int64_t prow = 0;
+        if (pe > 0) prow = table_row(positions, s, table_rows);
+
+#pragma unroll
+        for (int mbl = 0; mbl < MPI; ++mbl) {
+            f32x16 acc[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[nb][r] = 0.0f;
+
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int h0 = 16 * kb + a_h0;
+                const uint16_t* p = &lds[h0 * PITCH + mbl * 32 + a_col];
+                u32x4 v;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    v[jj] = pack2(p[(2 * jj) * PITCH], p[(2 * jj + 1) * PITCH]);
+                const bf16x8 af = as_bf16x8(v);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wf[kb][nb], acc[nb], 0, 0, 0);
+            }
+
+            // epilogue: lane half Q owns unit u; registers 0..7 = slot 0, 8..15 = slot 1
+            const int Q = lane >> 5;
+            const int u = 2 * (mb0 + mbl) + Q;
+            const int c0 = cm.base(u, 0), c1 = cm.base(u, 1);
+            float cs[8], sn[8];
+            const bool rot = cm.is_pe(u);
+            if (rot) {
+                const int i0 = 8 * (u - cm.nu_nope);
+                const f32x4* pc = reinterpret_cast<const f32x4*>(rcos + prow * cm.h2 + i0);
+                const f32x4* ps = reinterpret_cast<const f32x4*>(rsin + prow * cm.h2 + i0);
+                const f32x4 ca = pc[0], cb = pc[1], sa = ps[0], sb = ps[1];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    cs[e] = ca[e]; cs[4 + e] = cb[e];
+                    sn[e] = sa[e]; sn[4 + e] = sb[e];
+                }
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int row = 32 * nb + (lane & 31);  // output head
+                float y[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) y[r] = acc[nb][r];
+                if (rot) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float z0 = y[e], z1 = y[8 + e];
+                        if (DX) {   // RoPE: turn by +phi
+                            y[e] = z0 * cs[e] - z1 * sn[e];
+                            y[8 + e] = z1 * cs[e] + z0 * sn[e];
+                        } else {    // inverse RoPE: turn by -phi
+                            y[e] = z0 * cs[e] + z1 * sn[e];
+                            y[8 + e] = z1 * cs[e] - z0 * sn[e];
+                        }
+                    }
+                }
+                if (row < nh) {
+                    uint16_t* orow = Out + (s * nh + row) * (int64_t)d;
+                    if (c0 >= 0) {
+                        u32x4 v;
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+                            v[jj] = pack2(f32_to_bf16_rne(y[2 * jj]), f32_to_bf16_rne(y[2 * jj + 1]));
+                        *reinterpret_cast<u32x4*>(orow + c0) = v;
+                    }
+                    if (c1 >= 0) {
+                        u32x4 v;
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+                            v[jj] = pack2(f32_to_bf16_rne(y[8 + 2 * jj]), f32_to_bf16_rne(y[9 + 2 * jj]));
+                        *reinterpret_cast<u32x4*>(orow + c1) = v;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// weight-gradient partial kernel
+//
+//   P_b[g,h] = sum over tokens s of block b, channels c:
+//                  dY[s,g,c] * inv_rope(O)[s,h,c]
+//
+// MFMA with A = dY rows (m = g), B = inv_rope(O) rows (n = h), k = channels:
+// both operands are channel-contiguous, so each lane loads its 8 channels with
+// one 16-byte load straight from HBM.  K-step t covers channel groups 2t (lane
+// half 0) and 2t+1 (lane half 1).  For a pe group the lane also loads the
+// rotation partner group and the cos/sin of its 8 pairs, rotates in fp32 and
+// splits the result into bf16 hi + bf16 lo; both are accumulated, which keeps
+// the rotated operand to ~2^-17 relative (nope products are exact).
+//
+// 256 threads (4 waves).  nh <= 64 (NB <= 2): every wave owns all NB x NB
+// output tiles and the waves split the block's tokens round-robin; the four
+// wave sums are added in the fixed order (w0 + w2) + (w1 + w3) in LDS.
+// nh <= 128 (NB = 4): wave w owns the 2 x 2 tiles (g-blocks 2(w/2)+{0,1},
+// h-blocks 2(w%2)+{0,1}) over all tokens of the block; no cross-wave sum.
+// ---------------------------------------------------------------------------
+
+template <int NHP>
+__global__ __launch_bounds__(256) void dw_partial_kernel(
+    const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O,
+    const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
+    const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe,
+    float* __restrict__ partials, int tokens_per_block) {
+    constexpr int NB = (NHP + 31) / 32;
+    constexpr bool SPLIT_TOKENS = NB <= 2;
+    constexpr int TG = SPLIT_TOKENS ? NB : 2;
+    constexpr int TH = SPLIT_TOKENS ? NB : 2;
+    __shared__ __attribute__((aligned(16))) float red[SPLIT_TOKENS ? 2 * TG * TH * 16 * 64 : 1];
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int gb0 = SPLIT_TOKENS ? 0 : 2 * (wave >> 1);
+    const int hb0 = SPLIT_TOKENS ? 0 : 2 * (wave & 1);
+    const int d = nope + pe, h2 = pe >> 1;
+    const int ngroups = d >> 3;
+    const int ksteps = (ngroups + 1) >> 1;
+    const int pe_first_step = (nope >> 3) >> 1;  // first k-step holding a pe group
+    const int half = lane >> 5;
+
+    f32x16 acc[TG][TH];
+#pragma unroll
+    for (int a = 0; a < TG; ++a)
+#pragma unroll
+        for (int b = 0; b < TH; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+    const int64_t s_begin = (int64_t)blockIdx.x * tokens_per_block;
+    int64_t s_end = s_begin + tokens_per_block;
+    if (s_end > sq) s_end = sq;
+
+    for (int64_t s = s_begin + (SPLIT_TOKENS ? wave : 0); s < s_end; s += (SPLIT_TOKENS ? 4 : 1)) {
+        int64_t prow = 0;
+        if (pe > 0) prow = table_row(positions, s, table_rows);
+        const uint16_t* dys = dY + s * nh * (int64_t)d;
+        const uint16_t* os = O + s * nh * (int64_t)d;
+
+        for (int t = 0; t < ksteps; ++t) {
+            const int grp = 2 * t + half;
+            const int c = 8 * grp;
+            const bool gvalid = grp < ngroups;
+
+            bf16x8 a[TG];
+#pragma unroll
+            for (int tg = 0; tg < TG; ++tg) {
+                const int g = 32 * (gb0 + tg) + (lane & 31);
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (gvalid && g < nh) v = *reinterpret_cast<const u32x4*>(dys + g * d + c);
+                a[tg] = as_bf16x8(v);
+            }
+
+            if (t < pe_first_step) {
+                // nope channels only: the B operand is O itself (exact bf16)
+#pragma unroll
+                for (int th = 0; th < TH; ++th) {
+                    const int h = 32 * (hb0 + th) + (lane & 31);
+                    u32x4 v = {0u, 0u, 0u, 0u};
+                    if (gvalid && h < nh) v = *reinterpret_cast<const u32x4*>(os + h * d + c);
+                    const bf16x8 b = as_bf16x8(v);
+#pragma unroll
+                    for (int tg = 0; tg < TG; ++tg)
+                        acc[tg][th] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tg], b, acc[tg][th], 0, 0, 0);
+                }
+            } else {
+                // this k-step may hold pe groups: rotate, split hi/lo
+                const bool pe_grp = gvalid && c >= nope;
+                const bool first = c < nope + h2;
+                const int i0 = first ? c - nope : c - nope - h2;
+                const int cpart = first ? c + h2 : c - h2;
+                const float sgn = first ? 1.0f : -1.0f;
+                float cs[8], sn[8];
+                if (pe_grp) {
+                    const f32x4* pc = reinterpret_cast<const f32x4*>(rcos + prow * h2 + i0);
+                    const f32x4* ps = reinterpret_cast<const f32x4*>(rsin + prow * h2 + i0);
+                    const f32x4 ca = pc[0], cb = pc[1], sa = ps[0], sb = ps[1];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        cs[e] = ca[e]; cs[4 + e] = cb[e];
+                        sn[e] = sgn * sa[e]; sn[4 + e] = sgn * sb[e];
+                    }
+                }
+#pragma unroll
+                for (int th = 0; th < TH; ++th) {
+                    const int h = 32 * (hb0 + th) + (lane & 31);
+                    u32x4 own = {0u, 0u, 0u, 0u}, part = {0u, 0u, 0u, 0u};
+                    if (gvalid && h < nh) {
+                        own = *reinterpret_cast<const u32x4*>(os + h * d + c);
+                        if (pe_grp) part = *reinterpret_cast<const u32x4*>(os + h * d + cpart);
+                    }
+                    u32x4 hi = own, lo = {0u, 0u, 0u, 0u};
+                    if (pe_grp) {
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            uint32_t hw[2], lw[2];
+#pragma unroll
+                            for (int e = 0; e < 2; ++e) {
+                                const int k = 2 * jj + e;
+                                const float xa = bf16_to_f32((own[jj] >> (16 * e)) & 0xffffu);
+                                const float xb = bf16_to_f32((part[jj] >> (16 * e)) & 0xffffu);
+                                // first half: a C + b S; second half: a C - b S
+                                const float x = xa * cs[k] + xb * sn[k];
+                                const uint32_t xh = f32_to_bf16_rne(x);
+                                hw[e] = xh;
+                                lw[e] = f32_to_bf16_rne(x - bf16_to_f32(xh));
+                            }
+                            hi[jj] = pack2(hw[0], hw[1]);
+                            lo[jj] = pack2(lw[0], lw[1]);
+                        }
+                    }
+                    const bf16x8 bh = as_bf16x8(hi), bl = as_bf16x8(lo);
+#pragma unroll
+                    for (int tg = 0; tg < TG; ++tg) {
+                        acc[tg][th] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tg], bh, acc[tg][th], 0, 0, 0);
+                        acc[tg][th] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tg], bl, acc[tg][th], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+
+    float* part = partials + (int64_t)blockIdx.x * nh * nh;
+    if constexpr (SPLIT_TOKENS) {
+        // fixed-order sum of the four waves: (w0 + w2) + (w1 + w3)
+        auto slot = [&](int w2, int tg, int th, int r) -> float& {
+            return red[(((w2 * TG + tg) * TH + th) * 16 + r) * 64 + lane];
+        };
+        __syncthreads();
+        if (wave >= 2) {
+#pragma unroll
+            for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+                for (int th = 0; th < TH; ++th)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) slot(wave - 2, tg, th, r) = acc[tg][th][r];
+        }
+        __syncthreads();
+        if (wave < 2) {
+#pragma unroll
+            for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+                for (int th = 0; th < TH; ++th)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[tg][th][r] += slot(wave, tg, th, r);
+        }
+        __syncthreads();
+        if (wave == 1) {
+#pragma unroll
+            for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+                for (int th = 0; th < TH; ++th)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) slot(0, tg, th, r) = acc[tg][th][r];
+        }
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+            for (int th = 0; th < TH; ++th)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[tg][th][r] += slot(0, tg, th, r);
+    }
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+        for (int th = 0; th < TH; ++th) {
+            const int h = 32 * (hb0 + th) + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int g = 32 * (gb0 + tg) + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (g < nh && h < nh) part[g * nh + h] = acc[tg][th][r];
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// fixed-order reduction of the partials: dW[e] = sum_b P[b][e]
+//
+// Workgroup = 64 elements x 16 waves.  Wave w sums the blocks
+// [w*n/16, (w+1)*n/16) in batches of 16 (each batch added as a balanced
+// binary tree, batches added in order); the 16 wave sums are then added as a
+// balanced binary tree in LDS.  The order depends only on n.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(1024) void dw_reduce_kernel(const float* __restrict__ partials,
+                                                         int64_t n_blocks, int64_t n_elems,
+                                                         float* __restrict__ dW) {
+    __shared__ float red[16][64];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t e = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t b0 = n_blocks * wave / 16, b1 = n_blocks * (wave + 1) / 16;
+    float total = 0.0f;
+    if (e < n_elems) {
+        for (int64_t b = b0; b < b1; b += 16) {
+            float v[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                v[k] = (b + k < b1) ? partials[(b + k) * n_elems + e] : 0.0f;
+#pragma unroll
+            for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+                for (int k = 0; k < 16; k += 2 * w) v[k] += v[k + w];
+            total += v[0];
+        }
+    }
+    red[wave][lane] = total;
+    __syncthreads();
+    if (wave == 0) {
+        float v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = red[k][lane];
+#pragma unroll
+        for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+            for (int k = 0; k < 16; k += 2 * w) v[k] += v[k + w];
+        if (e < n_elems) dW[e] = v[0];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// RoPE tables: cos/sin(r * theta^(-2i/pe)) with the angle in fp64
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void rope_table_kernel(double theta, int pe, int64_t rows,
+                                                         float* __restrict__ cos_out,
+                                                         float* __restrict__ sin_out) {
+    const int h2 = pe >> 1;
+    const int64_t n = rows * h2;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = idx / h2;
+        const int i = (int)(idx - r * h2);
+        const double inv_freq = pow(theta, -2.0 * (double)i / (double)pe);
+        const double phi = (double)r * inv_freq;
+        double sv, cv;
+        sincos(phi, &sv, &cv);
+        cos_out[idx] = (float)cv;
+        sin_out[idx] = (float)sv;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host-side launchers (argument checks are done by the caller)
+// ---------------------------------------------------------------------------
+
+template <int NHP, int MPI, bool DX>
+static hipError_t launch_mix_t(const MixArgs& a, hipStream_t stream) {
+    const int d = a.nope + a.pe;
+    (void)d;
+    const int nu = (a.nope + 15) / 16 + (a.pe / 2) / 8;
+    const int mbt = (nu + 1) / 2;
+    const int ipt = (mbt + MPI - 1) / MPI;
+    const int64_t total = a.sq * ipt;
+    int64_t grid = (int64_t)a.n_cu * a.waves_per_cu;
+    if (grid > total) grid = total;
+    if (grid < 1) return hipSuccess;
+    hipLaunchKernelGGL((mix_kernel<NHP, MPI, DX>), dim3((unsigned)grid), dim3(64), 0, stream, a.X,
+                       a.W, a.rcos, a.rsin, a.table_rows, a.positions, a.nh, a.nope, a.pe, a.Out,
+                       total, ipt);
+    return hipGetLastError();
+}
+
+template <bool DX>
+static hipError_t launch_mix_dx(const MixArgs& a, hipStream_t stream) {
+    if (a.nh <= 16) return launch_mix_t<16, 2, DX>(a, stream);
+    if (a.nh <= 32) return launch_mix_t<32, 2, DX>(a, stream);
+    if (a.nh <= 64) return launch_mix_t<64, 2, DX>(a, stream);
+    return launch_mix_t<128, 1, DX>(a, stream);
+}
+
+hipError_t launch_mix(const MixArgs& a, bool dx, hipStream_t stream) {
+    return dx ? launch_mix_dx<true>(a, stream) : launch_mix_dx<false>(a, stream);
+}
+
+int dw_tokens_per_block(int64_t sq, int nh) {
+    int64_t t = (sq * nh + 65535) / 65536;
+    t = (t + 3) / 4 * 4;
+    if (t < 4) t = 4;
+    if (t > (1 << 20)) t = 1 << 20;
+    return (int)t;
+}
+
+int64_t dw_num_blocks(int64_t sq, int nh) {
+    const int t = dw_tokens_per_block(sq, nh);
+    return (sq + t - 1) / t;
+}
+
+template <int NHP>
+static hipError_t launch_dw_t(const DwArgs& a, hipStream_t stream) {
+    const int tpb = dw_tokens_per_block(a.sq, a.nh);
+    const int64_t nb = dw_num_blocks(a.sq, a.nh);
+    hipLaunchKernelGGL((dw_partial_kernel<NHP>), dim3((unsigned)nb), dim3(256), 0, stream, a.dY,
+                       a.O, a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe,
+                       a.partials, tpb);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t ne = (int64_t)a.nh * a.nh;
+    hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((ne + 63) / 64)), dim3(1024), 0, stream,
+                       a.partials, nb, ne, a.dW);
+    return hipGetLastError();
+}
+
+hipError_t launch_dw(const DwArgs& a, hipStream_t stream) {
+    if (a.nh <= 16) return launch_dw_t<16>(a, stream);
+    if (a.nh <= 32) return launch_dw_t<32>(a, stream);
+    if (a.nh <= 64) return launch_dw_t<64>(a, stream);
+    return launch_dw_t<128>(a, stream);
+}
+
+hipError_t launch_rope_table(double theta, int pe, int64_t rows, float* cos_out, float* sin_out,
+                             int n_cu, hipStream_t stream) {
+    const int64_t n = rows * (pe / 2);
+    if (n == 0) return hipSuccess;
+    int64_t grid = (n + 255) / 256;
+    const int64_t cap = (int64_t)n_cu * 32;
+    if (grid > cap) grid = cap;
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)grid), dim3(256), 0, stream, theta, pe,
+                       rows, cos_out, sin_out);
+    return hipGetLastError();
+}
+
+}  // namespace pm

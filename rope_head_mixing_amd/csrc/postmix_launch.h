@@ -1,0 +1,47 @@
+// postmix_launch.h -- internal interface between the C ABI layer and the
+// gfx950 kernels.  Not installed; the public interface is include/postmix.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pm {
+
+struct MixArgs {
+    const uint16_t* X;      // O (forward) or dY (input gradient)
+    const uint16_t* W;
+    const float* rcos;
+    const float* rsin;
+    int64_t table_rows;
+    const int32_t* positions;
+    int64_t sq;
+    int nh, nope, pe;
+    uint16_t* Out;          // Y or dO
+    int n_cu;               // compute units of the device
+    int waves_per_cu;       // resident single-wave workgroups to aim for per CU
+};
+
+struct DwArgs {
+    const uint16_t* dY;
+    const uint16_t* O;
+    const float* rcos;
+    const float* rsin;
+    int64_t table_rows;
+    const int32_t* positions;
+    int64_t sq;
+    int nh, nope, pe;
+    float* dW;
+    float* partials;        // [dw_num_blocks(sq, nh), nh, nh] fp32 workspace
+};
+
+hipError_t launch_mix(const MixArgs& a, bool dx, hipStream_t stream);
+hipError_t launch_dw(const DwArgs& a, hipStream_t stream);
+hipError_t launch_rope_table(double theta, int pe, int64_t rows, float* cos_out, float* sin_out,
+                             int n_cu, hipStream_t stream);
+
+// Token blocking of the weight gradient: a function of the shape only, so the
+// summation order (and therefore every bit of dW) does not depend on the GPU.
+int dw_tokens_per_block(int64_t sq, int nh);
+int64_t dw_num_blocks(int64_t sq, int nh);
+
+}  // namespace pm

@@ -1,0 +1,225 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/postmix.h declares, and rejects bad arguments before any HIP call.
+
+Pointers here are fake, suitably aligned integers: validation never
+dereferences them, and every case below fails validation, so no device call
+is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rope_head_mixing_amd import postmix as pm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "postmix.h")
+
+A = 0x10000      # 16-byte aligned fake device addresses, far apart
+B = 0x40000000
+C = 0x80000000
+D = 0xC0000000
+E = 0x100000000
+F = 0x140000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(postmix_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["postmix_fwd", "postmix_bwd_dx", "postmix_bwd_dw", "postmix_bwd_dw_workspace_bytes",
+              "postmix_rope_table", "postmix_status_string", "postmix_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = pm.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_exports_nothing_undeclared():
+    """The shared object's dynamic symbols named postmix_* are exactly the header's."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", pm.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(set(re.findall(r"\b(postmix_[a-z0-9_]+)\b", out)))
+    assert exported == declared_functions()
+
+
+def test_status_strings():
+    L = pm.lib()
+    codes = [pm.PM_OK, pm.PM_ERR_NULL, pm.PM_ERR_SHAPE, pm.PM_ERR_ALIGN, pm.PM_ERR_OVERLAP,
+             pm.PM_ERR_WORKSPACE, pm.PM_ERR_DEVICE, pm.PM_ERR_HIP]
+    texts = [L.postmix_status_string(c).decode() for c in codes]
+    assert len(set(texts)) == len(codes)
+    assert L.postmix_status_string(12345).decode() == "unknown status"
+
+
+def fwd(**kw):
+    args = dict(O=A, W=B, cos=C, sin=D, rows=32768, pos=E, sq=16, nh=64, nope=448, pe=64, Y=F)
+    args.update(kw)
+    L = pm.lib()
+    rc = L.postmix_fwd(args["O"], args["W"], args["cos"], args["sin"], args["rows"], args["pos"],
+                       args["sq"], args["nh"], args["nope"], args["pe"], args["Y"], None)
+    return rc, L.postmix_last_error().decode()
+
+
+def dx(**kw):
+    args = dict(dY=A, W=B, cos=C, sin=D, rows=32768, pos=E, sq=16, nh=64, nope=448, pe=64, dO=F)
+    args.update(kw)
+    L = pm.lib()
+    rc = L.postmix_bwd_dx(args["dY"], args["W"], args["cos"], args["sin"], args["rows"], args["pos"],
+                          args["sq"], args["nh"], args["nope"], args["pe"], args["dO"], None)
+    return rc, L.postmix_last_error().decode()
+
+
+def dw(**kw):
+    sq, nh, nope, pe = kw.get("sq", 16), kw.get("nh", 64), kw.get("nope", 448), kw.get("pe", 64)
+    need = pm.lib().postmix_bwd_dw_workspace_bytes(sq, nh, nope, pe)
+    args = dict(dY=A, O=B, cos=C, sin=D, rows=32768, pos=E, sq=sq, nh=nh, nope=nope, pe=pe, dW=F,
+                ws=0x180000000, wsb=need)
+    args.update(kw)
+    L = pm.lib()
+    rc = L.postmix_bwd_dw(args["dY"], args["O"], args["cos"], args["sin"], args["rows"], args["pos"],
+                          args["sq"], args["nh"], args["nope"], args["pe"], args["dW"], args["ws"],
+                          args["wsb"], None)
+    return rc, L.postmix_last_error().decode()
+
+
+@pytest.mark.parametrize("call", [fwd, dx])
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(nh=0), pm.PM_ERR_SHAPE, "nh"),
+    (dict(nh=129), pm.PM_ERR_SHAPE, "nh"),
+    (dict(nope=-8), pm.PM_ERR_SHAPE, "nope"),
+    (dict(nope=12), pm.PM_ERR_SHAPE, "nope"),
+    (dict(pe=8), pm.PM_ERR_SHAPE, "pe"),
+    (dict(pe=-16), pm.PM_ERR_SHAPE, "pe"),
+    (dict(nope=0, pe=0), pm.PM_ERR_SHAPE, "nope + pe"),
+    (dict(sq=-1), pm.PM_ERR_SHAPE, "sq"),
+    (dict(rows=0), pm.PM_ERR_SHAPE, "table_rows"),
+    (dict(W=0), pm.PM_ERR_NULL, "W"),
+    (dict(cos=0), pm.PM_ERR_NULL, "rope_cos"),
+    (dict(sin=0), pm.PM_ERR_NULL, "rope_sin"),
+    (dict(pos=0), pm.PM_ERR_NULL, "positions"),
+    (dict(cos=C + 4), pm.PM_ERR_ALIGN, "rope_cos"),
+    (dict(pos=E + 2), pm.PM_ERR_ALIGN, "positions"),
+    (dict(W=B + 1), pm.PM_ERR_ALIGN, "W"),
+])
+def test_mix_argument_errors(call, kw, code, word):
+    rc, msg = call(**kw)
+    assert rc == code, msg
+    assert word in msg
+
+
+@pytest.mark.parametrize("call,xname,oname", [(fwd, "O", "Y"), (dx, "dY", "dO")])
+def test_mix_named_tensor_errors(call, xname, oname):
+    rc, msg = call(**{xname: 0})
+    assert rc == pm.PM_ERR_NULL and xname in msg
+    rc, msg = call(**{oname: 0})
+    assert rc == pm.PM_ERR_NULL and oname in msg
+    rc, msg = call(**{xname: A + 8})
+    assert rc == pm.PM_ERR_ALIGN and xname in msg
+    rc, msg = call(**{oname: F + 2})
+    assert rc == pm.PM_ERR_ALIGN and oname in msg
+    # output overlapping the input (sq*nh*d*2 bytes = 1 MiB here)
+    rc, msg = call(**{oname: A + 4096})
+    assert rc == pm.PM_ERR_OVERLAP and oname in msg and xname in msg
+    rc, msg = call(**{oname: B})  # output on top of W
+    assert rc == pm.PM_ERR_OVERLAP and "W" in msg
+
+
+def test_pe_zero_does_not_need_tables():
+    """With pe == 0 the tables may be NULL; the call gets past validation
+    (then fails at the device check on a host without a gfx950)."""
+    rc, msg = fwd(pe=0, nope=512, cos=0, sin=0, pos=0, rows=0)
+    assert rc not in (pm.PM_ERR_NULL, pm.PM_ERR_SHAPE, pm.PM_ERR_ALIGN, pm.PM_ERR_OVERLAP), msg
+
+
+def test_empty_sq_is_a_noop_before_any_pointer_check():
+    rc, _ = fwd(sq=0, O=0, Y=0, W=0)
+    assert rc == pm.PM_OK
+    rc, _ = dx(sq=0, dY=0, dO=0, W=0)
+    assert rc == pm.PM_OK
+    rc, msg = fwd(sq=0, nh=0)
+    assert rc == pm.PM_ERR_SHAPE
+
+
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(dW=0), pm.PM_ERR_NULL, "dW"),
+    (dict(dY=0), pm.PM_ERR_NULL, "dY"),
+    (dict(O=0), pm.PM_ERR_NULL, "O"),
+    (dict(ws=0), pm.PM_ERR_NULL, "workspace"),
+    (dict(wsb=256), pm.PM_ERR_WORKSPACE, "workspace"),
+    (dict(ws=0x180000000 + 8), pm.PM_ERR_ALIGN, "workspace"),
+    (dict(dY=A + 4), pm.PM_ERR_ALIGN, "dY"),
+    (dict(dW=F + 2), pm.PM_ERR_ALIGN, "dW"),
+    (dict(dW=A + 64), pm.PM_ERR_OVERLAP, "dW"),
+    (dict(ws=B), pm.PM_ERR_OVERLAP, "workspace"),
+    (dict(nh=200), pm.PM_ERR_SHAPE, "nh"),
+    (dict(pos=0), pm.PM_ERR_NULL, "positions"),
+])
+def test_dw_argument_errors(kw, code, word):
+    rc, msg = dw(**kw)
+    assert rc == code, msg
+    assert word in msg
+
+
+def test_workspace_size_is_a_function_of_the_shape():
+    L = pm.lib()
+    # sq*nh = 2^20 -> 16 tokens per block -> 1024 blocks of nh*nh fp32 partials
+    assert L.postmix_bwd_dw_workspace_bytes(16384, 64, 448, 64) == 1024 * 64 * 64 * 4
+    assert L.postmix_bwd_dw_workspace_bytes(8192, 128, 448, 64) == 512 * 128 * 128 * 4
+    assert L.postmix_bwd_dw_workspace_bytes(0, 64, 448, 64) == 0
+    assert L.postmix_bwd_dw_workspace_bytes(16, 0, 448, 64) == 0
+    for args in [(64, 4, 48, 16), (8192, 3, 448, 64), (7, 5, 8, 16)]:
+        assert L.postmix_bwd_dw_workspace_bytes(*args) % 256 == 0
+        assert L.postmix_bwd_dw_workspace_bytes(*args) >= args[1] * args[1] * 4
+
+
+def test_rope_table_argument_errors():
+    L = pm.lib()
+    assert L.postmix_rope_table(0.0, 64, 10, A, B, None) == pm.PM_ERR_SHAPE
+    assert L.postmix_rope_table(1e4, 24, 10, A, B, None) == pm.PM_ERR_SHAPE
+    assert L.postmix_rope_table(1e4, 64, 10, 0, B, None) == pm.PM_ERR_NULL
+    assert L.postmix_rope_table(1e4, 64, 10, A + 4, B, None) == pm.PM_ERR_ALIGN
+    assert L.postmix_rope_table(1e4, 64, 10, A, A + 16, None) == pm.PM_ERR_OVERLAP
+    assert L.postmix_rope_table(1e4, 64, 0, 0, 0, None) == pm.PM_OK
+
+
+def test_last_error_is_thread_local():
+    import threading
+    rc, msg = fwd(nh=0)
+    assert "nh" in msg
+    seen = []
+
+    def other():
+        seen.append(pm.lib().postmix_last_error().decode())
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen == [""]
+    assert "nh" in pm.lib().postmix_last_error().decode()
+
+
+def test_binding_rejects_wrong_dtypes_by_name():
+    torch = pytest.importorskip("torch")
+    O = torch.zeros((2, 4, 64), dtype=torch.float16)
+    W = torch.zeros((4, 4), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="O must be torch.bfloat16"):
+        pm.postmix_fwd(O, W, None, None, None, 48, 16)
+    with pytest.raises(ValueError, match="dY must be torch.bfloat16"):
+        pm.postmix_bwd_dw(O, O, None, None, None, 48, 16)
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(pm, "_lib", None)
+    monkeypatch.setattr(pm, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        pm.lib()

@@ -1,0 +1,241 @@
+"""Parity of the gfx950 path (through the C ABI) with the fp64 oracle.
+
+Tolerances (tests/gpu_util.py): bf16 Y and dO within 1e-2*|ref| + 1e-3 of the
+fp64 oracle element by element; fp32 dW within 1e-4 relative (Frobenius norm,
+and every element within 1e-4 * max|ref|); dW bitwise identical across runs.
+
+Inputs are the seeded synthetic workloads of rope_head_mixing_amd.synthetic:
+the tiny case (sq=64, nh=4, 48+16), the forward-only case (sq=1024, nh=64,
+448+64), the production case (sq=16384, nh=64, 448+64, positions 16384..32767)
+and the head-count sweep (sq=8192, nh in {3, 128}); plus small shapes that
+span several tiles with ragged tails.  At the production sizes the oracle
+evaluates sampled outputs one by one.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from rope_head_mixing_amd import synthetic
+from tests import gpu_util as gu
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gu.has_gfx950(), reason="needs an MI355X (gfx950)")]
+
+THETA = synthetic.THETA
+
+
+def P():
+    from rope_head_mixing_amd import postmix
+    return postmix
+
+
+def tables(case, positions):
+    if case.pe == 0:
+        return None, None
+    rows = int(np.max(positions)) + 1 if len(positions) else 1
+    return P().postmix_rope_table(case.theta, case.pe, rows)
+
+
+class Dev:
+    """Device copies of one case's inputs."""
+
+    def __init__(self, case, O=None, W=None, dY=None, positions=None, need_dy=True):
+        self.case = case
+        self.O = case.O() if O is None else O
+        self.W = case.W() if W is None else W
+        self.dY = (case.dY() if dY is None else dY) if need_dy else None
+        self.pos = case.positions() if positions is None else np.asarray(positions, np.int32)
+        self.dO_ = gu.dev_bf16(self.O)
+        self.dW_ = gu.dev_bf16(self.W)
+        self.ddY_ = gu.dev_bf16(self.dY) if need_dy else None
+        self.dpos = gu.dev_i32(self.pos)
+        self.cos, self.sin = tables(case, self.pos)
+
+    def fwd(self):
+        c = self.case
+        return P().postmix_fwd(self.dO_, self.dW_, self.cos, self.sin, self.dpos, c.nope, c.pe)
+
+    def dx(self):
+        c = self.case
+        return P().postmix_bwd_dx(self.ddY_, self.dW_, self.cos, self.sin, self.dpos, c.nope, c.pe)
+
+    def dw(self, workspace=None):
+        c = self.case
+        return P().postmix_bwd_dw(self.ddY_, self.dO_, self.cos, self.sin, self.dpos, c.nope, c.pe,
+                                  workspace=workspace)
+
+
+def full_check(case, ops=("fwd", "dx", "dw")):
+    print(f"\n[parity] {case.name}: sq={case.sq} nh={case.nh} nope={case.nope} pe={case.pe}",
+          flush=True)
+    dv = Dev(case, need_dy=("dx" in ops or "dw" in ops))
+    out = {}
+    if "fwd" in ops:
+        Y = gu.host_bits(dv.fwd())
+        ref = oracle.fwd(dv.O, dv.W, dv.pos, case.theta, case.nope, case.pe)
+        out["fwd"] = gu.check_bf16(Y, ref, f"{case.name} Y")
+    if "dx" in ops:
+        dO = gu.host_bits(dv.dx())
+        ref = oracle.bwd_dx(dv.dY, dv.W, dv.pos, case.theta, case.nope, case.pe)
+        out["dx"] = gu.check_bf16(dO, ref, f"{case.name} dO")
+    if "dw" in ops:
+        dW = dv.dw().cpu().numpy()
+        ref = oracle.bwd_dw(dv.dY, dv.O, dv.pos, case.theta, case.nope, case.pe)
+        out["dw"] = gu.check_dw(dW, ref, f"{case.name} dW")
+    print(f"[parity] {case.name}: {out}", flush=True)
+    return out
+
+
+# --------------------------------------------------------------------------
+# first: the smallest launch, so a stall at compile/load time is told apart
+# from a problem of volume
+# --------------------------------------------------------------------------
+
+def test_00_one_token_one_head():
+    full_check(synthetic.case(1, 1, 0, 16, seed=7, pos_offset=3))
+
+
+def test_01_rope_table_matches_oracle_angles():
+    for pe, rows in [(16, 64), (64, 32768)]:
+        cos, sin = P().postmix_rope_table(THETA, pe, rows)
+        C, S = oracle.rope_angles(THETA, pe, np.arange(rows, dtype=np.int32))
+        # fp32 rounding of values in [-1, 1]: at most 2^-25 from the fp64 value
+        assert np.abs(cos.cpu().numpy().astype(np.float64) - C).max() <= 2.0 ** -24
+        assert np.abs(sin.cpu().numpy().astype(np.float64) - S).max() <= 2.0 ** -24
+
+
+def test_02_tiny_workload():
+    full_check(synthetic.CASES["tiny"])
+
+
+@pytest.mark.parametrize("sq,nh,nope,pe,off", [
+    (128, 4, 48, 16, 0),       # the (128, 4, 64) shape the pages' tests single out
+    (67, 64, 448, 64, 16384),  # production widths, ragged token count
+    (33, 20, 40, 16, 5),       # nh not a multiple of 16, nope % 16 == 8
+    (50, 3, 448, 64, 0),       # the smallest head count of the sweep
+    (19, 128, 448, 64, 8000),  # widest head mix
+    (40, 64, 512, 0, 0),       # pe = 0: plain head mix
+    (40, 8, 0, 64, 1000),      # nope = 0: every channel rotated
+    (21, 33, 8, 32, 77),       # nh just past a 32-head block
+    (9, 96, 64, 16, 31),       # nh = 96 (three 32-head output blocks)
+    (5, 1, 8, 16, 2),          # a single head
+])
+def test_small_shapes(sq, nh, nope, pe, off):
+    full_check(synthetic.case(sq, nh, nope, pe, seed=1000 + sq + nh, pos_offset=off))
+
+
+def test_forward_only_workload_sq1024():
+    full_check(synthetic.CASES["fwd_1k"], ops=("fwd",))
+
+
+def test_sweep_nh3_full():
+    full_check(synthetic.CASES["sweep_nh3"])
+
+
+# --------------------------------------------------------------------------
+# properties
+# --------------------------------------------------------------------------
+
+def test_identity_mix_keeps_nope_columns_bitwise():
+    c = synthetic.case(37, 64, 448, 64, seed=321, pos_offset=16384)
+    W = synthetic.f32_to_bf16_bits(np.eye(64, dtype=np.float32))
+    dv = Dev(c, W=W, need_dy=False)
+    Y = gu.host_bits(dv.fwd())
+    np.testing.assert_array_equal(Y[..., :448], dv.O[..., :448])
+    ref = oracle.fwd(dv.O, W, dv.pos, THETA, 448, 64)
+    gu.check_bf16(Y, ref, "W=I Y")
+
+
+def test_zero_positions_equal_the_unrotated_mix_bitwise():
+    c = synthetic.case(23, 64, 448, 64, seed=333)
+    dv = Dev(c, positions=np.zeros(23, np.int32))
+    Y = gu.host_bits(dv.fwd())
+    flat = synthetic.case(23, 64, 512, 0, seed=333)
+    dv2 = Dev(flat, O=dv.O, W=dv.W, dY=dv.dY)
+    np.testing.assert_array_equal(Y, gu.host_bits(dv2.fwd()))
+    np.testing.assert_array_equal(gu.host_bits(dv.dx()), gu.host_bits(dv2.dx()))
+
+
+def test_out_of_range_positions_are_clamped_not_read_out_of_bounds():
+    c = synthetic.case(6, 4, 48, 16, seed=55)
+    pos = np.array([-5, 0, 3, 63, 64, 1000], np.int32)
+    dv = Dev(c, positions=pos)
+    cos, sin = P().postmix_rope_table(THETA, 16, 64)
+    Y = P().postmix_fwd(dv.dO_, dv.dW_, cos, sin, dv.dpos, 48, 16)
+    clamped = np.clip(pos, 0, 63)
+    ref = oracle.fwd(dv.O, dv.W, clamped, THETA, 48, 16)
+    gu.check_bf16(gu.host_bits(Y), ref, "clamped positions")
+
+
+def test_empty_token_range():
+    import torch
+    c = synthetic.case(0, 4, 48, 16, seed=1)
+    O = torch.empty((0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    W = gu.dev_bf16(c.W())
+    pos = torch.empty((0,), dtype=torch.int32, device="cuda")
+    cos, sin = P().postmix_rope_table(THETA, 16, 8)
+    assert P().postmix_fwd(O, W, cos, sin, pos, 48, 16).shape == (0, 4, 64)
+    assert P().postmix_bwd_dx(O, W, cos, sin, pos, 48, 16).shape == (0, 4, 64)
+    dW = torch.full((4, 4), float("nan"), device="cuda")
+    P().postmix_bwd_dw(O, O, cos, sin, pos, 48, 16, out=dW)
+    assert torch.equal(dW.cpu(), torch.zeros(4, 4))
+
+
+def test_dw_repeatable_bitwise_small():
+    c = synthetic.case(300, 64, 448, 64, seed=444, pos_offset=100)
+    dv = Dev(c)
+    first = dv.dw().cpu().numpy()
+    for _ in range(9):
+        np.testing.assert_array_equal(dv.dw().cpu().numpy(), first)
+
+
+# --------------------------------------------------------------------------
+# the full-size workloads (sampled outputs from the oracle)
+# --------------------------------------------------------------------------
+
+def sampled_check(case, ops, n_samples=4096, dw_samples=24, repeat_dw=10):
+    print(f"\n[parity] {case.name} (sampled): sq={case.sq} nh={case.nh}", flush=True)
+    dv = Dev(case, need_dy=("dx" in ops or "dw" in ops))
+    rng = np.random.default_rng(case.seeds[0] + 99)
+    size = case.sq * case.nh * case.d
+    idx = rng.integers(0, size, n_samples)
+    # always include the first and last rows and some pe channels
+    idx[:4] = [0, size - 1, size - case.pe // 2, case.d * case.nh * (case.sq // 2) + case.nope]
+    res = {}
+    if "fwd" in ops:
+        Y = gu.host_bits(dv.fwd()).reshape(-1)
+        ref = oracle.fwd_at(dv.O, dv.W, dv.pos, case.theta, case.nope, case.pe, idx)
+        res["fwd"] = gu.check_bf16(Y[idx], ref, f"{case.name} Y")
+        del Y
+    if "dx" in ops:
+        dO = gu.host_bits(dv.dx()).reshape(-1)
+        ref = oracle.bwd_dx_at(dv.dY, dv.W, dv.pos, case.theta, case.nope, case.pe, idx)
+        res["dx"] = gu.check_bf16(dO[idx], ref, f"{case.name} dO")
+        del dO
+    if "dw" in ops:
+        import torch
+        ws = torch.empty(P().postmix_bwd_dw_workspace_bytes(case.sq, case.nh, case.nope, case.pe),
+                         dtype=torch.uint8, device="cuda")
+        dW = dv.dw(workspace=ws).cpu().numpy()
+        for _ in range(repeat_dw - 1):
+            np.testing.assert_array_equal(dv.dw(workspace=ws).cpu().numpy(), dW)
+        widx = rng.integers(0, case.nh * case.nh, dw_samples)
+        widx[:2] = [0, case.nh * case.nh - 1]
+        ref = oracle.bwd_dw_at(dv.dY, dv.O, dv.pos, case.theta, case.nope, case.pe, widx)
+        got = dW.reshape(-1)[widx].astype(np.float64)
+        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        assert rel <= gu.DW_REL, f"{case.name} dW sampled rel {rel:.3e}"
+        assert np.abs(got - ref).max() <= gu.DW_REL * np.abs(ref).max()
+        res["dw"] = rel
+    print(f"[parity] {case.name}: {res}", flush=True)
+    return res
+
+
+def test_sweep_nh128_sampled():
+    sampled_check(synthetic.CASES["sweep_nh128"], ("fwd", "dx", "dw"), repeat_dw=2)
+
+
+def test_production_forward_and_backward_sampled():
+    """sq=16384, nh=64, 448+64, positions 16384..32767: Y and dO sampled,
+    dW sampled and bitwise identical over 10 runs."""
+    sampled_check(synthetic.CASES["prod"], ("fwd", "dx", "dw"), repeat_dw=10)
