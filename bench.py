@@ -1,0 +1,326 @@
+"""Benchmark of the fused inverse-RoPE + VHA postmix on one MI355X.
+
+A step is one pass of the whole path over the production workload of
+PaddleFleet PR #1772 (PR body item 1: sq=16384 tokens of a 64K context with
+context_parallel_size=4, nh=64, nope=448, pe=64, a 1 GiB bf16 attention
+output): forward (postmix_fwd), input gradient (postmix_bwd_dx) and weight
+gradient (postmix_bwd_dw), each reading its inputs from HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints one JSON line.  `value` is the step's achieved HBM bandwidth: the
+algorithmic bytes of the three ops (activations in and out, W, the cos/sin
+rows touched, positions, dW) over the measured step time.  Per-op times come
+from HIP events recorded on the stream the kernels run on.  The oracle's
+CPU time on a bounded sample of the same workload is reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "postmix fwd/bwd µs + achieved HBM GB/s (% peak), sq=16384 nh=64 d=512 bf16"
+PEAK_GBPS = 8000.0  # MI355X HBM3E
+KERNEL_SOURCE = os.path.join(ROOT, "rope_head_mixing_amd", "csrc", "postmix_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+# The pages' own figures for this workload (another GPU; context only).
+PAGES_CONTEXT = {
+    "hardware": "1x B30Z (sm10.3)",
+    "fwd_us_unfused_to_fused": [643.7, 459.4],
+    "bwd_us_final_route_unfused_to_fused": [2700.1, 3012.3],
+    "bwd_us_head_major_route_unfused_to_fused": [2699.4, 1828.9],
+}
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            doc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if doc.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    entry = doc.get("kernels", {}).get(kernel_key)
+    if not entry:
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, O, W, dY, pos, target_s: float):
+    """The oracle, untouched, on the first S tokens of the workload (S sized
+    from a short calibration so the timed run is about target_s seconds)."""
+    import oracle
+    threads = oracle.default_threads()
+
+    def one_pass(S):
+        t0 = time.perf_counter()
+        oracle.fwd(O[:S], W, pos[:S], case.theta, case.nope, case.pe, nthreads=threads)
+        oracle.bwd_dx(dY[:S], W, pos[:S], case.theta, case.nope, case.pe, nthreads=threads)
+        oracle.bwd_dw(dY[:S], O[:S], pos[:S], case.theta, case.nope, case.pe, nthreads=threads)
+        return time.perf_counter() - t0
+
+    cal = min(case.sq, 256)
+    t_cal = one_pass(cal)
+    S = int(min(case.sq, max(cal, round(target_s / max(t_cal, 1e-6) * cal / 64) * 64)))
+    t = one_pass(S)
+    frac = S / case.sq
+    alg = sum(case.algorithmic_bytes(op) for op in ("fwd", "bwd_dx", "bwd_dw")) * frac
+    return {
+        "value": round(alg / t / 1e9, 3),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"fwd+bwd_dx+bwd_dw on the first {S} of {case.sq} tokens "
+                  f"({t:.2f} s; full step extrapolates to {t / frac * 1e6:.0f} us)",
+        "seconds": round(t, 3),
+        "us_per_full_step_extrapolated": round(t / frac * 1e6, 1),
+    }
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix):
+    """Turn rocprofv3 outputs (kernel-trace --stats, --pmc FETCH_SIZE, --pmc
+    WRITE_SIZE runs of this script) into profiles/<out_prefix>_*.md and the
+    per-launch HBM traffic file read by the benchmark.
+
+    The counters are calibrated on the plain 1 GiB device copy that the
+    benchmark runs (its known traffic: 1 GiB read, 1 GiB written)."""
+    import collections
+    import csv
+    import glob
+
+    def one(pattern):
+        hits = glob.glob(pattern, recursive=True)
+        if not hits:
+            raise SystemExit(f"no file matches {pattern}")
+        return hits[0]
+
+    stats = list(csv.DictReader(open(one(os.path.join(trace_dir, "**", "*kernel_stats.csv")))))
+
+    def counters(d, name):
+        agg = collections.defaultdict(list)
+        for r in csv.DictReader(open(one(os.path.join(d, "**", "*counter_collection.csv")))):
+            if r["Counter_Name"] == name:
+                agg[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]) * 1024)
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    fetch, write = counters(fetch_dir, "FETCH_SIZE"), counters(write_dir, "WRITE_SIZE")
+    gib = float(1 << 30)
+    # the 1 GiB copy: the copy kernel launch whose written bytes are largest
+    copy_key = max((k for k in write if "copy" in k[0].lower()), key=lambda k: write[k])
+    f_scale, w_scale = gib / fetch[copy_key], gib / write[copy_key]
+
+    def short(name):
+        return name.split("(")[0].replace("void ", "").replace("pm::", "")
+
+    rows = []
+    for r in stats:
+        rows.append((short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                     float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    traffic = {}
+    for (name, grid), fb in fetch.items():
+        wb = write.get((name, grid), 0.0)
+        traffic[short(name)] = {"fetch_bytes": fb * f_scale, "write_bytes": wb * w_scale,
+                                "hbm_bytes_per_launch": fb * f_scale + wb * w_scale}
+    ops = {"fwd": ["mix_kernel<64, 2, false>"], "bwd_dx": ["mix_kernel<64, 2, true>"],
+           "bwd_dw": ["dw_partial_kernel<64>", "dw_reduce_kernel"]}
+    doc = {"kernel_source_sha": kernel_source_sha(), "fetch_scale": f_scale, "write_scale": w_scale,
+           "kernels": {}}
+    for op, names in ops.items():
+        present = [n for n in names if n in traffic]
+        if present:
+            doc["kernels"][op] = {
+                "kernels": present,
+                "hbm_bytes_per_launch": sum(traffic[n]["hbm_bytes_per_launch"] for n in present)}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(doc, f, indent=1)
+        f.write("\n")
+    lines = [f"# {out_prefix}: rocprofv3 kernel trace and HBM counters", "",
+             "Commands (from the repository root on one MI355X):", "", "```", command_note.strip(),
+             "```", "", f"Kernel source sha256[:16]: `{doc['kernel_source_sha']}`", "",
+             "## Kernel durations (rocprofv3 --kernel-trace --stats)", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    lines += [f"| `{n}` | {c} | {a:.1f} | {mn:.1f} | {mx:.1f} |" for n, c, a, mn, mx in rows]
+    lines += ["", "## HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)", "",
+              f"Calibration on the benchmark's plain 1 GiB device copy (`{short(copy_key[0])}`): "
+              f"FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f} gives 1 GiB each.", "",
+              "| kernel | fetched GiB | written GiB | total GiB |", "|---|---|---|---|"]
+    for n, t in sorted(traffic.items()):
+        lines.append(f"| `{n}` | {t['fetch_bytes'] / gib:.4f} | {t['write_bytes'] / gib:.4f} | "
+                     f"{t['hbm_bytes_per_launch'] / gib:.4f} |")
+    path = os.path.join(ROOT, "profiles", f"{out_prefix}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+    print(TRAFFIC_FILE)
+
+
+def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
+        # bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR NAME COMMAND_NOTE_FILE
+        trace_dir, fetch_dir, write_dir, name, note_file = sys.argv[2:7]
+        summarize_profiles(trace_dir, fetch_dir, write_dir, open(note_file).read(), name)
+        return
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prod",
+                    help="prod (default) or another key of synthetic.CASES")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-target-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); this build has "
+              "no multi-GPU path: forward and input gradient shard by tokens with no exchange, "
+              "and the weight gradient would need one [nh,nh] fp32 sum across ranks.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from rope_head_mixing_amd import postmix as pm
+    from rope_head_mixing_amd import synthetic
+
+    pm.lib()  # raises if the HIP library is not built: no fallback
+    torch.cuda.set_device(0)
+    case = synthetic.CASES[args.workload]
+    t0 = time.perf_counter()
+    O, W, dY, pos = case.O(), case.W(), case.dY(), case.positions()
+    gen_s = time.perf_counter() - t0
+
+    def dev_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+
+    dO_in, dW_in, ddY = dev_bf16(O), dev_bf16(W), dev_bf16(dY)
+    dpos = torch.from_numpy(pos).cuda()
+    cos, sin = pm.postmix_rope_table(case.theta, case.pe, int(pos.max()) + 1)
+    Y = torch.empty_like(dO_in)
+    dO = torch.empty_like(ddY)
+    dW = torch.empty((case.nh, case.nh), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(256, pm.postmix_bwd_dw_workspace_bytes(case.sq, case.nh, case.nope, case.pe)),
+                     dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        pm.postmix_fwd(dO_in, dW_in, cos, sin, dpos, case.nope, case.pe, out=Y)
+        if evs is not None:
+            evs[1].record()
+        pm.postmix_bwd_dx(ddY, dW_in, cos, sin, dpos, case.nope, case.pe, out=dO)
+        if evs is not None:
+            evs[2].record()
+        pm.postmix_bwd_dw(ddY, dO_in, cos, sin, dpos, case.nope, case.pe, out=dW, workspace=ws)
+        if evs is not None:
+            evs[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    ops = ["fwd", "bwd_dx", "bwd_dw"]
+    per_op_ms = {op: float(np.mean([events[k][i].elapsed_time(events[k][i + 1])
+                                    for k in range(args.steps)]))
+                 for i, op in enumerate(ops)}
+    ms_per_step = wall * 1e3 / args.steps
+    alg = {op: case.algorithmic_bytes(op) for op in ops}
+    step_bytes = sum(alg.values())
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    op_report = {}
+    for op in ops:
+        gbps = alg[op] / (per_op_ms[op] * 1e-3) / 1e9
+        op_report[op] = {"us": round(per_op_ms[op] * 1e3, 1), "GBps": round(gbps, 1),
+                         "pct_peak": round(100 * gbps / PEAK_GBPS, 1),
+                         "algorithmic_bytes": alg[op]}
+
+    # device-to-device copy of the same 1 GiB, for an achievable-bandwidth reference
+    src = dO_in.view(torch.int16)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 2 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+    del dst
+
+    dominant = max(ops, key=lambda op: per_op_ms[op])
+    kernel_key = {"fwd": "mix_kernel<64, 2, false>", "bwd_dx": "mix_kernel<64, 2, true>",
+                  "bwd_dw": "dw_partial_kernel<64> + dw_reduce_kernel"}[dominant]
+    achieved = alg[dominant] / (per_op_ms[dominant] * 1e-3) / 1e9
+    roofline = {
+        "bound": "hbm",
+        "kernel": kernel_key if case.nh == 64 else dominant,
+        "achieved": round(achieved, 1),
+        "peak": PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / PEAK_GBPS, 4),
+        "traffic": measured_traffic(dominant) if args.workload == "prod" else None,
+    }
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{case.name}: fwd + bwd_dx + bwd_dw, O/dY [{case.sq}, {case.nh}, "
+                        f"{case.nope}+{case.pe}] bf16 N(0,1), W [{case.nh},{case.nh}] = I + N(0,0.02), "
+                        f"rotate-half RoPE theta={case.theta:g}, positions "
+                        f"{int(pos[0])}..{int(pos[-1])}",
+            "sq": case.sq, "nh": case.nh, "nope": case.nope, "pe": case.pe,
+        },
+        "ops": op_report,
+        "pct_peak": round(100 * value / PEAK_GBPS, 1),
+        "roofline": roofline,
+        "copy_GBps": round(copy_gbps, 1),
+        "input_generation_s": round(gen_s, 1),
+        "context_pages": PAGES_CONTEXT,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case, O, W, dY, pos, args.cpu_target_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
