@@ -32,6 +32,12 @@ PEAK_GBPS = 8000.0  # MI355X HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "rope_head_mixing_amd", "csrc", "postmix_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # The pages' own figures for this workload (another GPU; context only).
+# kernels behind each op at nh=64, d=512 (tiled path)
+KERNELS_NH64 = {
+    "fwd": "mix_part_kernel<64, 256, 4, false>",
+    "bwd_dx": "mix_part_kernel<64, 256, 4, true>",
+    "bwd_dw": "dw_chunk_kernel<64, 128> + dw_reduce_kernel",
+}
 PAGES_CONTEXT = {
     "hardware": "1x B30Z (sm10.3)",
     "fwd_us_unfused_to_fused": [643.7, 459.4],
@@ -136,8 +142,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix
         wb = write.get((name, grid), 0.0)
         traffic[short(name)] = {"fetch_bytes": fb * f_scale, "write_bytes": wb * w_scale,
                                 "hbm_bytes_per_launch": fb * f_scale + wb * w_scale}
-    ops = {"fwd": ["mix_kernel<64, 2, false>"], "bwd_dx": ["mix_kernel<64, 2, true>"],
-           "bwd_dw": ["dw_partial_kernel<64>", "dw_reduce_kernel"]}
+    ops = {op: [k.strip() for k in names.split("+")] for op, names in KERNELS_NH64.items()}
     doc = {"kernel_source_sha": kernel_source_sha(), "fetch_scale": f_scale, "write_scale": w_scale,
            "kernels": {}}
     for op, names in ops.items():
@@ -275,12 +280,11 @@ def main():
     del dst
 
     dominant = max(ops, key=lambda op: per_op_ms[op])
-    kernel_key = {"fwd": "mix_kernel<64, 2, false>", "bwd_dx": "mix_kernel<64, 2, true>",
-                  "bwd_dw": "dw_partial_kernel<64> + dw_reduce_kernel"}[dominant]
+    kernel_key = KERNELS_NH64[dominant] if case.nh == 64 else dominant
     achieved = alg[dominant] / (per_op_ms[dominant] * 1e-3) / 1e9
     roofline = {
         "bound": "hbm",
-        "kernel": kernel_key if case.nh == 64 else dominant,
+        "kernel": kernel_key,
         "achieved": round(achieved, 1),
         "peak": PEAK_GBPS,
         "unit": "GB/s",

@@ -142,6 +142,18 @@ const char *postmix_status_string(int status);
 /* Message for the last failing call on this thread ("" if none). */
 const char *postmix_last_error(void);
 
+/*
+ * Kernel choice (process-wide).  By default shapes with nh in {32, 64, 128}
+ * whose channels split into 128- or 256-channel parts that hold the whole pe
+ * range run the tiled kernels (postmix_fwd / postmix_bwd_dx: one workgroup per
+ * token part; postmix_bwd_dw: LDS-staged chunks); every other shape runs the
+ * general kernels.  enable != 0 routes every shape through the general
+ * kernels, which is how the two are tested against each other.  Y and dO agree
+ * up to fp32 summation order; dW of either choice is bitwise repeatable, but
+ * the two choices sum in different orders.  Returns the previous setting.
+ */
+int postmix_set_general_kernels(int enable);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,6 +34,7 @@ int ok() {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 std::atomic<int> g_dev_cus[kMaxDevices];
+std::atomic<int> g_force_general{0};
 
 int check_device(int* n_cu) {
     int dev = 0;
@@ -160,6 +161,7 @@ int mix_common(const char* xname, const pm_bf16* X, const pm_bf16* W, const floa
     a.Out = Out;
     a.n_cu = n_cu;
     a.waves_per_cu = 16;
+    a.force_general = g_force_general.load(std::memory_order_relaxed) != 0;
     hipError_t e = pm::launch_mix(a, dx, (hipStream_t)stream);
     if (e != hipSuccess) return fail(PM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -256,6 +258,7 @@ int postmix_bwd_dw(const pm_bf16* dY, const pm_bf16* O, const float* rope_cos,
     a.pe = pe;
     a.dW = dW;
     a.partials = (float*)workspace;
+    a.force_general = g_force_general.load(std::memory_order_relaxed) != 0;
     hipError_t e = pm::launch_dw(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(PM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -299,5 +302,9 @@ const char* postmix_status_string(int status) {
 }
 
 const char* postmix_last_error(void) { return g_last_error; }
+
+int postmix_set_general_kernels(int enable) {
+    return g_force_general.exchange(enable ? 1 : 0, std::memory_order_relaxed);
+}
 
 }  // extern "C"

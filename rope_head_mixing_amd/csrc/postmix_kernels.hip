@@ -537,6 +537,440 @@ __global__ __launch_bounds__(256) void rope_table_kernel(double theta, int pe, i
 }
 
 // ---------------------------------------------------------------------------
+// head-mix kernel, token-part tiles (forward and input gradient), nh in {32, 64, 128}
+//
+// One workgroup per (token s, channel part of CP channels): the [nh x CP] tile
+// is contiguous per row, so it is read with 16-byte non-temporal loads exactly
+// like a copy, staged in LDS, mixed on MFMA and written back with 16-byte
+// non-temporal stores of whole rows.
+//   1. tile -> LDS; W -> LDS (once per workgroup).
+//   2. each wave copies the B operand (W^T for the forward, W for dx) from
+//      LDS into registers.
+//   3. each wave owns M-blocks of 32 channels.  The A operand (rows =
+//      channels, k = heads) is read with the gfx950 transposing LDS load
+//      ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives
+//      T[k0+e][c0+i] for e = 0..3 when source lane j points at
+//      T[k0 + j/4][c0 + 4*(j%4)].  Two such loads give the 8 k-values a lane
+//      contributes to v_mfma_f32_32x32x16_bf16.
+//   4. results of nope channels are rounded to bf16 and written over the
+//      wave's own tile columns; results of pe channels go to an fp32 LDS
+//      scratch (which reuses W's LDS after a barrier).
+//   5. the store phase rotates the pe pairs (fp32, partner read from the
+//      scratch), rounds, and writes every row of the part to HBM.
+// ---------------------------------------------------------------------------
+
+template <int NH, int CP, int WAVES>
+struct PartCfg {
+    static constexpr int KB = NH / 16, NB = NH / 32, NT = 64 * WAVES;
+    static constexpr int PITCH = CP + 8;                 // bf16 elements per LDS row
+    static constexpr int VPR = CP / 8;                   // 16-byte vectors per tile row
+    static constexpr int VPT = NH * VPR / NT;            // vectors per thread
+    static constexpr int WVPT = (NH * NH / 8 + NT - 1) / NT;
+    static constexpr int MBP = CP / 32;                  // M-blocks per part
+    static_assert(NH % 32 == 0 && CP % 32 == 0 && (NH * VPR) % NT == 0, "part tile shape");
+    static size_t lds_bytes(int pe) {
+        const size_t tile = (size_t)NH * PITCH * 2;
+        const size_t w = (size_t)NH * NH * 2, p = (size_t)NH * pe * 4;
+        return tile + (w > p ? w : p);
+    }
+};
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// lane's 8 k-values of an MFMA operand from a row-major [k][n] LDS matrix:
+// rows k0 .. k0+7 are split 4 + 4 over two transposing loads; the lane group
+// g = lane/16 takes columns 16*(g%2) .. +16 of the 32-column block and
+// k rows 8*(g/2) .. +8 of the 16-row k-block.
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* base, int pitch, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const uint16_t* p = base + (8 * (g >> 1) + (i >> 2)) * pitch + 16 * (g & 1) + 4 * (i & 3);
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * pitch));
+    u32x4 v;
+    v[0] = pack2((uint16_t)lo[0], (uint16_t)lo[1]);
+    v[1] = pack2((uint16_t)lo[2], (uint16_t)lo[3]);
+    v[2] = pack2((uint16_t)hi[0], (uint16_t)hi[1]);
+    v[3] = pack2((uint16_t)hi[2], (uint16_t)hi[3]);
+    return as_bf16x8(v);
+}
+
+template <int NH, int CP, int WAVES, bool DX>
+__global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+    const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
+    const int32_t* __restrict__ positions, int nope, int pe, int cpt,
+    uint16_t* __restrict__ Out) {
+    using C = PartCfg<NH, CP, WAVES>;
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    uint16_t* tile = smem;                                   // [NH][PITCH] bf16
+    uint16_t* wl = smem + NH * C::PITCH;                     // [NH][NH] bf16, then:
+    float* pes = reinterpret_cast<float*>(wl);               // [NH][pe] fp32
+
+    const int d = nope + pe;
+    const int h2 = pe >> 1;
+    const int64_t s = blockIdx.x / cpt;
+    const int part = blockIdx.x - (int)(s * cpt);
+    const int c_base = part * CP;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint16_t* xs = X + s * NH * (int64_t)d + c_base;
+
+    // 1. loads: tile rows (contiguous CP channels each) and W
+    u32x4 v[C::VPT];
+#pragma unroll
+    for (int j = 0; j < C::VPT; ++j) {
+        const int q = j * C::NT + tid;
+        const int row = q / C::VPR, c8 = q % C::VPR;
+        v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xs + row * (int64_t)d + 8 * c8));
+    }
+    u32x4 wv[C::WVPT];
+#pragma unroll
+    for (int j = 0; j < C::WVPT; ++j) {
+        const int q = j * C::NT + tid;
+        if (q < NH * NH / 8) wv[j] = reinterpret_cast<const u32x4*>(W)[q];
+    }
+#pragma unroll
+    for (int j = 0; j < C::VPT; ++j) {
+        const int q = j * C::NT + tid;
+        const int row = q / C::VPR, c8 = q % C::VPR;
+        *reinterpret_cast<u32x4*>(tile + row * C::PITCH + 8 * c8) = v[j];
+    }
+#pragma unroll
+    for (int j = 0; j < C::WVPT; ++j) {
+        const int q = j * C::NT + tid;
+        if (q < NH * NH / 8) reinterpret_cast<u32x4*>(wl)[q] = wv[j];
+    }
+    __syncthreads();
+
+    // 2. B operand into registers: forward B[k=h][n=g] = W[g][h] (row reads),
+    //    dx B[k=g][n=h] = W[g][h] (transposing reads of W's rows)
+    bf16x8 wf[C::KB][C::NB];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+            if (DX) {
+                wf[kb][nb] = tr_frag(wl + (16 * kb) * NH + 32 * nb, NH, lane);
+            } else {
+                const int g = 32 * nb + (lane & 31), h = 16 * kb + 8 * (lane >> 5);
+                wf[kb][nb] = *reinterpret_cast<const bf16x8*>(wl + g * NH + h);
+            }
+        }
+    __syncthreads();  // W's LDS is reused as the fp32 pe scratch below
+
+    // 3./4. MFMA per owned M-block, results back to LDS
+    const int Q = lane >> 5;
+    for (int b = wave; b < C::MBP; b += WAVES) {
+        f32x16 acc[C::NB];
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[nb][r] = 0.0f;
+        bf16x8 af[C::KB];
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) af[kb] = tr_frag(tile + (16 * kb) * C::PITCH + 32 * b, C::PITCH, lane);
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb)
+                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], wf[kb][nb], acc[nb], 0, 0, 0);
+        // D register r of lane half Q: channel 32b + 8(r/4) + 4Q + r%4, head 32nb + lane%32
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+            const int g = 32 * nb + (lane & 31);
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int cl = 32 * b + 8 * a + 4 * Q;  // 4 consecutive channels, all nope or all pe
+                const int cg = c_base + cl;
+                if (cg < nope) {
+                    uint2 o;
+                    o.x = pack2(f32_to_bf16_rne(acc[nb][4 * a]), f32_to_bf16_rne(acc[nb][4 * a + 1]));
+                    o.y = pack2(f32_to_bf16_rne(acc[nb][4 * a + 2]), f32_to_bf16_rne(acc[nb][4 * a + 3]));
+                    *reinterpret_cast<uint2*>(tile + g * C::PITCH + cl) = o;
+                } else {
+                    f32x4 o = {acc[nb][4 * a], acc[nb][4 * a + 1], acc[nb][4 * a + 2], acc[nb][4 * a + 3]};
+                    *reinterpret_cast<f32x4*>(pes + g * pe + (cg - nope)) = o;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // 5. store phase: whole rows of the part; pe pairs rotated here
+    int64_t prow = 0;
+    if (pe > 0 && c_base + CP > nope) prow = table_row(positions, s, table_rows);
+    uint16_t* outs = Out + s * NH * (int64_t)d + c_base;
+#pragma unroll
+    for (int j = 0; j < C::VPT; ++j) {
+        const int q = j * C::NT + tid;
+        const int row = q / C::VPR, c8 = q % C::VPR;
+        const int cl = 8 * c8, cg = c_base + cl;
+        u32x4 o;
+        if (cg < nope) {
+            o = *reinterpret_cast<const u32x4*>(tile + row * C::PITCH + cl);
+        } else {
+            const int i = cg - nope;
+            const bool first = i < h2;
+            const int ii = first ? i : i - h2;
+            const float* own = pes + row * pe + i;
+            const float* par = pes + row * pe + (first ? i + h2 : i - h2);
+            const f32x4 o0 = reinterpret_cast<const f32x4*>(own)[0], o1 = reinterpret_cast<const f32x4*>(own)[1];
+            const f32x4 p0 = reinterpret_cast<const f32x4*>(par)[0], p1 = reinterpret_cast<const f32x4*>(par)[1];
+            const f32x4 c0 = reinterpret_cast<const f32x4*>(rcos + prow * h2 + ii)[0];
+            const f32x4 c1 = reinterpret_cast<const f32x4*>(rcos + prow * h2 + ii)[1];
+            const f32x4 s0 = reinterpret_cast<const f32x4*>(rsin + prow * h2 + ii)[0];
+            const f32x4 s1 = reinterpret_cast<const f32x4*>(rsin + prow * h2 + ii)[1];
+            // forward (turn by -phi): first half  a C + b S, second half b C - a S
+            // dx      (turn by +phi): first half  a C - b S, second half b C + a S
+            const float sg = (first != DX) ? 1.0f : -1.0f;
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                y[e] = o0[e] * c0[e] + sg * (p0[e] * s0[e]);
+                y[4 + e] = o1[e] * c1[e] + sg * (p1[e] * s1[e]);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) o[jj] = pack2(f32_to_bf16_rne(y[2 * jj]), f32_to_bf16_rne(y[2 * jj + 1]));
+        }
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(outs + row * (int64_t)d + cl));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// weight-gradient partial kernel, LDS-staged chunks (nh in {32, 64, 128})
+//
+// Same partition as dw_partial_kernel (block b = tokens [b*T, (b+1)*T), one
+// fp32 partial per block), but the block's data streams through LDS in chunks
+// of (token, CH channels): the dY and O rows of a chunk are read with
+// coalesced 16-byte non-temporal loads (prefetched one chunk ahead in
+// registers), and the MFMA fragments are read from LDS (channels are the
+// contraction axis, so no transpose is needed).  A pe group's rotation
+// partner lies in the same chunk (the pe range never crosses a chunk), so it
+// costs an LDS read, not an HBM read; the chunk's cos/sin rows are staged in
+// LDS too.
+// nh <= 64: the four waves split each chunk's k-steps and hold every output
+// tile; their sums are added in the fixed order (w0 + w2) + (w1 + w3).
+// nh == 128: wave w owns the 2 x 2 tiles (g-blocks 2(w/2)+{0,1}, h-blocks
+// 2(w%2)+{0,1}) over every k-step.
+// ---------------------------------------------------------------------------
+
+template <int NH, int CH>
+struct DwCfg {
+    static constexpr int WAVES = 4, NT = 256;
+    static constexpr int NB = NH / 32;
+    static constexpr bool SPLIT_K = NB <= 2;
+    static constexpr int TG = SPLIT_K ? NB : 2, TH = TG;
+    static constexpr int PITCH = CH + 8;
+    static constexpr int VPR = CH / 8;
+    static constexpr int VPO = NH * VPR;           // vectors per operand per chunk
+    static constexpr int VPT = 2 * VPO / NT;       // vectors per thread per chunk
+    static constexpr int KS = CH / 16;
+    static constexpr int KSW = SPLIT_K ? KS / WAVES : KS;
+    static constexpr int MAX_H2 = CH / 2;
+    static_assert(VPO % NT == 0 && KS % WAVES == 0, "chunk shape");
+};
+
+template <int NH, int CH>
+__global__ __launch_bounds__(256) void dw_chunk_kernel(
+    const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O,
+    const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
+    const int32_t* __restrict__ positions, int64_t sq, int nope, int pe,
+    float* __restrict__ partials, int tokens_per_block) {
+    using C = DwCfg<NH, CH>;
+    // one array: dY chunk, then O chunk; reused at the end for the wave sums
+    __shared__ __attribute__((aligned(16))) uint16_t lbuf[2 * NH * C::PITCH];
+    uint16_t* const dyl = lbuf;
+    uint16_t* const ol = lbuf + NH * C::PITCH;
+    __shared__ __attribute__((aligned(16))) float csl[C::MAX_H2];
+    __shared__ __attribute__((aligned(16))) float snl[C::MAX_H2];
+
+    const int d = nope + pe, h2 = pe >> 1;
+    const int cpt = d / CH;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+    const int gb0 = C::SPLIT_K ? 0 : 2 * (wave >> 1);
+    const int hb0 = C::SPLIT_K ? 0 : 2 * (wave & 1);
+
+    const int64_t s_begin = (int64_t)blockIdx.x * tokens_per_block;
+    int64_t s_end = s_begin + tokens_per_block;
+    if (s_end > sq) s_end = sq;
+    const int nchunks = (int)(s_end - s_begin) * cpt;
+
+    f32x16 acc[C::TG][C::TH];
+#pragma unroll
+    for (int a = 0; a < C::TG; ++a)
+#pragma unroll
+        for (int b = 0; b < C::TH; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+    u32x4 v[C::VPT];
+    f32x4 cv = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+    auto load_chunk = [&](int k) {
+        const int64_t s = s_begin + k / cpt;
+        const int part = k % cpt;
+        const int64_t rowbase = s * NH * (int64_t)d + part * CH;
+#pragma unroll
+        for (int j = 0; j < C::VPT; ++j) {
+            const int q = j * C::NT + tid;
+            const int op = q / C::VPO;               // 0: dY, 1: O (compile-time per j)
+            const int rem = q % C::VPO;
+            const int row = rem / C::VPR, c8 = rem % C::VPR;
+            const uint16_t* src = (op == 0 ? dY : O) + rowbase + row * (int64_t)d + 8 * c8;
+            v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+        }
+        if (pe > 0 && (part + 1) * CH > nope && tid < (h2 >> 2)) {
+            const int64_t prow = table_row(positions, s, table_rows);
+            cv = reinterpret_cast<const f32x4*>(rcos + prow * h2)[tid];
+            sv = reinterpret_cast<const f32x4*>(rsin + prow * h2)[tid];
+        }
+    };
+
+    if (nchunks > 0) load_chunk(0);
+    for (int k = 0; k < nchunks; ++k) {
+        const int part = k % cpt;
+        __syncthreads();  // every wave is done with the previous chunk
+#pragma unroll
+        for (int j = 0; j < C::VPT; ++j) {
+            const int q = j * C::NT + tid;
+            const int op = q / C::VPO;
+            const int rem = q % C::VPO;
+            const int row = rem / C::VPR, c8 = rem % C::VPR;
+            *reinterpret_cast<u32x4*>((op == 0 ? dyl : ol) + row * C::PITCH + 8 * c8) = v[j];
+        }
+        const bool chunk_pe = pe > 0 && (part + 1) * CH > nope;
+        if (chunk_pe && tid < (h2 >> 2)) {
+            reinterpret_cast<f32x4*>(csl)[tid] = cv;
+            reinterpret_cast<f32x4*>(snl)[tid] = sv;
+        }
+        __syncthreads();
+        if (k + 1 < nchunks) load_chunk(k + 1);  // in flight during the compute
+
+#pragma unroll
+        for (int kk = 0; kk < C::KSW; ++kk) {
+            const int t = C::SPLIT_K ? wave + C::WAVES * kk : kk;
+            const int c = 16 * t + 8 * half;          // channel within the chunk
+            const int cg = part * CH + c;             // channel within the head
+            bf16x8 a[C::TG];
+#pragma unroll
+            for (int tg = 0; tg < C::TG; ++tg)
+                a[tg] = *reinterpret_cast<const bf16x8*>(dyl + (32 * (gb0 + tg) + (lane & 31)) * C::PITCH + c);
+            const bool step_pe = chunk_pe && part * CH + 16 * t + 16 > nope;  // wave-uniform
+            if (!step_pe) {
+#pragma unroll
+                for (int th = 0; th < C::TH; ++th) {
+                    const bf16x8 b = *reinterpret_cast<const bf16x8*>(ol + (32 * (hb0 + th) + (lane & 31)) * C::PITCH + c);
+#pragma unroll
+                    for (int tg = 0; tg < C::TG; ++tg)
+                        acc[tg][th] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tg], b, acc[tg][th], 0, 0, 0);
+                }
+            } else {
+                const bool pe_grp = cg >= nope;
+                const bool first = cg < nope + h2;
+                const int i0 = first ? cg - nope : cg - nope - h2;
+                const int cpart = first ? c + h2 : c - h2;
+                const float sgn = first ? 1.0f : -1.0f;
+                float cs[8], sn[8];
+                if (pe_grp) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        cs[e] = csl[i0 + e];
+                        sn[e] = sgn * snl[i0 + e];
+                    }
+                }
+#pragma unroll
+                for (int th = 0; th < C::TH; ++th) {
+                    const int h = 32 * (hb0 + th) + (lane & 31);
+                    const u32x4 own = *reinterpret_cast<const u32x4*>(ol + h * C::PITCH + c);
+                    u32x4 hi = own, lo = {0u, 0u, 0u, 0u};
+                    if (pe_grp) {
+                        const u32x4 par = *reinterpret_cast<const u32x4*>(ol + h * C::PITCH + cpart);
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            uint32_t hw[2], lw[2];
+#pragma unroll
+                            for (int e = 0; e < 2; ++e) {
+                                const int kx = 2 * jj + e;
+                                const float xa = bf16_to_f32((own[jj] >> (16 * e)) & 0xffffu);
+                                const float xb = bf16_to_f32((par[jj] >> (16 * e)) & 0xffffu);
+                                const float x = xa * cs[kx] + xb * sn[kx];
+                                const uint32_t xh = f32_to_bf16_rne(x);
+                                hw[e] = xh;
+                                lw[e] = f32_to_bf16_rne(x - bf16_to_f32(xh));
+                            }
+                            hi[jj] = pack2(hw[0], hw[1]);
+                            lo[jj] = pack2(lw[0], lw[1]);
+                        }
+                    }
+                    const bf16x8 bh = as_bf16x8(hi), bl = as_bf16x8(lo);
+#pragma unroll
+                    for (int tg = 0; tg < C::TG; ++tg) {
+                        acc[tg][th] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tg], bh, acc[tg][th], 0, 0, 0);
+                        acc[tg][th] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tg], bl, acc[tg][th], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+
+    float* part_out = partials + (int64_t)blockIdx.x * NH * NH;
+    if constexpr (C::SPLIT_K) {
+        // fixed-order sum of the four waves, (w0 + w2) + (w1 + w3), in the
+        // chunk buffers (2 x TG x TH x 16 x 64 floats fit in dyl + ol)
+        float* red = reinterpret_cast<float*>(lbuf);
+        static_assert(2 * C::TG * C::TH * 16 * 64 * 4 <= (int)sizeof(lbuf), "reduction area");
+        auto slot = [&](int w2, int tg, int th, int r) -> float& {
+            return red[(((w2 * C::TG + tg) * C::TH + th) * 16 + r) * 64 + lane];
+        };
+        __syncthreads();
+        if (wave >= 2) {
+#pragma unroll
+            for (int tg = 0; tg < C::TG; ++tg)
+#pragma unroll
+                for (int th = 0; th < C::TH; ++th)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) slot(wave - 2, tg, th, r) = acc[tg][th][r];
+        }
+        __syncthreads();
+        if (wave < 2) {
+#pragma unroll
+            for (int tg = 0; tg < C::TG; ++tg)
+#pragma unroll
+                for (int th = 0; th < C::TH; ++th)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[tg][th][r] += slot(wave, tg, th, r);
+        }
+        __syncthreads();
+        if (wave == 1) {
+#pragma unroll
+            for (int tg = 0; tg < C::TG; ++tg)
+#pragma unroll
+                for (int th = 0; th < C::TH; ++th)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) slot(0, tg, th, r) = acc[tg][th][r];
+        }
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int tg = 0; tg < C::TG; ++tg)
+#pragma unroll
+            for (int th = 0; th < C::TH; ++th)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[tg][th][r] += slot(0, tg, th, r);
+    }
+#pragma unroll
+    for (int tg = 0; tg < C::TG; ++tg)
+#pragma unroll
+        for (int th = 0; th < C::TH; ++th) {
+            const int h = 32 * (hb0 + th) + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int g = 32 * (gb0 + tg) + 8 * (r >> 2) + 4 * half + (r & 3);
+                part_out[g * NH + h] = acc[tg][th][r];
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // host-side launchers (argument checks are done by the caller)
 // ---------------------------------------------------------------------------
 
@@ -557,8 +991,52 @@ static hipError_t launch_mix_t(const MixArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// token-part kernel: one workgroup per (token, CP-channel part)
+template <int NH, int CP, int WAVES, bool DX>
+static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
+    using C = PartCfg<NH, CP, WAVES>;
+    const int d = a.nope + a.pe;
+    const int cpt = d / CP;
+    const size_t lds = C::lds_bytes(a.pe);
+    static bool attr_done = false;  // idempotent; a race only repeats the call
+    if (!attr_done) {
+        const size_t lds_max = C::lds_bytes(CP);
+        if (lds_max > 65536) {
+            hipError_t e = hipFuncSetAttribute((const void*)mix_part_kernel<NH, CP, WAVES, DX>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
+            if (e != hipSuccess) return e;
+        }
+        attr_done = true;
+    }
+    hipLaunchKernelGGL((mix_part_kernel<NH, CP, WAVES, DX>), dim3((unsigned)(a.sq * cpt)),
+                       dim3(64 * WAVES), lds, stream, a.X, a.W, a.rcos, a.rsin, a.table_rows,
+                       a.positions, a.nope, a.pe, cpt, a.Out);
+    return hipGetLastError();
+}
+
+// Channel-part width of the token-part kernel for this shape, or 0 when the
+// shape needs the general kernel: nh must be 32, 64 or 128, the part must
+// divide d, hold the whole pe range, and the grid must stay below 2^31.
+int mix_part_width(int64_t sq, int nh, int nope, int pe) {
+    if (nh != 32 && nh != 64 && nh != 128) return 0;
+    const int d = nope + pe;
+    const int cands[2] = {nh == 128 ? 128 : 256, 128};
+    for (int cp : cands) {
+        if (d % cp != 0 || pe > cp) continue;
+        if (sq * (int64_t)(d / cp) >= ((int64_t)1 << 31)) return 0;
+        return cp;
+    }
+    return 0;
+}
+
 template <bool DX>
 static hipError_t launch_mix_dx(const MixArgs& a, hipStream_t stream) {
+    const int cp = a.force_general ? 0 : mix_part_width(a.sq, a.nh, a.nope, a.pe);
+    if (cp == 256 && a.nh == 64) return launch_part_t<64, 256, 4, DX>(a, stream);
+    if (cp == 128 && a.nh == 64) return launch_part_t<64, 128, 4, DX>(a, stream);
+    if (cp == 256 && a.nh == 32) return launch_part_t<32, 256, 4, DX>(a, stream);
+    if (cp == 128 && a.nh == 32) return launch_part_t<32, 128, 4, DX>(a, stream);
+    if (cp == 128 && a.nh == 128) return launch_part_t<128, 128, 4, DX>(a, stream);
     if (a.nh <= 16) return launch_mix_t<16, 2, DX>(a, stream);
     if (a.nh <= 32) return launch_mix_t<32, 2, DX>(a, stream);
     if (a.nh <= 64) return launch_mix_t<64, 2, DX>(a, stream);
@@ -582,13 +1060,27 @@ int64_t dw_num_blocks(int64_t sq, int nh) {
     return (sq + t - 1) / t;
 }
 
+// Chunk width of the LDS-staged weight-gradient kernel, or 0 for the direct kernel.
+int dw_chunk_width(int nh, int nope, int pe) {
+    if (nh != 32 && nh != 64 && nh != 128) return 0;
+    const int d = nope + pe;
+    return (d % 128 == 0 && pe <= 128) ? 128 : 0;
+}
+
 template <int NHP>
 static hipError_t launch_dw_t(const DwArgs& a, hipStream_t stream) {
     const int tpb = dw_tokens_per_block(a.sq, a.nh);
     const int64_t nb = dw_num_blocks(a.sq, a.nh);
-    hipLaunchKernelGGL((dw_partial_kernel<NHP>), dim3((unsigned)nb), dim3(256), 0, stream, a.dY,
-                       a.O, a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe,
-                       a.partials, tpb);
+    const int ch = a.force_general ? 0 : dw_chunk_width(a.nh, a.nope, a.pe);
+    if (ch == 128 && a.nh == NHP && (NHP == 32 || NHP == 64 || NHP == 128)) {
+        hipLaunchKernelGGL((dw_chunk_kernel<(NHP < 32 ? 32 : NHP), 128>), dim3((unsigned)nb), dim3(256), 0,
+                           stream, a.dY, a.O, a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nope,
+                           a.pe, a.partials, tpb);
+    } else {
+        hipLaunchKernelGGL((dw_partial_kernel<NHP>), dim3((unsigned)nb), dim3(256), 0, stream, a.dY,
+                           a.O, a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe,
+                           a.partials, tpb);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t ne = (int64_t)a.nh * a.nh;

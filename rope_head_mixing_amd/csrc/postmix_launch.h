@@ -19,6 +19,7 @@ struct MixArgs {
     uint16_t* Out;          // Y or dO
     int n_cu;               // compute units of the device
     int waves_per_cu;       // resident single-wave workgroups to aim for per CU
+    bool force_general;     // use the general (persistent) kernel for every shape
 };
 
 struct DwArgs {
@@ -32,9 +33,11 @@ struct DwArgs {
     int nh, nope, pe;
     float* dW;
     float* partials;        // [dw_num_blocks(sq, nh), nh, nh] fp32 workspace
+    bool force_general;     // use the direct-load kernel for every shape
 };
 
 hipError_t launch_mix(const MixArgs& a, bool dx, hipStream_t stream);
+int mix_part_width(int64_t sq, int nh, int nope, int pe);
 hipError_t launch_dw(const DwArgs& a, hipStream_t stream);
 hipError_t launch_rope_table(double theta, int pe, int64_t rows, float* cos_out, float* sin_out,
                              int n_cu, hipStream_t stream);
@@ -43,5 +46,6 @@ hipError_t launch_rope_table(double theta, int pe, int64_t rows, float* cos_out,
 // summation order (and therefore every bit of dW) does not depend on the GPU.
 int dw_tokens_per_block(int64_t sq, int nh);
 int64_t dw_num_blocks(int64_t sq, int nh);
+int dw_chunk_width(int nh, int nope, int pe);
 
 }  // namespace pm

@@ -67,6 +67,8 @@ def lib():
     L.postmix_status_string.restype = ctypes.c_char_p
     L.postmix_last_error.argtypes = []
     L.postmix_last_error.restype = ctypes.c_char_p
+    L.postmix_set_general_kernels.argtypes = [ctypes.c_int]
+    L.postmix_set_general_kernels.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -173,6 +175,11 @@ def postmix_bwd_dw(dY, O, rope_cos, rope_sin, positions, nope: int, pe: int, out
                                 dW.data_ptr(), workspace.data_ptr(), ws_bytes,
                                 _stream_handle(dY.device)))
     return dW
+
+
+def postmix_set_general_kernels(enable: bool) -> bool:
+    """Route fwd/dx through the general kernel for every shape; returns the previous setting."""
+    return bool(lib().postmix_set_general_kernels(1 if enable else 0))
 
 
 def postmix_rope_table(theta: float, pe: int, table_rows: int, device=None):

@@ -108,6 +108,15 @@ def test_02_tiny_workload():
     full_check(synthetic.CASES["tiny"])
 
 
+@pytest.fixture(params=["tiled", "general"])
+def kernel_policy(request):
+    """Run a test with the default (tiled where the shape allows) kernels, and
+    again with every shape forced onto the general kernels."""
+    prev = P().postmix_set_general_kernels(request.param == "general")
+    yield request.param
+    P().postmix_set_general_kernels(prev)
+
+
 @pytest.mark.parametrize("sq,nh,nope,pe,off", [
     (128, 4, 48, 16, 0),       # the (128, 4, 64) shape the pages' tests single out
     (67, 64, 448, 64, 16384),  # production widths, ragged token count
@@ -119,12 +128,43 @@ def test_02_tiny_workload():
     (21, 33, 8, 32, 77),       # nh just past a 32-head block
     (9, 96, 64, 16, 31),       # nh = 96 (three 32-head output blocks)
     (5, 1, 8, 16, 2),          # a single head
+    (25, 32, 192, 64, 9),      # nh = 32, one 256-channel part
+    (11, 64, 320, 64, 500),    # d = 384: 128-channel parts
+    (7, 64, 384, 128, 3),      # pe = 128
+    (13, 64, 432, 80, 4000),   # nope not a multiple of 32: an M-block straddles nope
+    (6, 128, 192, 64, 17),     # nh = 128 with two 128-channel parts
+    (3, 64, 0, 256, 100),      # every channel rotated, pe = one whole part
 ])
-def test_small_shapes(sq, nh, nope, pe, off):
+def test_small_shapes(sq, nh, nope, pe, off, kernel_policy):
     full_check(synthetic.case(sq, nh, nope, pe, seed=1000 + sq + nh, pos_offset=off))
 
 
-def test_forward_only_workload_sq1024():
+@pytest.mark.parametrize("sq,nh,nope,pe", [(70, 64, 448, 64), (21, 128, 448, 64), (30, 32, 432, 80)])
+def test_tiled_and_general_kernels_agree(sq, nh, nope, pe):
+    """Both kernel families on the same inputs: the MFMA inputs and k order are
+    the same, so nope outputs agree bitwise; rotated outputs may differ by the
+    fp32 evaluation order of the rotation (one bf16 ulp at most)."""
+    c = synthetic.case(sq, nh, nope, pe, seed=777, pos_offset=16384)
+    dv = Dev(c)
+    prev = P().postmix_set_general_kernels(False)
+    try:
+        Y1, dO1, dW1 = gu.host_bits(dv.fwd()), gu.host_bits(dv.dx()), dv.dw().cpu().numpy()
+        P().postmix_set_general_kernels(True)
+        Y2, dO2, dW2 = gu.host_bits(dv.fwd()), gu.host_bits(dv.dx()), dv.dw().cpu().numpy()
+    finally:
+        P().postmix_set_general_kernels(prev)
+    np.testing.assert_array_equal(Y1[..., :nope], Y2[..., :nope])
+    np.testing.assert_array_equal(dO1[..., :nope], dO2[..., :nope])
+    for a, b in [(Y1, Y2), (dO1, dO2)]:
+        fa, fb = gu.bf16_to_f64(a[..., nope:]), gu.bf16_to_f64(b[..., nope:])
+        # one bf16 ulp is at most 2^-7 of the value
+        assert np.all(np.abs(fa - fb) <= 2.0 ** -7 * np.abs(fb) + 1e-30), \
+            "rotated outputs differ by more than one bf16 ulp"
+    rel = np.linalg.norm(dW1 - dW2) / np.linalg.norm(dW2)
+    assert rel < 1e-5, rel
+
+
+def test_forward_only_workload_sq1024(kernel_policy):
     full_check(synthetic.CASES["fwd_1k"], ops=("fwd",))
 
 
