@@ -31,13 +31,13 @@ METRIC = "postmix fwd/bwd µs + achieved HBM GB/s (% peak), sq=16384 nh=64 d=512
 PEAK_GBPS = 8000.0  # MI355X HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "rope_head_mixing_amd", "csrc", "postmix_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-# The pages' own figures for this workload (another GPU; context only).
 # kernels behind each op at nh=64, d=512 (tiled path)
 KERNELS_NH64 = {
-    "fwd": "mix_part_kernel<64, 256, 4, false>",
-    "bwd_dx": "mix_part_kernel<64, 256, 4, true>",
+    "fwd": "mix_part_kernel<64, 256, 8, false, false>",
+    "bwd_dx": "mix_part_kernel<64, 256, 8, true, false>",
     "bwd_dw": "dw_chunk_kernel<64, 128> + dw_reduce_kernel",
 }
+# The pages' own figures for this workload (another GPU; context only).
 PAGES_CONTEXT = {
     "hardware": "1x B30Z (sm10.3)",
     "fwd_us_unfused_to_fused": [643.7, 459.4],
@@ -184,7 +184,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)  # ~35 ms: lets the clocks settle
     ap.add_argument("--workload", default="prod",
                     help="prod (default) or another key of synthetic.CASES")
     ap.add_argument("--no-cpu-baseline", action="store_true")

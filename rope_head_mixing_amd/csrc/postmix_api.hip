@@ -162,6 +162,7 @@ int mix_common(const char* xname, const pm_bf16* X, const pm_bf16* W, const floa
     a.n_cu = n_cu;
     a.waves_per_cu = 16;
     a.force_general = g_force_general.load(std::memory_order_relaxed) != 0;
+    a.mix_persistent = false;
     hipError_t e = pm::launch_mix(a, dx, (hipStream_t)stream);
     if (e != hipSuccess) return fail(PM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -539,40 +539,41 @@ __global__ __launch_bounds__(256) void rope_table_kernel(double theta, int pe, i
 // ---------------------------------------------------------------------------
 // head-mix kernel, token-part tiles (forward and input gradient), nh in {32, 64, 128}
 //
-// One workgroup per (token s, channel part of CP channels): the [nh x CP] tile
-// is contiguous per row, so it is read with 16-byte non-temporal loads exactly
-// like a copy, staged in LDS, mixed on MFMA and written back with 16-byte
-// non-temporal stores of whole rows.
-//   1. tile -> LDS; W -> LDS (once per workgroup).
-//   2. each wave copies the B operand (W^T for the forward, W for dx) from
-//      LDS into registers.
-//   3. each wave owns M-blocks of 32 channels.  The A operand (rows =
-//      channels, k = heads) is read with the gfx950 transposing LDS load
-//      ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives
-//      T[k0+e][c0+i] for e = 0..3 when source lane j points at
-//      T[k0 + j/4][c0 + 4*(j%4)].  Two such loads give the 8 k-values a lane
-//      contributes to v_mfma_f32_32x32x16_bf16.
-//   4. results of nope channels are rounded to bf16 and written over the
-//      wave's own tile columns; results of pe channels go to an fp32 LDS
-//      scratch (which reuses W's LDS after a barrier).
-//   5. the store phase rotates the pe pairs (fp32, partner read from the
-//      scratch), rounds, and writes every row of the part to HBM.
+// A tile is (token s, channel part of CP channels): [nh x CP], contiguous per
+// row, read with 16-byte non-temporal loads like a copy and written back the
+// same way.  Workgroups loop over tiles (tile = blockIdx.x + k*gridDim.x); the
+// next tile's loads are issued into registers before the current tile is
+// computed, so they are in flight during the compute and the store.  With a
+// grid of one workgroup per tile the loop runs once.
+//   setup: W -> LDS (rows padded) -> each wave copies its B operand (W^T for
+//          the forward, W for dx) into registers.  W's LDS is then reused as
+//          the fp32 pe scratch.
+//   tile:  registers -> LDS tile; each wave owns M-blocks of 32 channels; the
+//          A operand (rows = channels, k = heads) comes from the gfx950
+//          transposing LDS load ds_read_b64_tr_b16 (in each group of 16
+//          lanes, lane i receives T[k0+e][c0+i], e = 0..3, when source lane j
+//          points at T[k0 + j/4][c0 + 4*(j%4)]); nope results are rounded and
+//          written over the wave's own tile columns, pe results go to the fp32
+//          scratch; the store phase rotates the pe pairs and writes the rows.
 // ---------------------------------------------------------------------------
 
 template <int NH, int CP, int WAVES>
 struct PartCfg {
     static constexpr int KB = NH / 16, NB = NH / 32, NT = 64 * WAVES;
-    static constexpr int PITCH = CP + 8;                 // bf16 elements per LDS row
+    static constexpr int PITCH = CP + 8;                 // bf16 elements per LDS tile row
+    static constexpr int WPITCH = NH + 8;                // bf16 elements per LDS row of W
     static constexpr int VPR = CP / 8;                   // 16-byte vectors per tile row
     static constexpr int VPT = NH * VPR / NT;            // vectors per thread
-    static constexpr int WVPT = (NH * NH / 8 + NT - 1) / NT;
+    static constexpr int WVPR = NH / 8;                  // 16-byte vectors per row of W
+    static constexpr int WVPT = (NH * WVPR + NT - 1) / NT;
     static constexpr int MBP = CP / 32;                  // M-blocks per part
     static_assert(NH % 32 == 0 && CP % 32 == 0 && (NH * VPR) % NT == 0, "part tile shape");
-    static size_t lds_bytes(int pe) {
-        const size_t tile = (size_t)NH * PITCH * 2;
-        const size_t w = (size_t)NH * NH * 2, p = (size_t)NH * pe * 4;
-        return tile + (w > p ? w : p);
+    __host__ __device__ static size_t aux_bytes(int pe) {
+        const size_t w = (size_t)NH * WPITCH * 2, p = (size_t)NH * (pe + 4) * 4;
+        return w > p ? w : p;
     }
+    // tile, then W / pe scratch, then this tile's cos and sin rows (pe/2 floats each)
+    __host__ __device__ static size_t lds_bytes(int pe) { return (size_t)NH * PITCH * 2 + aux_bytes(pe) + (size_t)pe * 4; }
 };
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -595,144 +596,161 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* base, int pitch, int l
     return as_bf16x8(v);
 }
 
-template <int NH, int CP, int WAVES, bool DX>
+template <int NH, int CP, int WAVES, bool DX, bool PERSIST>
 __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
-    const int32_t* __restrict__ positions, int nope, int pe, int cpt,
+    const int32_t* __restrict__ positions, int nope, int pe, int cpt, int64_t n_tiles,
     uint16_t* __restrict__ Out) {
     using C = PartCfg<NH, CP, WAVES>;
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint16_t* tile = smem;                                   // [NH][PITCH] bf16
-    uint16_t* wl = smem + NH * C::PITCH;                     // [NH][NH] bf16, then:
-    float* pes = reinterpret_cast<float*>(wl);               // [NH][pe] fp32
+    uint16_t* wl = smem + NH * C::PITCH;                     // [NH][WPITCH] bf16, then:
+    float* pes = reinterpret_cast<float*>(wl);               // [NH][pe + 4] fp32
+    const int pes_pitch = pe + 4;
+    float* csl = reinterpret_cast<float*>(reinterpret_cast<char*>(wl) + C::aux_bytes(pe));  // [pe/2]
+    float* snl = csl + (pe >> 1);                                                            // [pe/2]
 
     const int d = nope + pe;
     const int h2 = pe >> 1;
-    const int64_t s = blockIdx.x / cpt;
-    const int part = blockIdx.x - (int)(s * cpt);
-    const int c_base = part * CP;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint16_t* xs = X + s * NH * (int64_t)d + c_base;
 
-    // 1. loads: tile rows (contiguous CP channels each) and W
+    int64_t t = blockIdx.x;
     u32x4 v[C::VPT];
+    f32x4 rope_v = {0.f, 0.f, 0.f, 0.f};  // cos (tid < pe/8) or sin (pe/8 <= tid < pe/4) of this tile
+    auto load_tile = [&](int64_t tt) {
+        const int64_t s = tt / cpt;
+        const int part = (int)(tt - s * cpt);
+        const uint16_t* xs = X + s * NH * (int64_t)d + part * CP;
+        if (pe > 0 && (part + 1) * CP > nope && tid < (pe >> 2)) {
+            const int64_t prow = table_row(positions, s, table_rows);
+            const int q4 = tid % (pe >> 3);
+            rope_v = reinterpret_cast<const f32x4*>((tid < (pe >> 3) ? rcos : rsin) + prow * h2)[q4];
+        }
 #pragma unroll
-    for (int j = 0; j < C::VPT; ++j) {
-        const int q = j * C::NT + tid;
-        const int row = q / C::VPR, c8 = q % C::VPR;
-        v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xs + row * (int64_t)d + 8 * c8));
-    }
-    u32x4 wv[C::WVPT];
+        for (int j = 0; j < C::VPT; ++j) {
+            const int q = j * C::NT + tid;
+            const int row = q / C::VPR, c8 = q % C::VPR;
+            v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xs + row * (int64_t)d + 8 * c8));
+        }
+    };
+    if (t < n_tiles) load_tile(t);  // first tile's loads overlap the W setup
+
+    // setup: W -> LDS -> B operand in registers
 #pragma unroll
     for (int j = 0; j < C::WVPT; ++j) {
         const int q = j * C::NT + tid;
-        if (q < NH * NH / 8) wv[j] = reinterpret_cast<const u32x4*>(W)[q];
-    }
-#pragma unroll
-    for (int j = 0; j < C::VPT; ++j) {
-        const int q = j * C::NT + tid;
-        const int row = q / C::VPR, c8 = q % C::VPR;
-        *reinterpret_cast<u32x4*>(tile + row * C::PITCH + 8 * c8) = v[j];
-    }
-#pragma unroll
-    for (int j = 0; j < C::WVPT; ++j) {
-        const int q = j * C::NT + tid;
-        if (q < NH * NH / 8) reinterpret_cast<u32x4*>(wl)[q] = wv[j];
+        if (q < NH * C::WVPR) {
+            const int row = q / C::WVPR, c8 = q % C::WVPR;
+            *reinterpret_cast<u32x4*>(wl + row * C::WPITCH + 8 * c8) = reinterpret_cast<const u32x4*>(W)[q];
+        }
     }
     __syncthreads();
-
-    // 2. B operand into registers: forward B[k=h][n=g] = W[g][h] (row reads),
-    //    dx B[k=g][n=h] = W[g][h] (transposing reads of W's rows)
     bf16x8 wf[C::KB][C::NB];
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
-            if (DX) {
-                wf[kb][nb] = tr_frag(wl + (16 * kb) * NH + 32 * nb, NH, lane);
-            } else {
+            if (DX) {  // B[k=g][n=h] = W[g][h]
+                wf[kb][nb] = tr_frag(wl + (16 * kb) * C::WPITCH + 32 * nb, C::WPITCH, lane);
+            } else {   // B[k=h][n=g] = W[g][h]
                 const int g = 32 * nb + (lane & 31), h = 16 * kb + 8 * (lane >> 5);
-                wf[kb][nb] = *reinterpret_cast<const bf16x8*>(wl + g * NH + h);
+                wf[kb][nb] = *reinterpret_cast<const bf16x8*>(wl + g * C::WPITCH + h);
             }
         }
-    __syncthreads();  // W's LDS is reused as the fp32 pe scratch below
+    __syncthreads();  // W's LDS becomes the pe scratch
 
-    // 3./4. MFMA per owned M-block, results back to LDS
     const int Q = lane >> 5;
-    for (int b = wave; b < C::MBP; b += WAVES) {
-        f32x16 acc[C::NB];
+    for (; t < n_tiles; t += (PERSIST ? (int64_t)gridDim.x : n_tiles)) {
+        const int64_t s = t / cpt;
+        const int part = (int)(t - s * cpt);
+        const int c_base = part * CP;
+
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[nb][r] = 0.0f;
-        bf16x8 af[C::KB];
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) af[kb] = tr_frag(tile + (16 * kb) * C::PITCH + 32 * b, C::PITCH, lane);
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
+        for (int j = 0; j < C::VPT; ++j) {
+            const int q = j * C::NT + tid;
+            const int row = q / C::VPR, c8 = q % C::VPR;
+            *reinterpret_cast<u32x4*>(tile + row * C::PITCH + 8 * c8) = v[j];
+        }
+        const bool tile_pe = pe > 0 && c_base + CP > nope;
+        if (tile_pe && tid < (pe >> 2)) reinterpret_cast<f32x4*>(csl)[tid] = rope_v;  // cos then sin
+        __syncthreads();
+        if (PERSIST && t + gridDim.x < n_tiles) load_tile(t + gridDim.x);  // in flight meanwhile
+
+        for (int b = wave; b < C::MBP; b += WAVES) {
+            f32x16 acc[C::NB];
 #pragma unroll
             for (int nb = 0; nb < C::NB; ++nb)
-                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], wf[kb][nb], acc[nb], 0, 0, 0);
-        // D register r of lane half Q: channel 32b + 8(r/4) + 4Q + r%4, head 32nb + lane%32
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-            const int g = 32 * nb + (lane & 31);
+                for (int r = 0; r < 16; ++r) acc[nb][r] = 0.0f;
+            bf16x8 af[C::KB];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int cl = 32 * b + 8 * a + 4 * Q;  // 4 consecutive channels, all nope or all pe
-                const int cg = c_base + cl;
-                if (cg < nope) {
-                    uint2 o;
-                    o.x = pack2(f32_to_bf16_rne(acc[nb][4 * a]), f32_to_bf16_rne(acc[nb][4 * a + 1]));
-                    o.y = pack2(f32_to_bf16_rne(acc[nb][4 * a + 2]), f32_to_bf16_rne(acc[nb][4 * a + 3]));
-                    *reinterpret_cast<uint2*>(tile + g * C::PITCH + cl) = o;
-                } else {
-                    f32x4 o = {acc[nb][4 * a], acc[nb][4 * a + 1], acc[nb][4 * a + 2], acc[nb][4 * a + 3]};
-                    *reinterpret_cast<f32x4*>(pes + g * pe + (cg - nope)) = o;
+            for (int kb = 0; kb < C::KB; ++kb)
+                af[kb] = tr_frag(tile + (16 * kb) * C::PITCH + 32 * b, C::PITCH, lane);
+#pragma unroll
+            for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+                for (int nb = 0; nb < C::NB; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], wf[kb][nb], acc[nb], 0, 0, 0);
+            // D register r of lane half Q: channel 32b + 8(r/4) + 4Q + r%4, head 32nb + lane%32
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) {
+                const int g = 32 * nb + (lane & 31);
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int cl = 32 * b + 8 * a + 4 * Q;  // 4 consecutive channels, all nope or all pe
+                    const int cg = c_base + cl;
+                    if (cg < nope) {
+                        uint2 o;
+                        o.x = pack2(f32_to_bf16_rne(acc[nb][4 * a]), f32_to_bf16_rne(acc[nb][4 * a + 1]));
+                        o.y = pack2(f32_to_bf16_rne(acc[nb][4 * a + 2]), f32_to_bf16_rne(acc[nb][4 * a + 3]));
+                        *reinterpret_cast<uint2*>(tile + g * C::PITCH + cl) = o;
+                    } else {
+                        f32x4 o = {acc[nb][4 * a], acc[nb][4 * a + 1], acc[nb][4 * a + 2], acc[nb][4 * a + 3]};
+                        *reinterpret_cast<f32x4*>(pes + g * pes_pitch + (cg - nope)) = o;
+                    }
                 }
             }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // 5. store phase: whole rows of the part; pe pairs rotated here
-    int64_t prow = 0;
-    if (pe > 0 && c_base + CP > nope) prow = table_row(positions, s, table_rows);
-    uint16_t* outs = Out + s * NH * (int64_t)d + c_base;
+        // store phase: whole rows of the part; pe pairs rotated here
+        uint16_t* outs = Out + s * NH * (int64_t)d + c_base;
 #pragma unroll
-    for (int j = 0; j < C::VPT; ++j) {
-        const int q = j * C::NT + tid;
-        const int row = q / C::VPR, c8 = q % C::VPR;
-        const int cl = 8 * c8, cg = c_base + cl;
-        u32x4 o;
-        if (cg < nope) {
-            o = *reinterpret_cast<const u32x4*>(tile + row * C::PITCH + cl);
-        } else {
-            const int i = cg - nope;
-            const bool first = i < h2;
-            const int ii = first ? i : i - h2;
-            const float* own = pes + row * pe + i;
-            const float* par = pes + row * pe + (first ? i + h2 : i - h2);
-            const f32x4 o0 = reinterpret_cast<const f32x4*>(own)[0], o1 = reinterpret_cast<const f32x4*>(own)[1];
-            const f32x4 p0 = reinterpret_cast<const f32x4*>(par)[0], p1 = reinterpret_cast<const f32x4*>(par)[1];
-            const f32x4 c0 = reinterpret_cast<const f32x4*>(rcos + prow * h2 + ii)[0];
-            const f32x4 c1 = reinterpret_cast<const f32x4*>(rcos + prow * h2 + ii)[1];
-            const f32x4 s0 = reinterpret_cast<const f32x4*>(rsin + prow * h2 + ii)[0];
-            const f32x4 s1 = reinterpret_cast<const f32x4*>(rsin + prow * h2 + ii)[1];
-            // forward (turn by -phi): first half  a C + b S, second half b C - a S
-            // dx      (turn by +phi): first half  a C - b S, second half b C + a S
-            const float sg = (first != DX) ? 1.0f : -1.0f;
-            float y[8];
+        for (int j = 0; j < C::VPT; ++j) {
+            const int q = j * C::NT + tid;
+            const int row = q / C::VPR, c8 = q % C::VPR;
+            const int cl = 8 * c8, cg = c_base + cl;
+            u32x4 o;
+            if (cg < nope) {
+                o = *reinterpret_cast<const u32x4*>(tile + row * C::PITCH + cl);
+            } else {
+                const int i = cg - nope;
+                const bool first = i < h2;
+                const int ii = first ? i : i - h2;
+                const float* own = pes + row * pes_pitch + i;
+                const float* par = pes + row * pes_pitch + (first ? i + h2 : i - h2);
+                const f32x4 o0 = reinterpret_cast<const f32x4*>(own)[0], o1 = reinterpret_cast<const f32x4*>(own)[1];
+                const f32x4 p0 = reinterpret_cast<const f32x4*>(par)[0], p1 = reinterpret_cast<const f32x4*>(par)[1];
+                const f32x4 c0 = reinterpret_cast<const f32x4*>(csl + ii)[0];
+                const f32x4 c1 = reinterpret_cast<const f32x4*>(csl + ii)[1];
+                const f32x4 s0 = reinterpret_cast<const f32x4*>(snl + ii)[0];
+                const f32x4 s1 = reinterpret_cast<const f32x4*>(snl + ii)[1];
+                // forward (turn by -phi): first half  a C + b S, second half b C - a S
+                // dx      (turn by +phi): first half  a C - b S, second half b C + a S
+                const float sg = (first != DX) ? 1.0f : -1.0f;
+                float y[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                y[e] = o0[e] * c0[e] + sg * (p0[e] * s0[e]);
-                y[4 + e] = o1[e] * c1[e] + sg * (p1[e] * s1[e]);
+                for (int e = 0; e < 4; ++e) {
+                    y[e] = o0[e] * c0[e] + sg * (p0[e] * s0[e]);
+                    y[4 + e] = o1[e] * c1[e] + sg * (p1[e] * s1[e]);
+                }
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) o[jj] = pack2(f32_to_bf16_rne(y[2 * jj]), f32_to_bf16_rne(y[2 * jj + 1]));
             }
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) o[jj] = pack2(f32_to_bf16_rne(y[2 * jj]), f32_to_bf16_rne(y[2 * jj + 1]));
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(outs + row * (int64_t)d + cl));
         }
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(outs + row * (int64_t)d + cl));
+        __syncthreads();  // the tile and the scratch are rewritten next iteration
     }
 }
 
@@ -991,27 +1009,44 @@ static hipError_t launch_mix_t(const MixArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// token-part kernel: one workgroup per (token, CP-channel part)
-template <int NH, int CP, int WAVES, bool DX>
-static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
+// token-part kernel: tiles = (token, CP-channel part); grid = one workgroup per
+// tile, or (persistent) as many workgroups as fit on the device at once
+template <int NH, int CP, int WAVES, bool DX, bool PERSIST>
+static hipError_t launch_part_one(const MixArgs& a, hipStream_t stream) {
     using C = PartCfg<NH, CP, WAVES>;
     const int d = a.nope + a.pe;
     const int cpt = d / CP;
+    const int64_t n_tiles = a.sq * cpt;
     const size_t lds = C::lds_bytes(a.pe);
+    auto kern = mix_part_kernel<NH, CP, WAVES, DX, PERSIST>;
     static bool attr_done = false;  // idempotent; a race only repeats the call
     if (!attr_done) {
         const size_t lds_max = C::lds_bytes(CP);
         if (lds_max > 65536) {
-            hipError_t e = hipFuncSetAttribute((const void*)mix_part_kernel<NH, CP, WAVES, DX>,
+            hipError_t e = hipFuncSetAttribute((const void*)kern,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
             if (e != hipSuccess) return e;
         }
         attr_done = true;
     }
-    hipLaunchKernelGGL((mix_part_kernel<NH, CP, WAVES, DX>), dim3((unsigned)(a.sq * cpt)),
-                       dim3(64 * WAVES), lds, stream, a.X, a.W, a.rcos, a.rsin, a.table_rows,
-                       a.positions, a.nope, a.pe, cpt, a.Out);
+    int64_t grid = n_tiles;
+    if (PERSIST) {
+        int per_cu = 0;
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, 64 * WAVES, lds);
+        if (e != hipSuccess) return e;
+        if (per_cu < 1) per_cu = 1;
+        const int64_t cap = (int64_t)a.n_cu * per_cu;
+        if (grid > cap) grid = cap;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WAVES), lds, stream, a.X, a.W, a.rcos,
+                       a.rsin, a.table_rows, a.positions, a.nope, a.pe, cpt, n_tiles, a.Out);
     return hipGetLastError();
+}
+
+template <int NH, int CP, int WAVES, bool DX>
+static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
+    return a.mix_persistent ? launch_part_one<NH, CP, WAVES, DX, true>(a, stream)
+                            : launch_part_one<NH, CP, WAVES, DX, false>(a, stream);
 }
 
 // Channel-part width of the token-part kernel for this shape, or 0 when the
@@ -1032,9 +1067,9 @@ int mix_part_width(int64_t sq, int nh, int nope, int pe) {
 template <bool DX>
 static hipError_t launch_mix_dx(const MixArgs& a, hipStream_t stream) {
     const int cp = a.force_general ? 0 : mix_part_width(a.sq, a.nh, a.nope, a.pe);
-    if (cp == 256 && a.nh == 64) return launch_part_t<64, 256, 4, DX>(a, stream);
+    if (cp == 256 && a.nh == 64) return launch_part_t<64, 256, 8, DX>(a, stream);
     if (cp == 128 && a.nh == 64) return launch_part_t<64, 128, 4, DX>(a, stream);
-    if (cp == 256 && a.nh == 32) return launch_part_t<32, 256, 4, DX>(a, stream);
+    if (cp == 256 && a.nh == 32) return launch_part_t<32, 256, 8, DX>(a, stream);
     if (cp == 128 && a.nh == 32) return launch_part_t<32, 128, 4, DX>(a, stream);
     if (cp == 128 && a.nh == 128) return launch_part_t<128, 128, 4, DX>(a, stream);
     if (a.nh <= 16) return launch_mix_t<16, 2, DX>(a, stream);
