@@ -98,7 +98,7 @@ def cpu_baseline(case, O, W, dY, pos, target_s: float):
     }
 
 
-def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix):
+def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix, timed=20):
     """Turn rocprofv3 outputs (kernel-trace --stats, --pmc FETCH_SIZE, --pmc
     WRITE_SIZE runs of this script) into profiles/<out_prefix>_*.md and the
     per-launch HBM traffic file read by the benchmark.
@@ -133,9 +133,19 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix
     def short(name):
         return name.split("(")[0].replace("void ", "").replace("pm::", "")
 
+    # per-kernel durations in launch order, to average the timed region (the
+    # last `timed` launches; the earlier ones are the warm-up)
+    launches = collections.defaultdict(list)
+    for r in csv.DictReader(open(one(os.path.join(trace_dir, "**", "*kernel_trace.csv")))):
+        launches[short(r["Kernel_Name"])].append(
+            (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
     rows = []
     for r in stats:
-        rows.append((short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+        n = short(r["Name"])
+        durs = [x[1] for x in sorted(launches.get(n, []))]
+        tail = durs[-timed:] if durs else []
+        rows.append((n, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                     sum(tail) / len(tail) if tail else float("nan"),
                      float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
     traffic = {}
     for (name, grid), fb in fetch.items():
@@ -159,8 +169,10 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix
              "Commands (from the repository root on one MI355X):", "", "```", command_note.strip(),
              "```", "", f"Kernel source sha256[:16]: `{doc['kernel_source_sha']}`", "",
              "## Kernel durations (rocprofv3 --kernel-trace --stats)", "",
-             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
-    lines += [f"| `{n}` | {c} | {a:.1f} | {mn:.1f} | {mx:.1f} |" for n, c, a, mn, mx in rows]
+             f"`timed avg` is the mean of the last {timed} launches of each kernel, the benchmark's "
+             "timed steps; `avg` includes the warm-up launches.", "",
+             "| kernel | calls | avg us | timed avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    lines += [f"| `{n}` | {c} | {a:.1f} | {ta:.1f} | {mn:.1f} | {mx:.1f} |" for n, c, a, ta, mn, mx in rows]
     lines += ["", "## HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)", "",
               f"Calibration on the benchmark's plain 1 GiB device copy (`{short(copy_key[0])}`): "
               f"FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f} gives 1 GiB each.", "",
