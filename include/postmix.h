@@ -39,7 +39,9 @@
  *    input range is rejected.
  *  - Limits: 1 <= nh <= 128; nope >= 0 with nope % 8 == 0; pe >= 0 with
  *    pe % 16 == 0; nope + pe > 0; sq >= 0.  sq == 0 is a successful no-op.
- *  - Activation, table and workspace pointers must be 16-byte aligned.
+ *  - Activation, table and workspace pointers must be 16-byte aligned; W must
+ *    be 2-byte aligned (the tiled kernels, which read W in 16-byte vectors,
+ *    are used only when W is 16-byte aligned).
  *  - Return 0 on success, else a negative PM_ERR_* code; a thread-local
  *    message naming the offending argument is available from
  *    postmix_last_error().  Arguments are validated before any HIP call.
@@ -126,6 +128,27 @@ int postmix_bwd_dw(const pm_bf16 *dY, const pm_bf16 *O, const float *rope_cos,
                    const int32_t *positions, int64_t sq, int32_t nh,
                    int32_t nope, int32_t pe, float *dW, void *workspace,
                    size_t workspace_bytes, void *stream);
+
+/*
+ * Backward, both gradients in one call: dO as postmix_bwd_dx and dW as
+ * postmix_bwd_dw, from a single pass over dY and O where the shape allows
+ * (nh == 64, nope + pe a multiple of 128, pe <= 128): each (token, channel
+ * chunk) of dY and O is read from HBM once and feeds both the head-mix
+ * gradient and the weight-gradient partials.  That is one full read of dY
+ * fewer than the two separate calls.  Other shapes (or
+ * postmix_set_general_kernels(1)) run the two separate computations.
+ * dO is bitwise the same as postmix_bwd_dx's; dW is deterministic and uses
+ * the same token blocks and reduction as postmix_bwd_dw, but sums each block
+ * in a different order, so the two may differ in the last bits.
+ *   dY, O [sq, nh, nope+pe] bf16, read;  W [nh, nh] bf16, read
+ *   dO    [sq, nh, nope+pe] bf16, written;  dW [nh, nh] fp32, written
+ *   workspace as postmix_bwd_dw (postmix_bwd_dw_workspace_bytes bytes).
+ */
+int postmix_bwd(const pm_bf16 *dY, const pm_bf16 *O, const pm_bf16 *W,
+                const float *rope_cos, const float *rope_sin, int64_t table_rows,
+                const int32_t *positions, int64_t sq, int32_t nh, int32_t nope,
+                int32_t pe, pm_bf16 *dO, float *dW, void *workspace,
+                size_t workspace_bytes, void *stream);
 
 /*
  * RoPE tables from theta: row r (position r), column i < pe/2:

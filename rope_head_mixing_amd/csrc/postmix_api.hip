@@ -265,6 +265,90 @@ int postmix_bwd_dw(const pm_bf16* dY, const pm_bf16* O, const float* rope_cos,
     return ok();
 }
 
+int postmix_bwd(const pm_bf16* dY, const pm_bf16* O, const pm_bf16* W, const float* rope_cos,
+                const float* rope_sin, int64_t table_rows, const int32_t* positions, int64_t sq,
+                int32_t nh, int32_t nope, int32_t pe, pm_bf16* dO, float* dW, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    int rc = check_shape(sq, nh, nope, pe);
+    if (rc) return rc;
+    if (!dW) return fail(PM_ERR_NULL, "dW is NULL");
+    if (((uintptr_t)dW & 3u) != 0) return fail(PM_ERR_ALIGN, "dW is not 4-byte aligned");
+    if (sq == 0) {
+        // no tokens: dO is empty and dW is an empty sum
+        return postmix_bwd_dw(dY, O, rope_cos, rope_sin, table_rows, positions, sq, nh, nope, pe, dW,
+                              workspace, workspace_bytes, stream);
+    }
+    if (!dY) return fail(PM_ERR_NULL, "dY is NULL");
+    if (!O) return fail(PM_ERR_NULL, "O is NULL");
+    if (!W) return fail(PM_ERR_NULL, "W is NULL");
+    if (!dO) return fail(PM_ERR_NULL, "dO is NULL");
+    rc = check_rope_args(rope_cos, rope_sin, table_rows, positions, pe);
+    if (rc) return rc;
+    if (!aligned16(dY)) return fail(PM_ERR_ALIGN, "dY is not 16-byte aligned");
+    if (!aligned16(O)) return fail(PM_ERR_ALIGN, "O is not 16-byte aligned");
+    if (!aligned16(dO)) return fail(PM_ERR_ALIGN, "dO is not 16-byte aligned");
+    if (((uintptr_t)W & 1u) != 0) return fail(PM_ERR_ALIGN, "W is not 2-byte aligned");
+    const size_t need = postmix_bwd_dw_workspace_bytes(sq, nh, nope, pe);
+    if (need > 0 && !workspace) return fail(PM_ERR_NULL, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+        return fail(PM_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(PM_ERR_ALIGN, "workspace is not 16-byte aligned");
+    const size_t act = (size_t)sq * nh * (nope + pe) * sizeof(pm_bf16);
+    const size_t tab = pe ? (size_t)table_rows * (pe / 2) * sizeof(float) : 0;
+    const Range outs[3] = {{"dO", dO, act}, {"dW", dW, (size_t)nh * nh * sizeof(float)},
+                           {"workspace", workspace, need}};
+    const Range ins[6] = {{"dY", dY, act},
+                          {"O", O, act},
+                          {"W", W, (size_t)nh * nh * sizeof(pm_bf16)},
+                          {"rope_cos", pe ? rope_cos : nullptr, tab},
+                          {"rope_sin", pe ? rope_sin : nullptr, tab},
+                          {"positions", pe ? positions : nullptr, (size_t)sq * sizeof(int32_t)}};
+    rc = check_no_overlap(outs, 3, ins, 6);
+    if (rc) return rc;
+    int n_cu = 0;
+    rc = check_device(&n_cu);
+    if (rc) return rc;
+    pm::MixArgs mx;
+    mx.X = dY;
+    mx.W = W;
+    mx.rcos = rope_cos;
+    mx.rsin = rope_sin;
+    mx.table_rows = table_rows;
+    mx.positions = positions;
+    mx.sq = sq;
+    mx.nh = nh;
+    mx.nope = nope;
+    mx.pe = pe;
+    mx.Out = dO;
+    mx.n_cu = n_cu;
+    mx.waves_per_cu = 16;
+    mx.force_general = g_force_general.load(std::memory_order_relaxed) != 0;
+    mx.mix_persistent = false;
+    pm::DwArgs a;
+    a.dY = dY;
+    a.O = O;
+    a.rcos = rope_cos;
+    a.rsin = rope_sin;
+    a.table_rows = table_rows;
+    a.positions = positions;
+    a.sq = sq;
+    a.nh = nh;
+    a.nope = nope;
+    a.pe = pe;
+    a.dW = dW;
+    a.partials = (float*)workspace;
+    a.force_general = mx.force_general;
+    hipError_t e;
+    if (!mx.force_general && ((uintptr_t)W & 15u) == 0 && pm::bwd_fused_applies(nh, nope, pe)) {
+        e = pm::launch_bwd_fused(mx, a, (hipStream_t)stream);
+    } else {
+        e = pm::launch_mix(mx, true, (hipStream_t)stream);
+        if (e == hipSuccess) e = pm::launch_dw(a, (hipStream_t)stream);
+    }
+    if (e != hipSuccess) return fail(PM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int postmix_rope_table(double theta, int32_t pe, int64_t table_rows, float* cos_out,
                        float* sin_out, void* stream) {
     if (!(theta > 0.0)) return fail(PM_ERR_SHAPE, "theta must be > 0");

@@ -989,6 +989,260 @@ __global__ __launch_bounds__(256) void dw_chunk_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// fused backward: input gradient and weight-gradient partials in one pass
+//
+// One read of dY and O serves both gradients: the block partition is the
+// weight gradient's (fixed token blocks, one fp32 partial each), and every
+// (token, 128-channel) chunk of dY and O is staged in LDS once.  From it
+//   - dW:  wave w owns output tile w%4 (g-block tile/2, h-block tile%2) over
+//          the k-steps of parity w/4; the two waves of a tile are added in
+//          the fixed order (w) + (w+4) at the end of the block;
+//   - dx:  wave w owns M-block w%4 and N-block w/4 of the chunk's head mix
+//          dX[c, h] = sum_g dY[g, c] W[g, h] (A = dY^T by transposing LDS
+//          loads, B = W in registers), writes nope results to an LDS output
+//          chunk and pe results to an fp32 scratch; the store phase rotates
+//          the pe pairs by +phi and writes dO rows with non-temporal stores.
+// The dx arithmetic (MFMA inputs, k order, rotation expression) is that of
+// the token-part kernel, so dO is bitwise the same as postmix_bwd_dx's.
+// nh = 64, d a multiple of 128, pe <= 128.
+// ---------------------------------------------------------------------------
+
+template <int NH, int CH>
+struct BwdCfg {
+    static constexpr int WAVES = 8, NT = 512;
+    static constexpr int NB = NH / 32, KB = NH / 16;
+    static constexpr int PITCH = CH + 8;
+    static constexpr int WPITCH = NH + 8;
+    static constexpr int VPR = CH / 8;
+    static constexpr int VPO = NH * VPR;            // vectors per operand per chunk
+    static constexpr int VPT = 2 * VPO / NT;        // vectors (dY + O) per thread per chunk
+    static constexpr int OPT = VPO / NT;            // dO vectors per thread per chunk
+    static constexpr int KS = CH / 16;              // k-steps of the weight gradient per chunk
+    static constexpr int MBC = CH / 32;             // M-blocks of the head mix per chunk
+    static constexpr int NTILE = NB * NB;           // dW output tiles
+    static constexpr int KSET = WAVES / NTILE;      // waves per dW tile
+    static_assert(NH == 64 && MBC * NB == WAVES && KSET == 2 && VPO % NT == 0, "fused shape");
+    __host__ __device__ static size_t aux_bytes(int pe) {
+        const size_t w = (size_t)NH * WPITCH * 2, p = (size_t)NH * (pe + 4) * 4;
+        return w > p ? w : p;
+    }
+    // dY chunk, O chunk, dO chunk, then W / pe scratch, then cos and sin
+    __host__ __device__ static size_t lds_bytes(int pe) {
+        return (size_t)3 * NH * PITCH * 2 + aux_bytes(pe) + (size_t)pe * 4;
+    }
+};
+
+template <int NH, int CH>
+__global__ __launch_bounds__(512, 4) void bwd_fused_kernel(
+    const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O, const uint16_t* __restrict__ W,
+    const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
+    const int32_t* __restrict__ positions, int64_t sq, int nope, int pe,
+    uint16_t* __restrict__ dO, float* __restrict__ partials, int tokens_per_block) {
+    using C = BwdCfg<NH, CH>;
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    uint16_t* dyl = smem;                               // [NH][PITCH]
+    uint16_t* ol = dyl + NH * C::PITCH;                 // [NH][PITCH]
+    uint16_t* dol = ol + NH * C::PITCH;                 // [NH][PITCH]
+    uint16_t* wl = dol + NH * C::PITCH;                 // [NH][WPITCH] bf16, then:
+    float* pes = reinterpret_cast<float*>(wl);          // [NH][pe + 4] fp32
+    const int pes_pitch = pe + 4;
+    float* csl = reinterpret_cast<float*>(reinterpret_cast<char*>(wl) + C::aux_bytes(pe));
+    float* snl = csl + (pe >> 1);
+
+    const int d = nope + pe, h2 = pe >> 1;
+    const int cpt = d / CH;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, Q = half;
+    const int tile = wave % C::NTILE, kset = wave / C::NTILE;
+    const int gb = tile / C::NB, hb = tile % C::NB;
+    const int mb = wave % C::MBC, nb = wave / C::MBC;
+
+    const int64_t s_begin = (int64_t)blockIdx.x * tokens_per_block;
+    int64_t s_end = s_begin + tokens_per_block;
+    if (s_end > sq) s_end = sq;
+    const int nchunks = (int)(s_end - s_begin) * cpt;
+
+    u32x4 v[C::VPT];
+    f32x4 rope_v = {0.f, 0.f, 0.f, 0.f};
+    auto load_chunk = [&](int k) {
+        const int64_t s = s_begin + k / cpt;
+        const int part = k % cpt;
+        const int64_t rowbase = s * NH * (int64_t)d + part * CH;
+#pragma unroll
+        for (int j = 0; j < C::VPT; ++j) {
+            const int q = j * C::NT + tid;
+            const int op = q / C::VPO;               // 0: dY, 1: O (compile-time per j)
+            const int rem = q % C::VPO;
+            const int row = rem / C::VPR, c8 = rem % C::VPR;
+            const uint16_t* src = (op == 0 ? dY : O) + rowbase + row * (int64_t)d + 8 * c8;
+            v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+        }
+        if (pe > 0 && (part + 1) * CH > nope && tid < (pe >> 2)) {
+            const int64_t prow = table_row(positions, s, table_rows);
+            rope_v = reinterpret_cast<const f32x4*>((tid < (pe >> 3) ? rcos : rsin) + prow * h2)[tid % (pe >> 3)];
+        }
+    };
+    if (nchunks > 0) load_chunk(0);
+
+    // W -> LDS -> this wave's dx B operand (B[k=g][n=h] = W[g][h], N-block nb)
+    for (int q = tid; q < NH * NH / 8; q += C::NT) {
+        const int row = q / (NH / 8), c8 = q % (NH / 8);
+        *reinterpret_cast<u32x4*>(wl + row * C::WPITCH + 8 * c8) = reinterpret_cast<const u32x4*>(W)[q];
+    }
+    __syncthreads();
+    bf16x8 wf[C::KB];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) wf[kb] = tr_frag(wl + (16 * kb) * C::WPITCH + 32 * nb, C::WPITCH, lane);
+    __syncthreads();  // W's LDS becomes the pe scratch
+
+    f32x16 acc_w;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_w[r] = 0.0f;
+
+    for (int k = 0; k < nchunks; ++k) {
+        const int64_t s = s_begin + k / cpt;
+        const int part = k % cpt;
+        const int c_base = part * CH;
+        const bool chunk_pe = pe > 0 && c_base + CH > nope;
+#pragma unroll
+        for (int j = 0; j < C::VPT; ++j) {
+            const int q = j * C::NT + tid;
+            const int op = q / C::VPO;
+            const int rem = q % C::VPO;
+            const int row = rem / C::VPR, c8 = rem % C::VPR;
+            *reinterpret_cast<u32x4*>((op == 0 ? dyl : ol) + row * C::PITCH + 8 * c8) = v[j];
+        }
+        if (chunk_pe && tid < (pe >> 2)) reinterpret_cast<f32x4*>(csl)[tid] = rope_v;
+        __syncthreads();
+        if (k + 1 < nchunks) load_chunk(k + 1);  // in flight during the compute and the stores
+
+        // ---- weight gradient: tile (gb, hb), k-steps t = kset, kset + 2, ...
+#pragma unroll
+        for (int t = kset; t < C::KS; t += C::KSET) {
+            const int c = 16 * t + 8 * half;
+            const int cg = c_base + c;
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(dyl + (32 * gb + (lane & 31)) * C::PITCH + c);
+            const int h = 32 * hb + (lane & 31);
+            const u32x4 own = *reinterpret_cast<const u32x4*>(ol + h * C::PITCH + c);
+            const bool step_pe = chunk_pe && c_base + 16 * t + 16 > nope;  // wave-uniform
+            if (!step_pe) {
+                acc_w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(own), acc_w, 0, 0, 0);
+            } else {
+                u32x4 hi = own, lo = {0u, 0u, 0u, 0u};
+                if (cg >= nope) {
+                    const bool first = cg < nope + h2;
+                    const int i0 = first ? cg - nope : cg - nope - h2;
+                    const float sgn = first ? 1.0f : -1.0f;
+                    const u32x4 par = *reinterpret_cast<const u32x4*>(ol + h * C::PITCH + (first ? c + h2 : c - h2));
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        uint32_t hw[2], lw[2];
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const int kx = 2 * jj + e;
+                            const float xa = bf16_to_f32((own[jj] >> (16 * e)) & 0xffffu);
+                            const float xb = bf16_to_f32((par[jj] >> (16 * e)) & 0xffffu);
+                            const float x = xa * csl[i0 + kx] + xb * (sgn * snl[i0 + kx]);
+                            const uint32_t xh = f32_to_bf16_rne(x);
+                            hw[e] = xh;
+                            lw[e] = f32_to_bf16_rne(x - bf16_to_f32(xh));
+                        }
+                        hi[jj] = pack2(hw[0], hw[1]);
+                        lo[jj] = pack2(lw[0], lw[1]);
+                    }
+                }
+                acc_w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(hi), acc_w, 0, 0, 0);
+                acc_w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(lo), acc_w, 0, 0, 0);
+            }
+        }
+
+        // ---- input gradient: M-block mb (channels), N-block nb (heads)
+        {
+            f32x16 acc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+            bf16x8 af[C::KB];
+#pragma unroll
+            for (int kb = 0; kb < C::KB; ++kb)
+                af[kb] = tr_frag(dyl + (16 * kb) * C::PITCH + 32 * mb, C::PITCH, lane);
+#pragma unroll
+            for (int kb = 0; kb < C::KB; ++kb)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], wf[kb], acc, 0, 0, 0);
+            const int hrow = 32 * nb + (lane & 31);
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int cl = 32 * mb + 8 * a + 4 * Q;
+                const int cg = c_base + cl;
+                if (cg < nope) {
+                    uint2 o;
+                    o.x = pack2(f32_to_bf16_rne(acc[4 * a]), f32_to_bf16_rne(acc[4 * a + 1]));
+                    o.y = pack2(f32_to_bf16_rne(acc[4 * a + 2]), f32_to_bf16_rne(acc[4 * a + 3]));
+                    *reinterpret_cast<uint2*>(dol + hrow * C::PITCH + cl) = o;
+                } else {
+                    f32x4 o = {acc[4 * a], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]};
+                    *reinterpret_cast<f32x4*>(pes + hrow * pes_pitch + (cg - nope)) = o;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- dO rows of the chunk; pe pairs turned by +phi
+        uint16_t* outs = dO + s * NH * (int64_t)d + c_base;
+#pragma unroll
+        for (int j = 0; j < C::OPT; ++j) {
+            const int q = j * C::NT + tid;
+            const int row = q / C::VPR, c8 = q % C::VPR;
+            const int cl = 8 * c8, cg = c_base + cl;
+            u32x4 o;
+            if (cg < nope) {
+                o = *reinterpret_cast<const u32x4*>(dol + row * C::PITCH + cl);
+            } else {
+                const int i = cg - nope;
+                const bool first = i < h2;
+                const int ii = first ? i : i - h2;
+                const float* own = pes + row * pes_pitch + i;
+                const float* par = pes + row * pes_pitch + (first ? i + h2 : i - h2);
+                const f32x4 o0 = reinterpret_cast<const f32x4*>(own)[0], o1 = reinterpret_cast<const f32x4*>(own)[1];
+                const f32x4 p0 = reinterpret_cast<const f32x4*>(par)[0], p1 = reinterpret_cast<const f32x4*>(par)[1];
+                const f32x4 c0 = reinterpret_cast<const f32x4*>(csl + ii)[0];
+                const f32x4 c1 = reinterpret_cast<const f32x4*>(csl + ii)[1];
+                const f32x4 s0 = reinterpret_cast<const f32x4*>(snl + ii)[0];
+                const f32x4 s1 = reinterpret_cast<const f32x4*>(snl + ii)[1];
+                // +phi: first half a C - b S, second half b C + a S
+                const float sg = first ? -1.0f : 1.0f;
+                float y[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    y[e] = o0[e] * c0[e] + sg * (p0[e] * s0[e]);
+                    y[4 + e] = o1[e] * c1[e] + sg * (p1[e] * s1[e]);
+                }
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) o[jj] = pack2(f32_to_bf16_rne(y[2 * jj]), f32_to_bf16_rne(y[2 * jj + 1]));
+            }
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(outs + row * (int64_t)d + cl));
+        }
+        __syncthreads();
+    }
+
+    // ---- dW partial: tile sum (wave tile) + (wave tile + 4), fixed order
+    float* red = reinterpret_cast<float*>(smem);
+    if (kset == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[(tile * 16 + r) * 64 + lane] = acc_w[r];
+    }
+    __syncthreads();
+    if (kset != 0) return;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_w[r] += red[(tile * 16 + r) * 64 + lane];
+    float* part_out = partials + (int64_t)blockIdx.x * NH * NH;
+    const int h = 32 * hb + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int g = 32 * gb + 8 * (r >> 2) + 4 * half + (r & 3);
+        part_out[g * NH + h] = acc_w[r];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host-side launchers (argument checks are done by the caller)
 // ---------------------------------------------------------------------------
 
@@ -1066,7 +1320,9 @@ int mix_part_width(int64_t sq, int nh, int nope, int pe) {
 
 template <bool DX>
 static hipError_t launch_mix_dx(const MixArgs& a, hipStream_t stream) {
-    const int cp = a.force_general ? 0 : mix_part_width(a.sq, a.nh, a.nope, a.pe);
+    // the tiled kernels read W with 16-byte loads
+    const bool w16 = ((uintptr_t)a.W & 15u) == 0;
+    const int cp = (a.force_general || !w16) ? 0 : mix_part_width(a.sq, a.nh, a.nope, a.pe);
     if (cp == 256 && a.nh == 64) return launch_part_t<64, 256, 8, DX>(a, stream);
     if (cp == 128 && a.nh == 64) return launch_part_t<64, 128, 4, DX>(a, stream);
     if (cp == 256 && a.nh == 32) return launch_part_t<32, 256, 8, DX>(a, stream);
@@ -1116,6 +1372,35 @@ static hipError_t launch_dw_t(const DwArgs& a, hipStream_t stream) {
                            a.O, a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe,
                            a.partials, tpb);
     }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t ne = (int64_t)a.nh * a.nh;
+    hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((ne + 63) / 64)), dim3(1024), 0, stream,
+                       a.partials, nb, ne, a.dW);
+    return hipGetLastError();
+}
+
+// fused backward (dx + dW partials in one pass), then the fixed-order reduce
+bool bwd_fused_applies(int nh, int nope, int pe) {
+    const int d = nope + pe;
+    return nh == 64 && d % 128 == 0 && pe <= 128;
+}
+
+hipError_t launch_bwd_fused(const MixArgs& mx, const DwArgs& a, hipStream_t stream) {
+    using C = BwdCfg<64, 128>;
+    const int tpb = dw_tokens_per_block(a.sq, a.nh);
+    const int64_t nb = dw_num_blocks(a.sq, a.nh);
+    const size_t lds = C::lds_bytes(a.pe);
+    auto kern = bwd_fused_kernel<64, 128>;
+    static bool attr_done = false;  // idempotent; a race only repeats the call
+    if (!attr_done) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)C::lds_bytes(128));
+        if (e != hipSuccess) return e;
+        attr_done = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(512), lds, stream, a.dY, a.O, mx.W, a.rcos, a.rsin,
+                       a.table_rows, a.positions, a.sq, a.nope, a.pe, mx.Out, a.partials, tpb);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t ne = (int64_t)a.nh * a.nh;

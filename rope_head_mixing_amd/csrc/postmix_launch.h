@@ -49,4 +49,9 @@ int dw_tokens_per_block(int64_t sq, int nh);
 int64_t dw_num_blocks(int64_t sq, int nh);
 int dw_chunk_width(int nh, int nope, int pe);
 
+// Fused backward: dx (into mx.Out) and the dW partials from one pass over dY
+// and O, then the reduce into a.dW.  Only for shapes where bwd_fused_applies.
+bool bwd_fused_applies(int nh, int nope, int pe);
+hipError_t launch_bwd_fused(const MixArgs& mx, const DwArgs& a, hipStream_t stream);
+
 }  // namespace pm

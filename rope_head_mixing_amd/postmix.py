@@ -10,7 +10,9 @@ Entry points keep the C names:
     postmix_bwd_dx(dY, W, rope_cos, rope_sin, positions, nope, pe, out=None)
     postmix_bwd_dw(dY, O, rope_cos, rope_sin, positions, nope, pe, out=None, workspace=None)
     postmix_bwd_dw_workspace_bytes(sq, nh, nope, pe)
+    postmix_bwd(dY, O, W, rope_cos, rope_sin, positions, nope, pe, ...)  -> (dO, dW)
     postmix_rope_table(theta, pe, table_rows, device=None)
+    postmix_set_general_kernels(enable)
 Tensors: O/Y/dY/dO bfloat16 [sq, nh, nope+pe]; W bfloat16 [nh, nh] (W[g,h], g =
 output head); rope_cos/rope_sin float32 [rows, pe/2]; positions int32 [sq];
 dW float32 [nh, nh].  Dtype mismatches raise ValueError naming the tensor (the
@@ -61,6 +63,8 @@ def lib():
     L.postmix_bwd_dw_workspace_bytes.restype = SZ
     L.postmix_bwd_dw.argtypes = [P, P, P, P, I64, P, I64, I32, I32, I32, P, P, SZ, P]
     L.postmix_bwd_dw.restype = ctypes.c_int
+    L.postmix_bwd.argtypes = [P, P, P, P, P, I64, P, I64, I32, I32, I32, P, P, P, SZ, P]
+    L.postmix_bwd.restype = ctypes.c_int
     L.postmix_rope_table.argtypes = [F64, I32, I64, P, P, P]
     L.postmix_rope_table.restype = ctypes.c_int
     L.postmix_status_string.argtypes = [ctypes.c_int]
@@ -175,6 +179,30 @@ def postmix_bwd_dw(dY, O, rope_cos, rope_sin, positions, nope: int, pe: int, out
                                 dW.data_ptr(), workspace.data_ptr(), ws_bytes,
                                 _stream_handle(dY.device)))
     return dW
+
+
+def postmix_bwd(dY, O, W, rope_cos, rope_sin, positions, nope: int, pe: int, out_dO=None,
+                out_dW=None, workspace=None):
+    """Both gradients in one call: (dO, dW) as postmix_bwd_dx and postmix_bwd_dw."""
+    torch = _torch()
+    _need(dY, "dY", torch.bfloat16, 3)
+    _need(O, "O", torch.bfloat16, 3)
+    _need(W, "W", torch.bfloat16, 2)
+    sq, nh, d = _act_shape(dY, "dY", nope, pe)
+    if tuple(O.shape) != tuple(dY.shape):
+        raise ValueError("O and dY must have the same shape")
+    c, s, rows, p = _rope_ptrs(rope_cos, rope_sin, positions, pe, sq)
+    dO = torch.empty_like(dY) if out_dO is None else _need(out_dO, "out_dO", torch.bfloat16, 3)
+    dW = (torch.empty((nh, nh), dtype=torch.float32, device=dY.device) if out_dW is None
+          else _need(out_dW, "out_dW", torch.float32, 2))
+    need = postmix_bwd_dw_workspace_bytes(sq, nh, nope, pe)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dY.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().postmix_bwd(dY.data_ptr(), O.data_ptr(), W.data_ptr(), c, s, rows, p, sq, nh,
+                             nope, pe, dO.data_ptr(), dW.data_ptr(), workspace.data_ptr(),
+                             ws_bytes, _stream_handle(dY.device)))
+    return dO, dW
 
 
 def postmix_set_general_kernels(enable: bool) -> bool:

@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ["postmix_fwd", "postmix_bwd_dx", "postmix_bwd_dw", "postmix_bwd_dw_workspace_bytes",
+    for n in ["postmix_fwd", "postmix_bwd_dx", "postmix_bwd_dw", "postmix_bwd", "postmix_bwd_dw_workspace_bytes",
               "postmix_rope_table", "postmix_status_string", "postmix_last_error"]:
         assert n in names
 
@@ -223,3 +223,38 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(pm, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         pm.lib()
+
+
+def bwd(**kw):
+    sq, nh, nope, pe = kw.get("sq", 16), kw.get("nh", 64), kw.get("nope", 448), kw.get("pe", 64)
+    need = pm.lib().postmix_bwd_dw_workspace_bytes(sq, nh, nope, pe)
+    args = dict(dY=A, O=B, W=0x200000000, cos=C, sin=D, rows=32768, pos=E, sq=sq, nh=nh, nope=nope,
+                pe=pe, dO=F, dW=0x240000000, ws=0x180000000, wsb=need)
+    args.update(kw)
+    L = pm.lib()
+    rc = L.postmix_bwd(args["dY"], args["O"], args["W"], args["cos"], args["sin"], args["rows"],
+                       args["pos"], args["sq"], args["nh"], args["nope"], args["pe"], args["dO"],
+                       args["dW"], args["ws"], args["wsb"], None)
+    return rc, L.postmix_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(dW=0), pm.PM_ERR_NULL, "dW"),
+    (dict(dO=0), pm.PM_ERR_NULL, "dO"),
+    (dict(W=0), pm.PM_ERR_NULL, "W"),
+    (dict(dY=0), pm.PM_ERR_NULL, "dY"),
+    (dict(O=0), pm.PM_ERR_NULL, "O"),
+    (dict(ws=0), pm.PM_ERR_NULL, "workspace"),
+    (dict(wsb=16), pm.PM_ERR_WORKSPACE, "workspace"),
+    (dict(W=0x200000000 + 1), pm.PM_ERR_ALIGN, "W"),
+    (dict(dO=F + 8), pm.PM_ERR_ALIGN, "dO"),
+    (dict(dO=A + 1024), pm.PM_ERR_OVERLAP, "dO"),
+    (dict(dW=F + 64), pm.PM_ERR_OVERLAP, "dW"),
+    (dict(ws=0x200000000), pm.PM_ERR_OVERLAP, "workspace"),
+    (dict(nope=20), pm.PM_ERR_SHAPE, "nope"),
+    (dict(sin=0), pm.PM_ERR_NULL, "rope_sin"),
+])
+def test_fused_backward_argument_errors(kw, code, word):
+    rc, msg = bwd(**kw)
+    assert rc == code, msg
+    assert word in msg

@@ -59,6 +59,11 @@ class Dev:
         c = self.case
         return P().postmix_bwd_dx(self.ddY_, self.dW_, self.cos, self.sin, self.dpos, c.nope, c.pe)
 
+    def bwd(self, workspace=None):
+        c = self.case
+        return P().postmix_bwd(self.ddY_, self.dO_, self.dW_, self.cos, self.sin, self.dpos, c.nope,
+                               c.pe, workspace=workspace)
+
     def dw(self, workspace=None):
         c = self.case
         return P().postmix_bwd_dw(self.ddY_, self.dO_, self.cos, self.sin, self.dpos, c.nope, c.pe,
@@ -164,6 +169,33 @@ def test_tiled_and_general_kernels_agree(sq, nh, nope, pe):
     assert rel < 1e-5, rel
 
 
+@pytest.mark.parametrize("sq,nh,nope,pe,off", [
+    (67, 64, 448, 64, 16384),   # fused path, ragged block count
+    (33, 64, 192, 64, 7),       # fused path, d = 256
+    (70, 64, 384, 128, 3),      # fused path, pe = 128 (one whole chunk rotated)
+    (19, 64, 432, 80, 99),      # fused path, nope straddles an M-block
+    (21, 32, 448, 64, 5),       # not fused (nh = 32): separate kernels
+    (9, 3, 448, 64, 0),         # not fused (nh = 3)
+])
+def test_fused_backward_matches_oracle_and_separate_calls(sq, nh, nope, pe, off):
+    c = synthetic.case(sq, nh, nope, pe, seed=4000 + sq, pos_offset=off)
+    print(f"\n[parity] fused bwd {c.name}", flush=True)
+    dv = Dev(c)
+    dO, dW = dv.bwd()
+    dO, dW = gu.host_bits(dO), dW.cpu().numpy()
+    gu.check_bf16(dO, oracle.bwd_dx(dv.dY, dv.W, dv.pos, c.theta, nope, pe), "fused dO")
+    gu.check_dw(dW, oracle.bwd_dw(dv.dY, dv.O, dv.pos, c.theta, nope, pe), "fused dW")
+    # dO is the same computation as postmix_bwd_dx, bit for bit
+    np.testing.assert_array_equal(dO, gu.host_bits(dv.dx()))
+    # dW: same blocks, different order inside a block; each repeats bitwise
+    dW_sep = dv.dw().cpu().numpy()
+    assert np.linalg.norm(dW - dW_sep) <= 1e-5 * np.linalg.norm(dW_sep)
+    for _ in range(3):
+        dO2, dW2 = dv.bwd()
+        np.testing.assert_array_equal(gu.host_bits(dO2), dO)
+        np.testing.assert_array_equal(dW2.cpu().numpy(), dW)
+
+
 def test_forward_only_workload_sq1024(kernel_policy):
     full_check(synthetic.CASES["fwd_1k"], ops=("fwd",))
 
@@ -207,6 +239,22 @@ def test_out_of_range_positions_are_clamped_not_read_out_of_bounds():
     gu.check_bf16(gu.host_bits(Y), ref, "clamped positions")
 
 
+def test_unaligned_W_takes_the_general_path():
+    """W that is 2-byte but not 16-byte aligned: same results as an aligned copy."""
+    import torch
+    c = synthetic.case(29, 64, 448, 64, seed=909, pos_offset=300)
+    dv = Dev(c)
+    store = torch.empty(64 * 64 + 1, dtype=torch.bfloat16, device="cuda")
+    Wv = store[1:].view(64, 64)
+    Wv.copy_(dv.dW_)
+    assert Wv.data_ptr() % 16 == 2
+    Y = P().postmix_fwd(dv.dO_, Wv, dv.cos, dv.sin, dv.dpos, c.nope, c.pe)
+    gu.check_bf16(gu.host_bits(Y), oracle.fwd(dv.O, dv.W, dv.pos, c.theta, c.nope, c.pe), "Y, W+2")
+    dO, dW = P().postmix_bwd(dv.ddY_, dv.dO_, Wv, dv.cos, dv.sin, dv.dpos, c.nope, c.pe)
+    gu.check_bf16(gu.host_bits(dO), oracle.bwd_dx(dv.dY, dv.W, dv.pos, c.theta, c.nope, c.pe), "dO, W+2")
+    gu.check_dw(dW.cpu().numpy(), oracle.bwd_dw(dv.dY, dv.O, dv.pos, c.theta, c.nope, c.pe), "dW, W+2")
+
+
 def test_empty_token_range():
     import torch
     c = synthetic.case(0, 4, 48, 16, seed=1)
@@ -247,11 +295,12 @@ def sampled_check(case, ops, n_samples=4096, dw_samples=24, repeat_dw=10):
         ref = oracle.fwd_at(dv.O, dv.W, dv.pos, case.theta, case.nope, case.pe, idx)
         res["fwd"] = gu.check_bf16(Y[idx], ref, f"{case.name} Y")
         del Y
+    dO_bits = None
     if "dx" in ops:
         dO = gu.host_bits(dv.dx()).reshape(-1)
         ref = oracle.bwd_dx_at(dv.dY, dv.W, dv.pos, case.theta, case.nope, case.pe, idx)
         res["dx"] = gu.check_bf16(dO[idx], ref, f"{case.name} dO")
-        del dO
+        dO_bits = dO
     if "dw" in ops:
         import torch
         ws = torch.empty(P().postmix_bwd_dw_workspace_bytes(case.sq, case.nh, case.nope, case.pe),
@@ -262,11 +311,22 @@ def sampled_check(case, ops, n_samples=4096, dw_samples=24, repeat_dw=10):
         widx = rng.integers(0, case.nh * case.nh, dw_samples)
         widx[:2] = [0, case.nh * case.nh - 1]
         ref = oracle.bwd_dw_at(dv.dY, dv.O, dv.pos, case.theta, case.nope, case.pe, widx)
-        got = dW.reshape(-1)[widx].astype(np.float64)
-        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
-        assert rel <= gu.DW_REL, f"{case.name} dW sampled rel {rel:.3e}"
-        assert np.abs(got - ref).max() <= gu.DW_REL * np.abs(ref).max()
-        res["dw"] = rel
+
+        def check_sampled(dW_, label):
+            got = dW_.reshape(-1)[widx].astype(np.float64)
+            rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+            assert rel <= gu.DW_REL, f"{case.name} {label} sampled rel {rel:.3e}"
+            assert np.abs(got - ref).max() <= gu.DW_REL * np.abs(ref).max()
+            return rel
+        res["dw"] = check_sampled(dW, "dW")
+        if "bwd" in ops:
+            # the fused backward: dO bitwise as bwd_dx, dW repeatable and on the oracle
+            dO_f, dW_f = dv.bwd(workspace=ws)
+            dW_f = dW_f.cpu().numpy()
+            np.testing.assert_array_equal(gu.host_bits(dO_f).reshape(-1), dO_bits)
+            for _ in range(repeat_dw - 1):
+                np.testing.assert_array_equal(dv.bwd(workspace=ws)[1].cpu().numpy(), dW_f)
+            res["bwd_dw"] = check_sampled(dW_f, "fused dW")
     print(f"[parity] {case.name}: {res}", flush=True)
     return res
 
@@ -278,4 +338,4 @@ def test_sweep_nh128_sampled():
 def test_production_forward_and_backward_sampled():
     """sq=16384, nh=64, 448+64, positions 16384..32767: Y and dO sampled,
     dW sampled and bitwise identical over 10 runs."""
-    sampled_check(synthetic.CASES["prod"], ("fwd", "dx", "dw"), repeat_dw=10)
+    sampled_check(synthetic.CASES["prod"], ("fwd", "dx", "dw", "bwd"), repeat_dw=10)
