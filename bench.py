@@ -3,16 +3,18 @@
 A step is one pass of the whole path over the production workload of
 PaddleFleet PR #1772 (PR body item 1: sq=16384 tokens of a 64K context with
 context_parallel_size=4, nh=64, nope=448, pe=64, a 1 GiB bf16 attention
-output): forward (postmix_fwd), input gradient (postmix_bwd_dx) and weight
-gradient (postmix_bwd_dw), each reading its inputs from HBM.
+output): the forward (postmix_fwd) and the backward (postmix_bwd: dO and dW
+from one pass over dY and O), each reading its inputs from HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 Prints one JSON line.  `value` is the step's achieved HBM bandwidth: the
-algorithmic bytes of the three ops (activations in and out, W, the cos/sin
+algorithmic bytes of the two calls (activations in and out, W, the cos/sin
 rows touched, positions, dW) over the measured step time.  Per-op times come
-from HIP events recorded on the stream the kernels run on.  The oracle's
-CPU time on a bounded sample of the same workload is reported beside it.
+from HIP events recorded on the stream the kernels run on.  The separate
+backward entry points (postmix_bwd_dx, postmix_bwd_dw) are timed after the
+steps and reported per op.  The oracle's CPU time on a bounded sample of the
+same workload is reported beside it.
 """
 from __future__ import annotations
 
@@ -34,9 +36,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # kernels behind each op at nh=64, d=512 (tiled path)
 KERNELS_NH64 = {
     "fwd": "mix_part_kernel<64, 256, 8, false, false>",
+    "bwd": "bwd_fused_kernel<64, 128> + dw_reduce_kernel",
     "bwd_dx": "mix_part_kernel<64, 256, 8, true, false>",
     "bwd_dw": "dw_chunk_kernel<64, 128> + dw_reduce_kernel",
 }
+STEP_OPS = ("fwd", "bwd")          # the timed step
+EXTRA_OPS = ("bwd_dx", "bwd_dw")   # the separate backward entry points, timed after
 # The pages' own figures for this workload (another GPU; context only).
 PAGES_CONTEXT = {
     "hardware": "1x B30Z (sm10.3)",
@@ -85,13 +90,13 @@ def cpu_baseline(case, O, W, dY, pos, target_s: float):
     S = int(min(case.sq, max(cal, round(target_s / max(t_cal, 1e-6) * cal / 64) * 64)))
     t = one_pass(S)
     frac = S / case.sq
-    alg = sum(case.algorithmic_bytes(op) for op in ("fwd", "bwd_dx", "bwd_dw")) * frac
+    alg = sum(case.algorithmic_bytes(op) for op in STEP_OPS) * frac
     return {
         "value": round(alg / t / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"fwd+bwd_dx+bwd_dw on the first {S} of {case.sq} tokens "
+        "sample": f"fwd, dx and dW on the first {S} of {case.sq} tokens "
                   f"({t:.2f} s; full step extrapolates to {t / frac * 1e6:.0f} us)",
         "seconds": round(t, 3),
         "us_per_full_step_extrapolated": round(t / frac * 1e6, 1),
@@ -236,38 +241,43 @@ def main():
                      dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
 
-    def step(evs=None):
-        if evs is not None:
-            evs[0].record()
-        pm.postmix_fwd(dO_in, dW_in, cos, sin, dpos, case.nope, case.pe, out=Y)
-        if evs is not None:
-            evs[1].record()
-        pm.postmix_bwd_dx(ddY, dW_in, cos, sin, dpos, case.nope, case.pe, out=dO)
-        if evs is not None:
-            evs[2].record()
-        pm.postmix_bwd_dw(ddY, dO_in, cos, sin, dpos, case.nope, case.pe, out=dW, workspace=ws)
-        if evs is not None:
-            evs[3].record()
+    calls = {
+        "fwd": lambda: pm.postmix_fwd(dO_in, dW_in, cos, sin, dpos, case.nope, case.pe, out=Y),
+        "bwd": lambda: pm.postmix_bwd(ddY, dO_in, dW_in, cos, sin, dpos, case.nope, case.pe,
+                                      out_dO=dO, out_dW=dW, workspace=ws),
+        "bwd_dx": lambda: pm.postmix_bwd_dx(ddY, dW_in, cos, sin, dpos, case.nope, case.pe, out=dO),
+        "bwd_dw": lambda: pm.postmix_bwd_dw(ddY, dO_in, cos, sin, dpos, case.nope, case.pe, out=dW,
+                                            workspace=ws),
+    }
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def timed_loop(ops):
+        """Warm up, then time args.steps passes of `ops`; events between calls."""
+        for _ in range(args.warmup):
+            for op in ops:
+                calls[op]()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)]
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            ev[k][0].record()
+            for i, op in enumerate(ops):
+                calls[op]()
+                ev[k][i + 1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = {op: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
+              for i, op in enumerate(ops)}
+        return wall, ms
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for k in range(args.steps):
-        step(events[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-
-    ops = ["fwd", "bwd_dx", "bwd_dw"]
-    per_op_ms = {op: float(np.mean([events[k][i].elapsed_time(events[k][i + 1])
-                                    for k in range(args.steps)]))
-                 for i, op in enumerate(ops)}
+    wall, per_op_ms = timed_loop(STEP_OPS)
+    _, extra_ms = timed_loop(EXTRA_OPS)
+    per_op_ms.update(extra_ms)
+    ops = list(STEP_OPS) + list(EXTRA_OPS)
     ms_per_step = wall * 1e3 / args.steps
     alg = {op: case.algorithmic_bytes(op) for op in ops}
-    step_bytes = sum(alg.values())
+    step_bytes = sum(alg[op] for op in STEP_OPS)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     op_report = {}
@@ -275,7 +285,7 @@ def main():
         gbps = alg[op] / (per_op_ms[op] * 1e-3) / 1e9
         op_report[op] = {"us": round(per_op_ms[op] * 1e3, 1), "GBps": round(gbps, 1),
                          "pct_peak": round(100 * gbps / PEAK_GBPS, 1),
-                         "algorithmic_bytes": alg[op]}
+                         "algorithmic_bytes": alg[op], "in_step": op in STEP_OPS}
 
     # device-to-device copy of the same 1 GiB, for an achievable-bandwidth reference
     src = dO_in.view(torch.int16)
@@ -291,7 +301,7 @@ def main():
     copy_gbps = 2 * src.numel() * 2 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
     del dst
 
-    dominant = max(ops, key=lambda op: per_op_ms[op])
+    dominant = max(STEP_OPS, key=lambda op: per_op_ms[op])
     kernel_key = KERNELS_NH64[dominant] if case.nh == 64 else dominant
     achieved = alg[dominant] / (per_op_ms[dominant] * 1e-3) / 1e9
     roofline = {
@@ -318,7 +328,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{case.name}: fwd + bwd_dx + bwd_dw, O/dY [{case.sq}, {case.nh}, "
+            "workload": f"{case.name}: postmix_fwd + postmix_bwd (dO and dW), O/dY [{case.sq}, {case.nh}, "
                         f"{case.nope}+{case.pe}] bf16 N(0,1), W [{case.nh},{case.nh}] = I + N(0,0.02), "
                         f"rotate-half RoPE theta={case.theta:g}, positions "
                         f"{int(pos[0])}..{int(pos[-1])}",

@@ -98,6 +98,8 @@ class Case:
             return 2 * act + w + tables + pos
         if op == "bwd_dw":
             return 2 * act + tables + pos + self.nh * self.nh * 4
+        if op == "bwd":  # both gradients from one read of dY and O
+            return 3 * act + w + tables + pos + self.nh * self.nh * 4
         raise ValueError(op)
 
     def flops(self) -> int:
