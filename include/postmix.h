@@ -159,6 +159,40 @@ int postmix_bwd(const pm_bf16 *dY, const pm_bf16 *O, const pm_bf16 *W,
 int postmix_rope_table(double theta, int32_t pe, int64_t table_rows,
                        float *cos_out, float *sin_out, void *stream);
 
+/*
+ * Full-width rotary embedding, out of place: the tensor the unfused route of
+ * PR #1772 materialises (body item 1) and its final backward rebuilds
+ * (rope_full_out_of_place, follow-up commit).  Provided so that route can be
+ * run on this GPU next to the fused one; the fused entry points never need it.
+ *   direction = -1: Out = inv_rope(X);  +1: Out = rope(X).
+ *   X, Out [sq, nh, nope+pe] bf16 (RNE), nope channels copied; other
+ *   arguments as postmix_fwd.  Out must not overlap X.
+ */
+int postmix_rope_apply(const pm_bf16 *X, const float *rope_cos,
+                       const float *rope_sin, int64_t table_rows,
+                       const int32_t *positions, int64_t sq, int32_t nh,
+                       int32_t nope, int32_t pe, int32_t direction, pm_bf16 *Out,
+                       void *stream);
+
+/*
+ * KV column index remap (PR #1772 body item 2, "sparse_attn_global_kv_idx_
+ * remap_fusion", and description part 二): the sparse-attention index table
+ * [rows = b*sq, topk] int32 holds per-batch-local KV column indices; the
+ * flat-global index of row r (batch r / sq) is idx + batch * seqlen_kv.
+ *   out[r, k] = idx[r, k] >= 0 ? idx[r, k] + (r / sq) * seqlen_kv : pad_value
+ * Negative entries are padding (a reading: the pages name the unfused route's
+ * steps, a fill, a >= 0 test, a batch arange, an expand, a scale, an add and
+ * a select, but not the fill value; it is the caller's pad_value here).
+ *   idx [rows, topk] int32 device, read;  out [rows, topk] int32 device,
+ *   written; out == idx (in place) is allowed, a partial overlap is not.
+ * rows % sq == 0; (rows / sq) * seqlen_kv must fit in int32 (valid entries
+ * are expected below seqlen_kv; larger ones wrap as int32 arithmetic does).
+ * 4-byte alignment; 16-byte alignment and topk % 4 == 0 take the vector path.
+ */
+int postmix_kv_index_remap(const int32_t *idx, int64_t rows, int64_t sq,
+                           int64_t topk, int64_t seqlen_kv, int32_t pad_value,
+                           int32_t *out, void *stream);
+
 /* Static text for a PM_* code. */
 const char *postmix_status_string(int status);
 

@@ -95,6 +95,7 @@ def _bind(lib):
         "oracle_fwd_at_bf16": ([_P, _P, _P, _F64, _I64, _I32, _I32, _I32, _P, _I64, _P], _I32),
         "oracle_bwd_dx_at_bf16": ([_P, _P, _P, _F64, _I64, _I32, _I32, _I32, _P, _I64, _P], _I32),
         "oracle_bwd_dw_at_bf16": ([_P, _P, _P, _F64, _I64, _I32, _I32, _I32, _P, _I64, _P, _I32], _I32),
+        "oracle_kv_remap": ([_P, _I64, _I64, _I64, _I64, _I32, _P], _I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -248,4 +249,16 @@ def bwd_dw_at(dY, O, positions, theta, nope, pe, flat_idx, nthreads=None) -> np.
     _check_rc(_load().oracle_bwd_dw_at_bf16(_ptr(dY), _ptr(O), _ptr(p), float(theta), sq, nh,
                                             nope, pe, _ptr(idx), idx.shape[0], _ptr(out), nt),
               "bwd_dw_at")
+    return out
+
+
+def kv_remap(idx, sq, seqlen_kv, pad_value=-1) -> np.ndarray:
+    """Flat-global KV column indices: idx [b*sq, topk] int32; row r belongs to
+    batch r // sq; valid (>= 0) entries get + batch * seqlen_kv, negative
+    entries become pad_value."""
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+    rows, topk = idx.shape
+    out = np.empty_like(idx)
+    _check_rc(_load().oracle_kv_remap(_ptr(idx), rows, int(sq), topk, int(seqlen_kv),
+                                      int(pad_value), _ptr(out)), "kv_remap")
     return out

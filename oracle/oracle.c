@@ -9,7 +9,9 @@
  *   [P1772] PaddleFleet PR #1772, "Fuse HCA inverse RoPE into the VHA postmix,
  *           and the sparse-attention KV index remap": PR body, item 1
  *           ("fuse_inv_rope_into_vha_postmix"); the follow-up commit that
- *           changed the backward route; the Chinese description, part 一.
+ *           changed the backward route; the Chinese description, part 一;
+ *           and, for the KV index remap at the end of this file, PR body
+ *           item 2 ("sparse_attn_global_kv_idx_remap_fusion") and part 二.
  *
  * What the pages fix:
  *   - The HCA layer applies an inverse RoPE to the attention output O and
@@ -546,4 +548,26 @@ int oracle_bwd_dw_at_bf16(const uint16_t *dY, const uint16_t *O,
     }
     free(slabs);
     return rc;
+}
+
+/* ------------------------------------------------------------------ */
+/* KV column index remap ([P1772] PR body item 2 and description part */
+/* 二): a per-batch-local index table [b*sq, topk] becomes flat-global */
+/* by adding b * seqlen_kv to every valid (non-negative) entry of the  */
+/* rows of batch b.  Reading: negative entries are padding and become  */
+/* pad_value.  Plain per-element definition.                           */
+/* ------------------------------------------------------------------ */
+
+int oracle_kv_remap(const int32_t *idx, int64_t rows, int64_t sq, int64_t topk,
+                    int64_t seqlen_kv, int32_t pad_value, int32_t *out)
+{
+    if (rows < 0 || sq < 1 || topk < 0 || seqlen_kv < 0 || rows % sq != 0) return -2;
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = r / sq;
+        for (int64_t k = 0; k < topk; ++k) {
+            int32_t v = idx[r * topk + k];
+            out[r * topk + k] = v >= 0 ? (int32_t)(v + b * seqlen_kv) : pad_value;
+        }
+    }
+    return 0;
 }

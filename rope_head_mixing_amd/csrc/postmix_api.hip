@@ -349,6 +349,71 @@ int postmix_bwd(const pm_bf16* dY, const pm_bf16* O, const pm_bf16* W, const flo
     return ok();
 }
 
+int postmix_rope_apply(const pm_bf16* X, const float* rope_cos, const float* rope_sin,
+                       int64_t table_rows, const int32_t* positions, int64_t sq, int32_t nh,
+                       int32_t nope, int32_t pe, int32_t direction, pm_bf16* Out, void* stream) {
+    int rc = check_shape(sq, nh, nope, pe);
+    if (rc) return rc;
+    if (direction != 1 && direction != -1) return fail(PM_ERR_SHAPE, "direction must be +1 or -1");
+    if (sq == 0) return ok();
+    if (!X) return fail(PM_ERR_NULL, "X is NULL");
+    if (!Out) return fail(PM_ERR_NULL, "Out is NULL");
+    rc = check_rope_args(rope_cos, rope_sin, table_rows, positions, pe);
+    if (rc) return rc;
+    if (!aligned16(X)) return fail(PM_ERR_ALIGN, "X is not 16-byte aligned");
+    if (!aligned16(Out)) return fail(PM_ERR_ALIGN, "Out is not 16-byte aligned");
+    const size_t act = (size_t)sq * nh * (nope + pe) * sizeof(pm_bf16);
+    const size_t tab = pe ? (size_t)table_rows * (pe / 2) * sizeof(float) : 0;
+    const Range outs[1] = {{"Out", Out, act}};
+    const Range ins[4] = {{"X", X, act},
+                          {"rope_cos", pe ? rope_cos : nullptr, tab},
+                          {"rope_sin", pe ? rope_sin : nullptr, tab},
+                          {"positions", pe ? positions : nullptr, (size_t)sq * sizeof(int32_t)}};
+    rc = check_no_overlap(outs, 1, ins, 4);
+    if (rc) return rc;
+    int n_cu = 0;
+    rc = check_device(&n_cu);
+    if (rc) return rc;
+    hipError_t e = pm::launch_rope_apply(X, rope_cos, rope_sin, table_rows, positions, sq, nh, nope, pe,
+                                         direction, Out, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int postmix_kv_index_remap(const int32_t* idx, int64_t rows, int64_t sq, int64_t topk,
+                           int64_t seqlen_kv, int32_t pad_value, int32_t* out, void* stream) {
+    if (rows < 0) return fail(PM_ERR_SHAPE, "rows must be >= 0");
+    if (sq < 1) return fail(PM_ERR_SHAPE, "sq must be >= 1");
+    if (rows % sq != 0) return fail(PM_ERR_SHAPE, "rows (%lld) must be a multiple of sq (%lld)",
+                                    (long long)rows, (long long)sq);
+    if (topk < 0) return fail(PM_ERR_SHAPE, "topk must be >= 0");
+    if (seqlen_kv < 0) return fail(PM_ERR_SHAPE, "seqlen_kv must be >= 0");
+    const int64_t batches = rows / sq;
+    if (batches > 0 && seqlen_kv > (int64_t)INT32_MAX / batches)
+        return fail(PM_ERR_SHAPE, "batches * seqlen_kv = %lld * %lld exceeds the int32 index range",
+                    (long long)batches, (long long)seqlen_kv);
+    if (rows > ((int64_t)1 << 40) / (topk > 0 ? topk : 1))
+        return fail(PM_ERR_SHAPE, "table of %lld x %lld entries is too large", (long long)rows, (long long)topk);
+    if (rows == 0 || topk == 0) return ok();
+    if (!idx) return fail(PM_ERR_NULL, "idx is NULL");
+    if (!out) return fail(PM_ERR_NULL, "out is NULL");
+    if (((uintptr_t)idx & 3u) != 0) return fail(PM_ERR_ALIGN, "idx is not 4-byte aligned");
+    if (((uintptr_t)out & 3u) != 0) return fail(PM_ERR_ALIGN, "out is not 4-byte aligned");
+    const size_t bytes = (size_t)rows * topk * sizeof(int32_t);
+    if (out != idx) {  // in place is fine (each element is read, then written, by one thread)
+        const Range outs[1] = {{"out", out, bytes}};
+        const Range ins[1] = {{"idx", idx, bytes}};
+        int rc = check_no_overlap(outs, 1, ins, 1);
+        if (rc) return rc;
+    }
+    int n_cu = 0;
+    int rc = check_device(&n_cu);
+    if (rc) return rc;
+    hipError_t e = pm::launch_kv_remap(idx, rows, sq, topk, seqlen_kv, pad_value, out, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int postmix_rope_table(double theta, int32_t pe, int64_t table_rows, float* cos_out,
                        float* sin_out, void* stream) {
     if (!(theta > 0.0)) return fail(PM_ERR_SHAPE, "theta must be > 0");

@@ -1026,9 +1026,9 @@ struct BwdCfg {
         const size_t w = (size_t)NH * WPITCH * 2, p = (size_t)NH * (pe + 4) * 4;
         return w > p ? w : p;
     }
-    // dY chunk, O chunk, dO chunk, then W / pe scratch, then cos and sin
+    // dY chunk, O chunk, dO chunk, then W / pe scratch, then cos and sin of two chunks
     __host__ __device__ static size_t lds_bytes(int pe) {
-        return (size_t)3 * NH * PITCH * 2 + aux_bytes(pe) + (size_t)pe * 4;
+        return (size_t)3 * NH * PITCH * 2 + aux_bytes(pe) + (size_t)pe * 8;
     }
 };
 
@@ -1046,8 +1046,8 @@ __global__ __launch_bounds__(512, 4) void bwd_fused_kernel(
     uint16_t* wl = dol + NH * C::PITCH;                 // [NH][WPITCH] bf16, then:
     float* pes = reinterpret_cast<float*>(wl);          // [NH][pe + 4] fp32
     const int pes_pitch = pe + 4;
-    float* csl = reinterpret_cast<float*>(reinterpret_cast<char*>(wl) + C::aux_bytes(pe));
-    float* snl = csl + (pe >> 1);
+    // cos/sin rows of two consecutive chunks: [2][pe] floats (cos then sin each)
+    float* const rope_l = reinterpret_cast<float*>(reinterpret_cast<char*>(wl) + C::aux_bytes(pe));
 
     const int d = nope + pe, h2 = pe >> 1;
     const int cpt = d / CH;
@@ -1081,6 +1081,19 @@ __global__ __launch_bounds__(512, 4) void bwd_fused_kernel(
             rope_v = reinterpret_cast<const f32x4*>((tid < (pe >> 3) ? rcos : rsin) + prow * h2)[tid % (pe >> 3)];
         }
     };
+    auto stage_chunk = [&](int k) {  // registers of chunk k -> LDS
+        const int part = k % cpt;
+#pragma unroll
+        for (int j = 0; j < C::VPT; ++j) {
+            const int q = j * C::NT + tid;
+            const int op = q / C::VPO;
+            const int rem = q % C::VPO;
+            const int row = rem / C::VPR, c8 = rem % C::VPR;
+            *reinterpret_cast<u32x4*>((op == 0 ? dyl : ol) + row * C::PITCH + 8 * c8) = v[j];
+        }
+        if (pe > 0 && (part + 1) * CH > nope && tid < (pe >> 2))
+            reinterpret_cast<f32x4*>(rope_l + (k & 1) * pe)[tid] = rope_v;
+    };
     if (nchunks > 0) load_chunk(0);
 
     // W -> LDS -> this wave's dx B operand (B[k=g][n=h] = W[g][h], N-block nb)
@@ -1098,22 +1111,22 @@ __global__ __launch_bounds__(512, 4) void bwd_fused_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_w[r] = 0.0f;
 
+    // Pipeline: chunk k is computed from the dY/O buffers; once every wave is
+    // done with them (barrier), chunk k+1 (already in registers) is staged
+    // there and chunk k+2 is requested, and only then are chunk k's dO rows
+    // stored (they live in separate buffers).  Two barriers per chunk.
+    if (nchunks > 0) {
+        stage_chunk(0);
+        if (nchunks > 1) load_chunk(1);
+    }
+    __syncthreads();
     for (int k = 0; k < nchunks; ++k) {
         const int64_t s = s_begin + k / cpt;
         const int part = k % cpt;
         const int c_base = part * CH;
         const bool chunk_pe = pe > 0 && c_base + CH > nope;
-#pragma unroll
-        for (int j = 0; j < C::VPT; ++j) {
-            const int q = j * C::NT + tid;
-            const int op = q / C::VPO;
-            const int rem = q % C::VPO;
-            const int row = rem / C::VPR, c8 = rem % C::VPR;
-            *reinterpret_cast<u32x4*>((op == 0 ? dyl : ol) + row * C::PITCH + 8 * c8) = v[j];
-        }
-        if (chunk_pe && tid < (pe >> 2)) reinterpret_cast<f32x4*>(csl)[tid] = rope_v;
-        __syncthreads();
-        if (k + 1 < nchunks) load_chunk(k + 1);  // in flight during the compute and the stores
+        const float* csl = rope_l + (k & 1) * pe;
+        const float* snl = csl + (pe >> 1);
 
         // ---- weight gradient: tile (gb, hb), k-steps t = kset, kset + 2, ...
 #pragma unroll
@@ -1183,7 +1196,11 @@ __global__ __launch_bounds__(512, 4) void bwd_fused_kernel(
                 }
             }
         }
-        __syncthreads();
+        __syncthreads();  // dY/O buffers free; dO and the pe scratch complete
+        if (k + 1 < nchunks) {
+            stage_chunk(k + 1);
+            if (k + 2 < nchunks) load_chunk(k + 2);  // in flight during two compute phases
+        }
 
         // ---- dO rows of the chunk; pe pairs turned by +phi
         uint16_t* outs = dO + s * NH * (int64_t)d + c_base;
@@ -1220,7 +1237,7 @@ __global__ __launch_bounds__(512, 4) void bwd_fused_kernel(
             }
             __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(outs + row * (int64_t)d + cl));
         }
-        __syncthreads();
+        __syncthreads();  // dO buffers read; chunk k+1 staged
     }
 
     // ---- dW partial: tile sum (wave tile) + (wave tile + 4), fixed order
@@ -1240,6 +1257,128 @@ __global__ __launch_bounds__(512, 4) void bwd_fused_kernel(
         const int g = 32 * gb + 8 * (r >> 2) + 4 * half + (r & 3);
         part_out[g * NH + h] = acc_w[r];
     }
+}
+
+// ---------------------------------------------------------------------------
+// KV column index remap (PaddleFleet PR #1772, PR body item 2 and description
+// part 二): per-batch-local indices of a [b*sq, topk] int32 table become
+// flat-global, out = idx >= 0 ? idx + batch * seqlen_kv : pad_value, with
+// batch = row / sq.  One pass over the table instead of the unfused route's
+// seven elementwise kernels.  Integer work, HBM-bound: 16-byte non-temporal
+// vectors when a row is a whole number of vectors.
+// ---------------------------------------------------------------------------
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int32_t remap_one(int32_t v, int64_t batch, int64_t seqlen_kv, int32_t pad) {
+    return v >= 0 ? (int32_t)((int64_t)v + batch * seqlen_kv) : pad;
+}
+
+__global__ __launch_bounds__(256) void kv_remap_vec_kernel(const int32_t* __restrict__ idx,
+                                                           int64_t n_vec, int64_t vec_per_row,
+                                                           int64_t sq, int64_t seqlen_kv, int32_t pad,
+                                                           int32_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_vec) return;
+    const int64_t batch = (i / vec_per_row) / sq;
+    const i32x4 v = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(idx) + i);
+    i32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = remap_one(v[e], batch, seqlen_kv, pad);
+    __builtin_nontemporal_store(o, reinterpret_cast<i32x4*>(out) + i);
+}
+
+__global__ __launch_bounds__(256) void kv_remap_scalar_kernel(const int32_t* __restrict__ idx,
+                                                              int64_t n, int64_t topk, int64_t sq,
+                                                              int64_t seqlen_kv, int32_t pad,
+                                                              int32_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    out[i] = remap_one(idx[i], (i / topk) / sq, seqlen_kv, pad);
+}
+
+hipError_t launch_kv_remap(const int32_t* idx, int64_t rows, int64_t sq, int64_t topk,
+                           int64_t seqlen_kv, int32_t pad, int32_t* out, hipStream_t stream) {
+    const int64_t n = rows * topk;
+    if (n == 0) return hipSuccess;
+    const bool vec = topk % 4 == 0 && ((uintptr_t)idx & 15u) == 0 && ((uintptr_t)out & 15u) == 0;
+    if (vec) {
+        const int64_t n_vec = n / 4;
+        hipLaunchKernelGGL(kv_remap_vec_kernel, dim3((unsigned)((n_vec + 255) / 256)), dim3(256), 0, stream,
+                           idx, n_vec, topk / 4, sq, seqlen_kv, pad, out);
+    } else {
+        hipLaunchKernelGGL(kv_remap_scalar_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                           idx, n, topk, sq, seqlen_kv, pad, out);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// full-width rotary embedding, out of place: out = rope(X) (direction +1) or
+// inv_rope(X) (direction -1) on the trailing pe channels of every head row,
+// nope channels copied.  The unfused route of PaddleFleet PR #1772 (PR body
+// item 1) materialises exactly this tensor before the postmix GEMM, and its
+// final backward rebuilds it (rope_full_out_of_place, follow-up commit); it
+// is here to run that route on this GPU for comparison.
+// Work item = (head row, 8-channel group): a nope group is copied; a pe item
+// covers one first-half group and its partner group.  HBM-bound; 16-byte
+// non-temporal loads and stores.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void rope_apply_kernel(
+    const uint16_t* __restrict__ X, const float* __restrict__ rcos, const float* __restrict__ rsin,
+    int64_t table_rows, const int32_t* __restrict__ positions, int64_t n_rows, int nh, int nope,
+    int pe, int direction, uint16_t* __restrict__ Out) {
+    const int d = nope + pe, h2 = pe >> 1;
+    const int items_per_row = (nope >> 3) + (h2 >> 3);
+    const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (item >= n_rows * items_per_row) return;
+    const int64_t row = item / items_per_row;            // (token, head)
+    const int g = (int)(item - row * items_per_row);
+    const uint16_t* x = X + row * d;
+    uint16_t* o = Out + row * d;
+    if (g < (nope >> 3)) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + 8 * g));
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(o + 8 * g));
+        return;
+    }
+    const int i0 = 8 * (g - (nope >> 3));
+    const int64_t prow = table_row(positions, row / nh, table_rows);
+    const u32x4 va = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + nope + i0));
+    const u32x4 vb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + nope + h2 + i0));
+    const f32x4* pc = reinterpret_cast<const f32x4*>(rcos + prow * h2 + i0);
+    const f32x4* ps = reinterpret_cast<const f32x4*>(rsin + prow * h2 + i0);
+    const f32x4 c0 = pc[0], c1 = pc[1], s0 = ps[0], s1 = ps[1];
+    const float sg = (float)direction;  // +1: turn by +phi, -1: by -phi
+    u32x4 oa, ob;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        uint32_t ra[2], rb[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int k = 2 * jj + e;
+            const float c = k < 4 ? c0[k] : c1[k - 4];
+            const float sn = sg * (k < 4 ? s0[k] : s1[k - 4]);
+            const float a = bf16_to_f32((va[jj] >> (16 * e)) & 0xffffu);
+            const float b = bf16_to_f32((vb[jj] >> (16 * e)) & 0xffffu);
+            ra[e] = f32_to_bf16_rne(a * c - b * sn);
+            rb[e] = f32_to_bf16_rne(b * c + a * sn);
+        }
+        oa[jj] = pack2(ra[0], ra[1]);
+        ob[jj] = pack2(rb[0], rb[1]);
+    }
+    __builtin_nontemporal_store(oa, reinterpret_cast<u32x4*>(o + nope + i0));
+    __builtin_nontemporal_store(ob, reinterpret_cast<u32x4*>(o + nope + h2 + i0));
+}
+
+hipError_t launch_rope_apply(const uint16_t* X, const float* rcos, const float* rsin, int64_t table_rows,
+                             const int32_t* positions, int64_t sq, int nh, int nope, int pe, int direction,
+                             uint16_t* Out, hipStream_t stream) {
+    const int64_t items = sq * nh * ((nope >> 3) + (pe >> 4));
+    if (items == 0) return hipSuccess;
+    hipLaunchKernelGGL(rope_apply_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, X,
+                       rcos, rsin, table_rows, positions, sq * nh, nh, nope, pe, direction, Out);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -1338,8 +1477,11 @@ hipError_t launch_mix(const MixArgs& a, bool dx, hipStream_t stream) {
     return dx ? launch_mix_dx<true>(a, stream) : launch_mix_dx<false>(a, stream);
 }
 
+// Tokens per weight-gradient block: sq*nh/32768 rounded up to a multiple of 4
+// (at least 4).  At sq=16384, nh=64 that is 32 tokens, 512 blocks: two
+// resident workgroups on each of 256 CUs, one round.
 int dw_tokens_per_block(int64_t sq, int nh) {
-    int64_t t = (sq * nh + 65535) / 65536;
+    int64_t t = (sq * nh + 32767) / 32768;
     t = (t + 3) / 4 * 4;
     if (t < 4) t = 4;
     if (t > (1 << 20)) t = 1 << 20;

@@ -40,6 +40,11 @@ struct DwArgs {
 hipError_t launch_mix(const MixArgs& a, bool dx, hipStream_t stream);
 int mix_part_width(int64_t sq, int nh, int nope, int pe);
 hipError_t launch_dw(const DwArgs& a, hipStream_t stream);
+hipError_t launch_kv_remap(const int32_t* idx, int64_t rows, int64_t sq, int64_t topk,
+                           int64_t seqlen_kv, int32_t pad, int32_t* out, hipStream_t stream);
+hipError_t launch_rope_apply(const uint16_t* X, const float* rcos, const float* rsin, int64_t table_rows,
+                             const int32_t* positions, int64_t sq, int nh, int nope, int pe, int direction,
+                             uint16_t* Out, hipStream_t stream);
 hipError_t launch_rope_table(double theta, int pe, int64_t rows, float* cos_out, float* sin_out,
                              int n_cu, hipStream_t stream);
 

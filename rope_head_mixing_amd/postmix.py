@@ -12,6 +12,10 @@ Entry points keep the C names:
     postmix_bwd_dw_workspace_bytes(sq, nh, nope, pe)
     postmix_bwd(dY, O, W, rope_cos, rope_sin, positions, nope, pe, ...)  -> (dO, dW)
     postmix_rope_table(theta, pe, table_rows, device=None)
+    postmix_kv_index_remap(idx, sq, seqlen_kv, pad_value=-1, out=None)
+    postmix_rope_apply(X, rope_cos, rope_sin, positions, nope, pe, direction, out=None)
+The unfused comparison route (unfused_fwd, unfused_bwd) is composed of these
+entry points only.
     postmix_set_general_kernels(enable)
 Tensors: O/Y/dY/dO bfloat16 [sq, nh, nope+pe]; W bfloat16 [nh, nh] (W[g,h], g =
 output head); rope_cos/rope_sin float32 [rows, pe/2]; positions int32 [sq];
@@ -65,6 +69,10 @@ def lib():
     L.postmix_bwd_dw.restype = ctypes.c_int
     L.postmix_bwd.argtypes = [P, P, P, P, P, I64, P, I64, I32, I32, I32, P, P, P, SZ, P]
     L.postmix_bwd.restype = ctypes.c_int
+    L.postmix_rope_apply.argtypes = [P, P, P, I64, P, I64, I32, I32, I32, I32, P, P]
+    L.postmix_rope_apply.restype = ctypes.c_int
+    L.postmix_kv_index_remap.argtypes = [P, I64, I64, I64, I64, I32, P, P]
+    L.postmix_kv_index_remap.restype = ctypes.c_int
     L.postmix_rope_table.argtypes = [F64, I32, I64, P, P, P]
     L.postmix_rope_table.restype = ctypes.c_int
     L.postmix_status_string.argtypes = [ctypes.c_int]
@@ -203,6 +211,46 @@ def postmix_bwd(dY, O, W, rope_cos, rope_sin, positions, nope: int, pe: int, out
                              nope, pe, dO.data_ptr(), dW.data_ptr(), workspace.data_ptr(),
                              ws_bytes, _stream_handle(dY.device)))
     return dO, dW
+
+
+def postmix_rope_apply(X, rope_cos, rope_sin, positions, nope: int, pe: int, direction: int,
+                       out=None):
+    """Out = inv_rope(X) (direction -1) or rope(X) (+1), materialised in bf16."""
+    torch = _torch()
+    _need(X, "X", torch.bfloat16, 3)
+    sq, nh, d = _act_shape(X, "X", nope, pe)
+    c, s, rows, p = _rope_ptrs(rope_cos, rope_sin, positions, pe, sq)
+    Out = torch.empty_like(X) if out is None else _need(out, "out", torch.bfloat16, 3)
+    _check(lib().postmix_rope_apply(X.data_ptr(), c, s, rows, p, sq, nh, nope, pe, int(direction),
+                                    Out.data_ptr(), _stream_handle(X.device)))
+    return Out
+
+
+def unfused_fwd(O, W, rope_cos, rope_sin, positions, nope: int, pe: int):
+    """The unfused route: X = inv_rope(O) materialised (bf16), then Y = W . X."""
+    X = postmix_rope_apply(O, rope_cos, rope_sin, positions, nope, pe, -1)
+    return postmix_fwd(X, W, None, None, None, nope + pe, 0)
+
+
+def unfused_bwd(dY, O, W, rope_cos, rope_sin, positions, nope: int, pe: int, workspace=None):
+    """The unfused backward route: rebuild X = inv_rope(O), the plain mix's
+    gradients dX = W^T dY and dW = sum dY X^T, then dO = rope(dX)."""
+    X = postmix_rope_apply(O, rope_cos, rope_sin, positions, nope, pe, -1)
+    dX = postmix_bwd_dx(dY, W, None, None, None, nope + pe, 0)
+    dW = postmix_bwd_dw(dY, X, None, None, None, nope + pe, 0, workspace=workspace)
+    dO = postmix_rope_apply(dX, rope_cos, rope_sin, positions, nope, pe, +1)
+    return dO, dW
+
+
+def postmix_kv_index_remap(idx, sq: int, seqlen_kv: int, pad_value: int = -1, out=None):
+    """Per-batch-local KV column indices -> flat-global: idx [b*sq, topk] int32."""
+    torch = _torch()
+    _need(idx, "idx", torch.int32, 2)
+    rows, topk = idx.shape
+    out = torch.empty_like(idx) if out is None else _need(out, "out", torch.int32, 2)
+    _check(lib().postmix_kv_index_remap(idx.data_ptr(), rows, sq, topk, seqlen_kv, pad_value,
+                                        out.data_ptr(), _stream_handle(idx.device)))
+    return out
 
 
 def postmix_set_general_kernels(enable: bool) -> bool:

@@ -172,9 +172,9 @@ def test_dw_argument_errors(kw, code, word):
 
 def test_workspace_size_is_a_function_of_the_shape():
     L = pm.lib()
-    # sq*nh = 2^20 -> 16 tokens per block -> 1024 blocks of nh*nh fp32 partials
-    assert L.postmix_bwd_dw_workspace_bytes(16384, 64, 448, 64) == 1024 * 64 * 64 * 4
-    assert L.postmix_bwd_dw_workspace_bytes(8192, 128, 448, 64) == 512 * 128 * 128 * 4
+    # sq*nh = 2^20 -> 32 tokens per block -> 512 blocks of nh*nh fp32 partials
+    assert L.postmix_bwd_dw_workspace_bytes(16384, 64, 448, 64) == 512 * 64 * 64 * 4
+    assert L.postmix_bwd_dw_workspace_bytes(8192, 128, 448, 64) == 256 * 128 * 128 * 4
     assert L.postmix_bwd_dw_workspace_bytes(0, 64, 448, 64) == 0
     assert L.postmix_bwd_dw_workspace_bytes(16, 0, 448, 64) == 0
     for args in [(64, 4, 48, 16), (8192, 3, 448, 64), (7, 5, 8, 16)]:
@@ -258,3 +258,36 @@ def test_fused_backward_argument_errors(kw, code, word):
     rc, msg = bwd(**kw)
     assert rc == code, msg
     assert word in msg
+
+
+def remap(**kw):
+    args = dict(idx=A, rows=8, sq=4, topk=16, seqlen_kv=1000, pad=-1, out=F)
+    args.update(kw)
+    L = pm.lib()
+    rc = L.postmix_kv_index_remap(args["idx"], args["rows"], args["sq"], args["topk"],
+                                  args["seqlen_kv"], args["pad"], args["out"], None)
+    return rc, L.postmix_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(rows=9), pm.PM_ERR_SHAPE, "multiple of sq"),
+    (dict(sq=0), pm.PM_ERR_SHAPE, "sq"),
+    (dict(topk=-1), pm.PM_ERR_SHAPE, "topk"),
+    (dict(seqlen_kv=-5), pm.PM_ERR_SHAPE, "seqlen_kv"),
+    (dict(rows=8, sq=1, seqlen_kv=1 << 29), pm.PM_ERR_SHAPE, "int32"),
+    (dict(idx=0), pm.PM_ERR_NULL, "idx"),
+    (dict(out=0), pm.PM_ERR_NULL, "out"),
+    (dict(idx=A + 2), pm.PM_ERR_ALIGN, "idx"),
+    (dict(out=A + 64), pm.PM_ERR_OVERLAP, "out"),
+])
+def test_kv_remap_argument_errors(kw, code, word):
+    rc, msg = remap(**kw)
+    assert rc == code, msg
+    assert word in msg
+
+
+def test_kv_remap_empty_and_in_place_pass_validation():
+    assert remap(rows=0, idx=0, out=0)[0] == pm.PM_OK
+    assert remap(topk=0, idx=0, out=0)[0] == pm.PM_OK
+    rc, msg = remap(out=A)  # in place: validation passes, then the device check decides
+    assert rc not in (pm.PM_ERR_NULL, pm.PM_ERR_SHAPE, pm.PM_ERR_ALIGN, pm.PM_ERR_OVERLAP), msg

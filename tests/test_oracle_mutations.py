@@ -11,6 +11,7 @@ import inspect
 import pytest
 
 import oracle
+from tests import test_oracle_kv_remap as kv_pins
 from tests import test_oracle_pins as pins
 
 # (name, exact source text, replacement, which occurrence)
@@ -51,6 +52,11 @@ MUTANTS = [
      "double wg = bf16_bits_to_double(W[h * nh + g]);", 0),
     ("dw_at_wrong_head", "inv_rope_elem_bf16(p->O, s, h, c, nh, p->nope, p->pe, cs, sn);",
      "inv_rope_elem_bf16(p->O, s, g, c, nh, p->nope, p->pe, cs, sn);", 0),
+    ("kv_remap_batch_off_by_one", "out[r * topk + k] = v >= 0 ? (int32_t)(v + b * seqlen_kv) : pad_value;",
+     "out[r * topk + k] = v >= 0 ? (int32_t)(v + (b + 1) * seqlen_kv) : pad_value;", 0),
+    ("kv_remap_zero_is_padding", "out[r * topk + k] = v >= 0 ? (int32_t)(v + b * seqlen_kv) : pad_value;",
+     "out[r * topk + k] = v > 0 ? (int32_t)(v + b * seqlen_kv) : pad_value;", 0),
+    ("kv_remap_batch_of_column", "int64_t b = r / sq;", "int64_t b = r % sq;", 0),
 ]
 
 
@@ -64,7 +70,8 @@ def _replace_nth(text, old, new, n):
 def _pin_cases():
     """(name, callable) for every pin, parametrized cases expanded."""
     out = []
-    for name, fn in inspect.getmembers(pins, inspect.isfunction):
+    members = inspect.getmembers(pins, inspect.isfunction) + inspect.getmembers(kv_pins, inspect.isfunction)
+    for name, fn in members:
         # the stored-output regression guard is the oracle's own output, not a pin
         if not name.startswith("test_") or name.startswith("test_golden"):
             continue
