@@ -271,8 +271,22 @@ def main():
               for i, op in enumerate(ops)}
         return wall, ms
 
+    # the unfused route (materialised inv_rope(O); rebuilt in the backward) and
+    # the KV index remap at the pages' table shape [1 * 16384, 2176]
+    calls["unfused_fwd"] = lambda: pm.unfused_fwd(dO_in, dW_in, cos, sin, dpos, case.nope, case.pe)
+    calls["unfused_bwd"] = lambda: pm.unfused_bwd(ddY, dO_in, dW_in, cos, sin, dpos, case.nope, case.pe,
+                                                  workspace=ws)
+    kv_rows, kv_topk, kv_seqlen = 16384, 2176, 16384
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    kv_idx = torch.randint(-1, kv_seqlen, (kv_rows, kv_topk), generator=gen, device="cuda",
+                           dtype=torch.int32)
+    kv_out = torch.empty_like(kv_idx)
+    calls["kv_remap"] = lambda: pm.postmix_kv_index_remap(kv_idx, kv_rows, kv_seqlen, out=kv_out)
+
     wall, per_op_ms = timed_loop(STEP_OPS)
     _, extra_ms = timed_loop(EXTRA_OPS)
+    _, cmp_ms = timed_loop(("unfused_fwd", "unfused_bwd", "kv_remap"))
     per_op_ms.update(extra_ms)
     ops = list(STEP_OPS) + list(EXTRA_OPS)
     ms_per_step = wall * 1e3 / args.steps
@@ -337,6 +351,22 @@ def main():
         "ops": op_report,
         "pct_peak": round(100 * value / PEAK_GBPS, 1),
         "roofline": roofline,
+        "unfused_route": {
+            "fwd_us": round(cmp_ms["unfused_fwd"] * 1e3, 1),
+            "bwd_us": round(cmp_ms["unfused_bwd"] * 1e3, 1),
+            "fused_fwd_saves_pct": round(100 * (1 - per_op_ms["fwd"] / cmp_ms["unfused_fwd"]), 1),
+            "fused_bwd_saves_pct": round(100 * (1 - per_op_ms["bwd"] / cmp_ms["unfused_bwd"]), 1),
+            "extra_live_bytes": case.sq * case.nh * case.d * 2,
+            "note": "same library's kernels: inv_rope(O) materialised in bf16, then the plain mix; "
+                    "backward rebuilds it, plain dx and dW, then rope(dX)",
+        },
+        "kv_remap": {
+            "table": [kv_rows, kv_topk],
+            "us": round(cmp_ms["kv_remap"] * 1e3, 1),
+            "GBps": round(2 * kv_rows * kv_topk * 4 / (cmp_ms["kv_remap"] * 1e-3) / 1e9, 1),
+            "pct_peak": round(100 * 2 * kv_rows * kv_topk * 4 / (cmp_ms["kv_remap"] * 1e-3) / 1e9
+                              / PEAK_GBPS, 1),
+        },
         "copy_GBps": round(copy_gbps, 1),
         "input_generation_s": round(gen_s, 1),
         "context_pages": PAGES_CONTEXT,
