@@ -162,7 +162,6 @@ int mix_common(const char* xname, const pm_bf16* X, const pm_bf16* W, const floa
     a.n_cu = n_cu;
     a.waves_per_cu = 16;
     a.force_general = g_force_general.load(std::memory_order_relaxed) != 0;
-    a.mix_persistent = false;
     hipError_t e = pm::launch_mix(a, dx, (hipStream_t)stream);
     if (e != hipSuccess) return fail(PM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -323,7 +322,6 @@ int postmix_bwd(const pm_bf16* dY, const pm_bf16* O, const pm_bf16* W, const flo
     mx.n_cu = n_cu;
     mx.waves_per_cu = 16;
     mx.force_general = g_force_general.load(std::memory_order_relaxed) != 0;
-    mx.mix_persistent = false;
     pm::DwArgs a;
     a.dY = dY;
     a.O = O;

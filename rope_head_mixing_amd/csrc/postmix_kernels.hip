@@ -541,10 +541,8 @@ __global__ __launch_bounds__(256) void rope_table_kernel(double theta, int pe, i
 //
 // A tile is (token s, channel part of CP channels): [nh x CP], contiguous per
 // row, read with 16-byte non-temporal loads like a copy and written back the
-// same way.  Workgroups loop over tiles (tile = blockIdx.x + k*gridDim.x); the
-// next tile's loads are issued into registers before the current tile is
-// computed, so they are in flight during the compute and the store.  With a
-// grid of one workgroup per tile the loop runs once.
+// same way.  One workgroup per tile: the tile's loads are issued into
+// registers first, so they are in flight while W is staged.
 //   setup: W -> LDS (rows padded) -> each wave copies its B operand (W^T for
 //          the forward, W for dx) into registers.  W's LDS is then reused as
 //          the fp32 pe scratch.
@@ -596,7 +594,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* base, int pitch, int l
     return as_bf16x8(v);
 }
 
-template <int NH, int CP, int WAVES, bool DX, bool PERSIST>
+template <int NH, int CP, int WAVES, bool DX>
 __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
@@ -634,7 +632,7 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
             v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xs + row * (int64_t)d + 8 * c8));
         }
     };
-    if (t < n_tiles) load_tile(t);  // first tile's loads overlap the W setup
+    if (t < n_tiles) load_tile(t);  // the tile's loads overlap the W setup
 
     // setup: W -> LDS -> B operand in registers
 #pragma unroll
@@ -661,7 +659,7 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
     __syncthreads();  // W's LDS becomes the pe scratch
 
     const int Q = lane >> 5;
-    for (; t < n_tiles; t += (PERSIST ? (int64_t)gridDim.x : n_tiles)) {
+    if (t < n_tiles) {
         const int64_t s = t / cpt;
         const int part = (int)(t - s * cpt);
         const int c_base = part * CP;
@@ -675,7 +673,6 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
         const bool tile_pe = pe > 0 && c_base + CP > nope;
         if (tile_pe && tid < (pe >> 2)) reinterpret_cast<f32x4*>(csl)[tid] = rope_v;  // cos then sin
         __syncthreads();
-        if (PERSIST && t + gridDim.x < n_tiles) load_tile(t + gridDim.x);  // in flight meanwhile
 
         for (int b = wave; b < C::MBP; b += WAVES) {
             f32x16 acc[C::NB];
@@ -750,7 +747,6 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
             }
             __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(outs + row * (int64_t)d + cl));
         }
-        __syncthreads();  // the tile and the scratch are rewritten next iteration
     }
 }
 
@@ -1402,16 +1398,15 @@ static hipError_t launch_mix_t(const MixArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// token-part kernel: tiles = (token, CP-channel part); grid = one workgroup per
-// tile, or (persistent) as many workgroups as fit on the device at once
-template <int NH, int CP, int WAVES, bool DX, bool PERSIST>
-static hipError_t launch_part_one(const MixArgs& a, hipStream_t stream) {
+// token-part kernel: one workgroup per tile = (token, CP-channel part)
+template <int NH, int CP, int WAVES, bool DX>
+static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
     using C = PartCfg<NH, CP, WAVES>;
     const int d = a.nope + a.pe;
     const int cpt = d / CP;
     const int64_t n_tiles = a.sq * cpt;
     const size_t lds = C::lds_bytes(a.pe);
-    auto kern = mix_part_kernel<NH, CP, WAVES, DX, PERSIST>;
+    auto kern = mix_part_kernel<NH, CP, WAVES, DX>;
     static bool attr_done = false;  // idempotent; a race only repeats the call
     if (!attr_done) {
         const size_t lds_max = C::lds_bytes(CP);
@@ -1422,24 +1417,9 @@ static hipError_t launch_part_one(const MixArgs& a, hipStream_t stream) {
         }
         attr_done = true;
     }
-    int64_t grid = n_tiles;
-    if (PERSIST) {
-        int per_cu = 0;
-        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, 64 * WAVES, lds);
-        if (e != hipSuccess) return e;
-        if (per_cu < 1) per_cu = 1;
-        const int64_t cap = (int64_t)a.n_cu * per_cu;
-        if (grid > cap) grid = cap;
-    }
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WAVES), lds, stream, a.X, a.W, a.rcos,
+    hipLaunchKernelGGL(kern, dim3((unsigned)n_tiles), dim3(64 * WAVES), lds, stream, a.X, a.W, a.rcos,
                        a.rsin, a.table_rows, a.positions, a.nope, a.pe, cpt, n_tiles, a.Out);
     return hipGetLastError();
-}
-
-template <int NH, int CP, int WAVES, bool DX>
-static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
-    return a.mix_persistent ? launch_part_one<NH, CP, WAVES, DX, true>(a, stream)
-                            : launch_part_one<NH, CP, WAVES, DX, false>(a, stream);
 }
 
 // Channel-part width of the token-part kernel for this shape, or 0 when the

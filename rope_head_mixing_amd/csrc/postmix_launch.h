@@ -20,7 +20,6 @@ struct MixArgs {
     int n_cu;               // compute units of the device
     int waves_per_cu;       // resident single-wave workgroups to aim for per CU
     bool force_general;     // use the general (persistent) kernel for every shape
-    bool mix_persistent;    // token-part kernel: persistent grid instead of one workgroup per tile
 };
 
 struct DwArgs {
