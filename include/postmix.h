@@ -100,9 +100,11 @@ int postmix_bwd_dx(const pm_bf16 *dY, const pm_bf16 *W, const float *rope_cos,
                    int32_t nope, int32_t pe, pm_bf16 *dO, void *stream);
 
 /*
- * Bytes of device workspace postmix_bwd_dw needs for this shape (a multiple
- * of 256).  Depends on (sq, nh, nope, pe) only.  Returns 0 for sq == 0 and
- * for shapes outside the limits.
+ * Bytes of device workspace postmix_bwd_dw and postmix_bwd need for this
+ * shape (a multiple of 256): one nh x nh fp32 partial per token block, for
+ * the larger of the two block counts the calls may use.  Depends on
+ * (sq, nh, nope, pe) only.  Returns 0 for sq == 0 and for shapes outside the
+ * limits.
  */
 size_t postmix_bwd_dw_workspace_bytes(int64_t sq, int32_t nh, int32_t nope,
                                       int32_t pe);
@@ -137,9 +139,10 @@ int postmix_bwd_dw(const pm_bf16 *dY, const pm_bf16 *O, const float *rope_cos,
  * gradient and the weight-gradient partials.  That is one full read of dY
  * fewer than the two separate calls.  Other shapes (or
  * postmix_set_general_kernels(1)) run the two separate computations.
- * dO is bitwise the same as postmix_bwd_dx's; dW is deterministic and uses
- * the same token blocks and reduction as postmix_bwd_dw, but sums each block
- * in a different order, so the two may differ in the last bits.
+ * dO is bitwise the same as postmix_bwd_dx's; dW is deterministic (fixed
+ * token blocks, half the size of postmix_bwd_dw's, and the same fixed-order
+ * reduction), but it sums in a different order than postmix_bwd_dw, so the
+ * two may differ in the last bits.
  *   dY, O [sq, nh, nope+pe] bf16, read;  W [nh, nh] bf16, read
  *   dO    [sq, nh, nope+pe] bf16, written;  dW [nh, nh] fp32, written
  *   workspace as postmix_bwd_dw (postmix_bwd_dw_workspace_bytes bytes).

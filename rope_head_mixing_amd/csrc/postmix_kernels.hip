@@ -987,25 +987,27 @@ __global__ __launch_bounds__(256) void dw_chunk_kernel(
 // ---------------------------------------------------------------------------
 // fused backward: input gradient and weight-gradient partials in one pass
 //
-// One read of dY and O serves both gradients: the block partition is the
-// weight gradient's (fixed token blocks, one fp32 partial each), and every
-// (token, 128-channel) chunk of dY and O is staged in LDS once.  From it
+// One read of dY and O serves both gradients: fixed token blocks (a function
+// of the shape only), one fp32 weight-gradient partial each, and every
+// (token, CH-channel) chunk of dY and O is staged in LDS once.  CH = 256 with
+// 16 waves (one workgroup per CU) where d allows, else CH = 128 with 8 waves.
+// With KSET = WAVES/4 waves per dW output tile:
 //   - dW:  wave w owns output tile w%4 (g-block tile/2, h-block tile%2) over
-//          the k-steps of parity w/4; the two waves of a tile are added in
-//          the fixed order (w) + (w+4) at the end of the block;
-//   - dx:  wave w owns M-block w%4 and N-block w/4 of the chunk's head mix
+//          the k-steps t = w/4 (mod KSET); at the end of the block the KSET
+//          waves of a tile are added in k-set order (fixed);
+//   - dx:  wave w owns M-block w%(CH/32) and N-block w/(CH/32) of the chunk's head mix
 //          dX[c, h] = sum_g dY[g, c] W[g, h] (A = dY^T by transposing LDS
 //          loads, B = W in registers), writes nope results to an LDS output
 //          chunk and pe results to an fp32 scratch; the store phase rotates
 //          the pe pairs by +phi and writes dO rows with non-temporal stores.
 // The dx arithmetic (MFMA inputs, k order, rotation expression) is that of
 // the token-part kernel, so dO is bitwise the same as postmix_bwd_dx's.
-// nh = 64, d a multiple of 128, pe <= 128.
+// nh = 64, d a multiple of 128, pe <= 128 (all pe channels in a token's last chunk).
 // ---------------------------------------------------------------------------
 
-template <int NH, int CH>
+template <int NH, int CH, int WAVES>
 struct BwdCfg {
-    static constexpr int WAVES = 8, NT = 512;
+    static constexpr int NT = 64 * WAVES;
     static constexpr int NB = NH / 32, KB = NH / 16;
     static constexpr int PITCH = CH + 8;
     static constexpr int WPITCH = NH + 8;
@@ -1017,7 +1019,7 @@ struct BwdCfg {
     static constexpr int MBC = CH / 32;             // M-blocks of the head mix per chunk
     static constexpr int NTILE = NB * NB;           // dW output tiles
     static constexpr int KSET = WAVES / NTILE;      // waves per dW tile
-    static_assert(NH == 64 && MBC * NB == WAVES && KSET == 2 && VPO % NT == 0, "fused shape");
+    static_assert(NH == 64 && MBC * NB == WAVES && KS % KSET == 0 && VPO % NT == 0, "fused shape");
     __host__ __device__ static size_t aux_bytes(int pe) {
         const size_t w = (size_t)NH * WPITCH * 2, p = (size_t)NH * (pe + 4) * 4;
         return w > p ? w : p;
@@ -1028,13 +1030,13 @@ struct BwdCfg {
     }
 };
 
-template <int NH, int CH>
-__global__ __launch_bounds__(512, 4) void bwd_fused_kernel(
+template <int NH, int CH, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O, const uint16_t* __restrict__ W,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
     const int32_t* __restrict__ positions, int64_t sq, int nope, int pe,
     uint16_t* __restrict__ dO, float* __restrict__ partials, int tokens_per_block) {
-    using C = BwdCfg<NH, CH>;
+    using C = BwdCfg<NH, CH, WAVES>;
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint16_t* dyl = smem;                               // [NH][PITCH]
     uint16_t* ol = dyl + NH * C::PITCH;                 // [NH][PITCH]
@@ -1047,7 +1049,12 @@ __global__ __launch_bounds__(512, 4) void bwd_fused_kernel(
 
     const int d = nope + pe, h2 = pe >> 1;
     const int cpt = d / CH;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, Q = half;
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, Q = half;
+    const int wave = tid >> 6;
+    // the cos row of a pe chunk is fetched by lanes < pe/8 of wave 0, the sin
+    // row by those of wave 1 (a wave-uniform table pointer)
+    const bool rope_lane = wave < 2 && lane < (pe >> 3);
+    const float* const rtab = __builtin_amdgcn_readfirstlane(tid >> 6) == 0 ? rcos : rsin;
     const int tile = wave % C::NTILE, kset = wave / C::NTILE;
     const int gb = tile / C::NB, hb = tile % C::NB;
     const int mb = wave % C::MBC, nb = wave / C::MBC;
@@ -1072,9 +1079,9 @@ __global__ __launch_bounds__(512, 4) void bwd_fused_kernel(
             const uint16_t* src = (op == 0 ? dY : O) + rowbase + row * (int64_t)d + 8 * c8;
             v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
         }
-        if (pe > 0 && (part + 1) * CH > nope && tid < (pe >> 2)) {
+        if (pe > 0 && (part + 1) * CH > nope && rope_lane) {
             const int64_t prow = table_row(positions, s, table_rows);
-            rope_v = reinterpret_cast<const f32x4*>((tid < (pe >> 3) ? rcos : rsin) + prow * h2)[tid % (pe >> 3)];
+            rope_v = reinterpret_cast<const f32x4*>(rtab + prow * h2)[lane];
         }
     };
     auto stage_chunk = [&](int k) {  // registers of chunk k -> LDS
@@ -1087,8 +1094,8 @@ __global__ __launch_bounds__(512, 4) void bwd_fused_kernel(
             const int row = rem / C::VPR, c8 = rem % C::VPR;
             *reinterpret_cast<u32x4*>((op == 0 ? dyl : ol) + row * C::PITCH + 8 * c8) = v[j];
         }
-        if (pe > 0 && (part + 1) * CH > nope && tid < (pe >> 2))
-            reinterpret_cast<f32x4*>(rope_l + (k & 1) * pe)[tid] = rope_v;
+        if (pe > 0 && (part + 1) * CH > nope && rope_lane)
+            reinterpret_cast<f32x4*>(rope_l + (k & 1) * pe)[wave * (pe >> 3) + lane] = rope_v;
     };
     if (nchunks > 0) load_chunk(0);
 
@@ -1126,7 +1133,8 @@ __global__ __launch_bounds__(512, 4) void bwd_fused_kernel(
 
         // ---- weight gradient: tile (gb, hb), k-steps t = kset, kset + 2, ...
 #pragma unroll
-        for (int t = kset; t < C::KS; t += C::KSET) {
+        for (int j = 0; j < C::KS / C::KSET; ++j) {
+            const int t = kset + C::KSET * j;
             const int c = 16 * t + 8 * half;
             const int cg = c_base + c;
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(dyl + (32 * gb + (lane & 31)) * C::PITCH + c);
@@ -1236,16 +1244,18 @@ __global__ __launch_bounds__(512, 4) void bwd_fused_kernel(
         __syncthreads();  // dO buffers read; chunk k+1 staged
     }
 
-    // ---- dW partial: tile sum (wave tile) + (wave tile + 4), fixed order
+    // ---- dW partial: the k-sets of each tile summed in k-set order (fixed)
     float* red = reinterpret_cast<float*>(smem);
-    if (kset == 1) {
+    if (kset != 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red[(tile * 16 + r) * 64 + lane] = acc_w[r];
+        for (int r = 0; r < 16; ++r) red[(((kset - 1) * C::NTILE + tile) * 16 + r) * 64 + lane] = acc_w[r];
     }
     __syncthreads();
     if (kset != 0) return;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc_w[r] += red[(tile * 16 + r) * 64 + lane];
+    for (int k = 1; k < C::KSET; ++k)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_w[r] += red[(((k - 1) * C::NTILE + tile) * 16 + r) * 64 + lane];
     float* part_out = partials + (int64_t)blockIdx.x * NH * NH;
     const int h = 32 * hb + (lane & 31);
 #pragma unroll
@@ -1473,6 +1483,23 @@ int64_t dw_num_blocks(int64_t sq, int nh) {
     return (sq + t - 1) / t;
 }
 
+// The fused backward uses blocks of half as many tokens (sq*nh/65536 rounded
+// up to a multiple of 4, at least 4): its one 16-wave workgroup per CU then
+// works through four rounds of blocks at the production shape, which balances
+// better than two.
+int bwd_fused_tokens_per_block(int64_t sq, int nh) {
+    int64_t t = (sq * nh + 65535) / 65536;
+    t = (t + 3) / 4 * 4;
+    if (t < 4) t = 4;
+    if (t > (1 << 20)) t = 1 << 20;
+    return (int)t;
+}
+
+int64_t bwd_fused_num_blocks(int64_t sq, int nh) {
+    const int t = bwd_fused_tokens_per_block(sq, nh);
+    return (sq + t - 1) / t;
+}
+
 // Chunk width of the LDS-staged weight-gradient kernel, or 0 for the direct kernel.
 int dw_chunk_width(int nh, int nope, int pe) {
     if (nh != 32 && nh != 64 && nh != 128) return 0;
@@ -1508,12 +1535,13 @@ bool bwd_fused_applies(int nh, int nope, int pe) {
     return nh == 64 && d % 128 == 0 && pe <= 128;
 }
 
-hipError_t launch_bwd_fused(const MixArgs& mx, const DwArgs& a, hipStream_t stream) {
-    using C = BwdCfg<64, 128>;
-    const int tpb = dw_tokens_per_block(a.sq, a.nh);
-    const int64_t nb = dw_num_blocks(a.sq, a.nh);
-    const size_t lds = C::lds_bytes(a.pe);
-    auto kern = bwd_fused_kernel<64, 128>;
+// chunk width of the fused backward: 256 channels (16 waves) where d allows
+static int bwd_fused_chunk(int d) { return d % 256 == 0 ? 256 : 128; }
+
+template <int CH, int WAVES>
+static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int tpb, int64_t nb, hipStream_t stream) {
+    using C = BwdCfg<64, CH, WAVES>;
+    auto kern = bwd_fused_kernel<64, CH, WAVES>;
     static bool attr_done = false;  // idempotent; a race only repeats the call
     if (!attr_done) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1521,9 +1549,16 @@ hipError_t launch_bwd_fused(const MixArgs& mx, const DwArgs& a, hipStream_t stre
         if (e != hipSuccess) return e;
         attr_done = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(512), lds, stream, a.dY, a.O, mx.W, a.rcos, a.rsin,
-                       a.table_rows, a.positions, a.sq, a.nope, a.pe, mx.Out, a.partials, tpb);
-    hipError_t err = hipGetLastError();
+    hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), C::lds_bytes(a.pe), stream, a.dY, a.O, mx.W,
+                       a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nope, a.pe, mx.Out, a.partials, tpb);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_fused(const MixArgs& mx, const DwArgs& a, hipStream_t stream) {
+    const int tpb = bwd_fused_tokens_per_block(a.sq, a.nh);
+    const int64_t nb = bwd_fused_num_blocks(a.sq, a.nh);
+    hipError_t err = bwd_fused_chunk(a.nope + a.pe) == 256 ? launch_bwd_fused_t<256, 16>(mx, a, tpb, nb, stream)
+                                                          : launch_bwd_fused_t<128, 8>(mx, a, tpb, nb, stream);
     if (err != hipSuccess) return err;
     const int64_t ne = (int64_t)a.nh * a.nh;
     hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((ne + 63) / 64)), dim3(1024), 0, stream,

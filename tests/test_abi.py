@@ -173,7 +173,11 @@ def test_dw_argument_errors(kw, code, word):
 def test_workspace_size_is_a_function_of_the_shape():
     L = pm.lib()
     # sq*nh = 2^20 -> 32 tokens per block -> 512 blocks of nh*nh fp32 partials
-    assert L.postmix_bwd_dw_workspace_bytes(16384, 64, 448, 64) == 512 * 64 * 64 * 4
+    # nh = 64 with d a multiple of 128: the single-pass backward's 1024 blocks of 16 tokens
+    assert L.postmix_bwd_dw_workspace_bytes(16384, 64, 448, 64) == 1024 * 64 * 64 * 4
+    # otherwise the weight-gradient kernels' 512 blocks of 32 tokens
+    assert L.postmix_bwd_dw_workspace_bytes(16384, 64, 440, 64) == 512 * 64 * 64 * 4
+    assert L.postmix_bwd_dw_workspace_bytes(16384, 32, 448, 64) == 1024 * 32 * 32 * 4  # 16-token blocks
     assert L.postmix_bwd_dw_workspace_bytes(8192, 128, 448, 64) == 256 * 128 * 128 * 4
     assert L.postmix_bwd_dw_workspace_bytes(0, 64, 448, 64) == 0
     assert L.postmix_bwd_dw_workspace_bytes(16, 0, 448, 64) == 0
