@@ -138,17 +138,37 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix
     def short(name):
         return name.split("(")[0].replace("void ", "").replace("pm::", "")
 
-    # per-kernel durations in launch order, to average the timed region (the
-    # last `timed` launches; the earlier ones are the warm-up)
+    # per-kernel durations in launch order.  The timed steps are the last
+    # `timed` repetitions of the step's kernel sequence (fwd then bwd) in the
+    # longest back-to-back run of it; other kernels average their last `timed`
+    # launches (each extra op is timed in a loop of its own, but some kernels
+    # serve several ops, so that figure is indicative only).
+    seq = sorted((int(r["Start_Timestamp"]), short(r["Kernel_Name"]),
+                  (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+                 for r in csv.DictReader(open(one(os.path.join(trace_dir, "**", "*kernel_trace.csv")))))
+    names = [x[1] for x in seq]
+    pat = [k.strip() for op in STEP_OPS for k in KERNELS_NH64[op].split("+")]
+    occ = [i for i in range(len(seq) - len(pat) + 1) if names[i:i + len(pat)] == pat]
+    runs, cur = [], []
+    for i in occ:
+        if cur and i != cur[-1] + len(pat):
+            runs.append(cur)
+            cur = []
+        cur.append(i)
+    if cur:
+        runs.append(cur)
+    step_run = max(runs, key=len) if runs else []
+    step_durs = collections.defaultdict(list)
+    for i in step_run[-timed:]:
+        for j, n in enumerate(pat):
+            step_durs[n].append(seq[i + j][2])
     launches = collections.defaultdict(list)
-    for r in csv.DictReader(open(one(os.path.join(trace_dir, "**", "*kernel_trace.csv")))):
-        launches[short(r["Kernel_Name"])].append(
-            (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    for _, n, dur in seq:
+        launches[n].append(dur)
     rows = []
     for r in stats:
         n = short(r["Name"])
-        durs = [x[1] for x in sorted(launches.get(n, []))]
-        tail = durs[-timed:] if durs else []
+        tail = step_durs.get(n) or launches.get(n, [])[-timed:]
         rows.append((n, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
                      sum(tail) / len(tail) if tail else float("nan"),
                      float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
@@ -174,8 +194,10 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix
              "Commands (from the repository root on one MI355X):", "", "```", command_note.strip(),
              "```", "", f"Kernel source sha256[:16]: `{doc['kernel_source_sha']}`", "",
              "## Kernel durations (rocprofv3 --kernel-trace --stats)", "",
-             f"`timed avg` is the mean of the last {timed} launches of each kernel, the benchmark's "
-             "timed steps; `avg` includes the warm-up launches.", "",
+             f"`timed avg`: for the step's kernels ({' + '.join(pat)}), the mean over the "
+             f"benchmark's {len(step_run[-timed:])} timed steps (the last {timed} repetitions of that "
+             f"sequence in its back-to-back run of {len(step_run)}); for other kernels the mean of "
+             f"their last {timed} launches.  `avg` includes warm-up launches.", "",
              "| kernel | calls | avg us | timed avg us | min us | max us |", "|---|---|---|---|---|---|"]
     lines += [f"| `{n}` | {c} | {a:.1f} | {ta:.1f} | {mn:.1f} | {mx:.1f} |" for n, c, a, ta, mn, mx in rows]
     lines += ["", "## HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)", "",

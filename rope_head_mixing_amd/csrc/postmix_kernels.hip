@@ -1326,64 +1326,79 @@ hipError_t launch_kv_remap(const int32_t* idx, int64_t rows, int64_t sq, int64_t
 // item 1) materialises exactly this tensor before the postmix GEMM, and its
 // final backward rebuilds it (rope_full_out_of_place, follow-up commit); it
 // is here to run that route on this GPU for comparison.
-// Work item = (head row, 8-channel group): a nope group is copied; a pe item
-// covers one first-half group and its partner group.  HBM-bound; 16-byte
+// Workgroup = (token, group of R head rows), R = min(nh, max(1, 512 / (d/8))).
+// Its first R*nope/8 work items copy the nope vectors of the R rows; the last
+// R*pe/8 items each produce one pe output vector from its own input vector and
+// the partner vector pe/2 channels away.  At d = 512 (R = 8) that is seven
+// copy waves and one rotation wave, so no wave mixes the two paths.  Index
+// arithmetic is 32-bit apart from the row base.  HBM-bound; 16-byte
 // non-temporal loads and stores.
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void rope_apply_kernel(
+__global__ __launch_bounds__(512) void rope_apply_kernel(
     const uint16_t* __restrict__ X, const float* __restrict__ rcos, const float* __restrict__ rsin,
-    int64_t table_rows, const int32_t* __restrict__ positions, int64_t n_rows, int nh, int nope,
-    int pe, int direction, uint16_t* __restrict__ Out) {
-    const int d = nope + pe, h2 = pe >> 1;
-    const int items_per_row = (nope >> 3) + (h2 >> 3);
-    const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (item >= n_rows * items_per_row) return;
-    const int64_t row = item / items_per_row;            // (token, head)
-    const int g = (int)(item - row * items_per_row);
-    const uint16_t* x = X + row * d;
-    uint16_t* o = Out + row * d;
-    if (g < (nope >> 3)) {
-        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + 8 * g));
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(o + 8 * g));
-        return;
-    }
-    const int i0 = 8 * (g - (nope >> 3));
-    const int64_t prow = table_row(positions, row / nh, table_rows);
-    const u32x4 va = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + nope + i0));
-    const u32x4 vb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + nope + h2 + i0));
-    const f32x4* pc = reinterpret_cast<const f32x4*>(rcos + prow * h2 + i0);
-    const f32x4* ps = reinterpret_cast<const f32x4*>(rsin + prow * h2 + i0);
-    const f32x4 c0 = pc[0], c1 = pc[1], s0 = ps[0], s1 = ps[1];
+    int64_t table_rows, const int32_t* __restrict__ positions, int nh, int nope, int pe, int rows_per_wg,
+    int groups_per_token, int direction, uint16_t* __restrict__ Out) {
+    const int d = nope + pe, h2 = pe >> 1, nv = nope >> 3, pv = pe >> 3;
+    const int64_t s = blockIdx.x / (unsigned)groups_per_token;      // token
+    const int h0 = (int)(blockIdx.x - s * groups_per_token) * rows_per_wg;
+    const int n_copy = rows_per_wg * nv, n_all = rows_per_wg * (nv + pv);
     const float sg = (float)direction;  // +1: turn by +phi, -1: by -phi
-    u32x4 oa, ob;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        uint32_t ra[2], rb[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int k = 2 * jj + e;
-            const float c = k < 4 ? c0[k] : c1[k - 4];
-            const float sn = sg * (k < 4 ? s0[k] : s1[k - 4]);
-            const float a = bf16_to_f32((va[jj] >> (16 * e)) & 0xffffu);
-            const float b = bf16_to_f32((vb[jj] >> (16 * e)) & 0xffffu);
-            ra[e] = f32_to_bf16_rne(a * c - b * sn);
-            rb[e] = f32_to_bf16_rne(b * c + a * sn);
+    for (int t = threadIdx.x; t < n_all; t += blockDim.x) {
+        if (t < n_copy) {
+            const int r = t / nv, v = t - r * nv;
+            if (h0 + r >= nh) continue;
+            const int64_t off = (s * nh + h0 + r) * d + 8 * v;
+            const u32x4 val = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(X + off));
+            __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(Out + off));
+            continue;
         }
-        oa[jj] = pack2(ra[0], ra[1]);
-        ob[jj] = pack2(rb[0], rb[1]);
+        const int u = t - n_copy, r = u / pv, i0 = 8 * (u - r * pv);
+        if (h0 + r >= nh) continue;
+        const bool first = i0 < h2;
+        const int ii = first ? i0 : i0 - h2;
+        const int64_t base = (s * nh + h0 + r) * d + nope;
+        const u32x4 own = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(X + base + i0));
+        const u32x4 par = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(X + base + (first ? i0 + h2 : ii)));
+        const int64_t prow = table_row(positions, s, table_rows);
+        const f32x4* pc = reinterpret_cast<const f32x4*>(rcos + prow * h2 + ii);
+        const f32x4* ps = reinterpret_cast<const f32x4*>(rsin + prow * h2 + ii);
+        const f32x4 c0 = pc[0], c1 = pc[1], s0 = ps[0], s1 = ps[1];
+        // first half: a C - b S';  second half: b C + a S'  (S' = direction * S)
+        const float sp = first ? -sg : sg;
+        u32x4 o;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            uint32_t rr[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int k = 2 * jj + e;
+                const float c = k < 4 ? c0[k] : c1[k - 4];
+                const float sn = sp * (k < 4 ? s0[k] : s1[k - 4]);
+                const float x = bf16_to_f32((own[jj] >> (16 * e)) & 0xffffu);
+                const float y = bf16_to_f32((par[jj] >> (16 * e)) & 0xffffu);
+                rr[e] = f32_to_bf16_rne(x * c + y * sn);
+            }
+            o[jj] = pack2(rr[0], rr[1]);
+        }
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(Out + base + i0));
     }
-    __builtin_nontemporal_store(oa, reinterpret_cast<u32x4*>(o + nope + i0));
-    __builtin_nontemporal_store(ob, reinterpret_cast<u32x4*>(o + nope + h2 + i0));
 }
 
 hipError_t launch_rope_apply(const uint16_t* X, const float* rcos, const float* rsin, int64_t table_rows,
                              const int32_t* positions, int64_t sq, int nh, int nope, int pe, int direction,
                              uint16_t* Out, hipStream_t stream) {
-    const int64_t items = sq * nh * ((nope >> 3) + (pe >> 4));
-    if (items == 0) return hipSuccess;
-    hipLaunchKernelGGL(rope_apply_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, X,
-                       rcos, rsin, table_rows, positions, sq * nh, nh, nope, pe, direction, Out);
+    const int vpr = (nope + pe) / 8;
+    if (sq == 0 || vpr == 0) return hipSuccess;
+    int rows_per_wg = vpr >= 512 ? 1 : 512 / vpr;
+    if (rows_per_wg > nh) rows_per_wg = nh;
+    const int groups = (nh + rows_per_wg - 1) / rows_per_wg;
+    const int64_t grid = sq * groups;
+    if (grid > 0xffffffffll) return hipErrorInvalidValue;
+    int threads = (rows_per_wg * vpr + 63) / 64 * 64;
+    if (threads > 512) threads = 512;
+    hipLaunchKernelGGL(rope_apply_kernel, dim3((unsigned)grid), dim3(threads), 0, stream, X, rcos, rsin,
+                       table_rows, positions, nh, nope, pe, rows_per_wg, groups, direction, Out);
     return hipGetLastError();
 }
 

@@ -24,8 +24,13 @@ def P():
     return postmix
 
 
-@pytest.mark.parametrize("sq,nh,nope,pe,off", [(37, 64, 448, 64, 16384), (9, 4, 48, 16, 3),
-                                               (5, 3, 0, 32, 1000)])
+@pytest.mark.parametrize("sq,nh,nope,pe,off", [
+    (37, 64, 448, 64, 16384),   # the production row shape, 4 head rows per workgroup
+    (9, 4, 48, 16, 3),
+    (5, 3, 0, 32, 1000),        # no nope channels; fewer heads than rows per workgroup
+    (4, 7, 464, 16, 11),        # 60 vectors per row: 16 idle threads, a ragged head group
+    (3, 5, 2048, 64, 7),        # 264 vectors per row: one row per workgroup, looped
+])
 @pytest.mark.parametrize("direction", [-1, +1])
 def test_rope_apply_matches_oracle_rotation(sq, nh, nope, pe, off, direction):
     c = synthetic.case(sq, nh, nope, pe, seed=60 + sq, pos_offset=off)
