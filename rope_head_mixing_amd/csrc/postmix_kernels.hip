@@ -1276,31 +1276,45 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int32_t remap_one(int32_t v, int64_t batch, int64_t seqlen_kv, int32_t pad) {
-    return v >= 0 ? (int32_t)((int64_t)v + batch * seqlen_kv) : pad;
+// v + batch*seqlen_kv for v >= 0 (its low 32 bits, as the int64 sum cast to
+// int32), else the pad value; `off` = batch*seqlen_kv mod 2^32
+__device__ __forceinline__ int32_t remap_one(int32_t v, uint32_t off, int32_t pad) {
+    return v >= 0 ? (int32_t)((uint32_t)v + off) : pad;
+}
+
+// batch of element (or vector) i, with `per_batch` elements per batch: one
+// scalar division per workgroup when a batch spans at least a workgroup
+// (then a workgroup holds at most one batch boundary), else per element
+__device__ __forceinline__ int64_t batch_of(int64_t i, int64_t per_batch) {
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x;
+    if (per_batch >= (int64_t)blockDim.x) {
+        const int64_t b0 = i0 / per_batch;
+        return b0 + (i >= (b0 + 1) * per_batch ? 1 : 0);
+    }
+    return i / per_batch;
 }
 
 __global__ __launch_bounds__(256) void kv_remap_vec_kernel(const int32_t* __restrict__ idx,
-                                                           int64_t n_vec, int64_t vec_per_row,
-                                                           int64_t sq, int64_t seqlen_kv, int32_t pad,
+                                                           int64_t n_vec, int64_t vec_per_batch,
+                                                           int64_t seqlen_kv, int32_t pad,
                                                            int32_t* __restrict__ out) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n_vec) return;
-    const int64_t batch = (i / vec_per_row) / sq;
+    const uint32_t off = (uint32_t)(batch_of(i, vec_per_batch) * seqlen_kv);
     const i32x4 v = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(idx) + i);
     i32x4 o;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = remap_one(v[e], batch, seqlen_kv, pad);
+    for (int e = 0; e < 4; ++e) o[e] = remap_one(v[e], off, pad);
     __builtin_nontemporal_store(o, reinterpret_cast<i32x4*>(out) + i);
 }
 
 __global__ __launch_bounds__(256) void kv_remap_scalar_kernel(const int32_t* __restrict__ idx,
-                                                              int64_t n, int64_t topk, int64_t sq,
+                                                              int64_t n, int64_t per_batch,
                                                               int64_t seqlen_kv, int32_t pad,
                                                               int32_t* __restrict__ out) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
-    out[i] = remap_one(idx[i], (i / topk) / sq, seqlen_kv, pad);
+    out[i] = remap_one(idx[i], (uint32_t)(batch_of(i, per_batch) * seqlen_kv), pad);
 }
 
 hipError_t launch_kv_remap(const int32_t* idx, int64_t rows, int64_t sq, int64_t topk,
@@ -1311,10 +1325,10 @@ hipError_t launch_kv_remap(const int32_t* idx, int64_t rows, int64_t sq, int64_t
     if (vec) {
         const int64_t n_vec = n / 4;
         hipLaunchKernelGGL(kv_remap_vec_kernel, dim3((unsigned)((n_vec + 255) / 256)), dim3(256), 0, stream,
-                           idx, n_vec, topk / 4, sq, seqlen_kv, pad, out);
+                           idx, n_vec, (topk / 4) * sq, seqlen_kv, pad, out);
     } else {
         hipLaunchKernelGGL(kv_remap_scalar_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                           idx, n, topk, sq, seqlen_kv, pad, out);
+                           idx, n, topk * sq, seqlen_kv, pad, out);
     }
     return hipGetLastError();
 }

@@ -35,7 +35,9 @@ def table(b, sq, topk, seqlen_kv, seed, pad_frac=0.1):
     (3, 1024, 2176, 131072, -1),
     (4, 333, 640, 65536, 0),
     (3, 5, 7, 100, -9),          # topk % 4 != 0: scalar path
-    (2, 64, 130, 1 << 20, -1),   # ragged topk, large offsets
+    (2, 64, 130, 1 << 20, -1),   # ragged topk, large offsets; a batch boundary inside a workgroup
+    (6, 3, 8, 50, -1),           # batches shorter than a workgroup (vector path)
+    (5, 2, 100, 1000, -3),
 ])
 def test_kv_remap_matches_oracle_bitwise(b, sq, topk, seqlen_kv, pad_value):
     import torch
