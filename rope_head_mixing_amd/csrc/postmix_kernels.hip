@@ -580,9 +580,12 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // rows k0 .. k0+7 are split 4 + 4 over two transposing loads; the lane group
 // g = lane/16 takes columns 16*(g%2) .. +16 of the 32-column block and
 // k rows 8*(g/2) .. +8 of the 16-row k-block.
-__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* base, int pitch, int lane) {
+// tr_frag2: the same with the two 16-column halves taken from column bases
+// clo (lanes of groups 0, 2) and chi (groups 1, 3) of row-major `base`, so
+// MFMA rows 0..15 are columns clo.. and rows 16..31 columns chi..
+__device__ __forceinline__ bf16x8 tr_frag2(const uint16_t* base, int clo, int chi, int pitch, int lane) {
     const int g = lane >> 4, i = lane & 15;
-    const uint16_t* p = base + (8 * (g >> 1) + (i >> 2)) * pitch + 16 * (g & 1) + 4 * (i & 3);
+    const uint16_t* p = base + (8 * (g >> 1) + (i >> 2)) * pitch + ((g & 1) ? chi : clo) + 4 * (i & 3);
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * pitch));
@@ -592,6 +595,50 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* base, int pitch, int l
     v[2] = pack2((uint16_t)hi[0], (uint16_t)hi[1]);
     v[3] = pack2((uint16_t)hi[2], (uint16_t)hi[3]);
     return as_bf16x8(v);
+}
+
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* base, int pitch, int lane) {
+    return tr_frag2(base, 0, 16, pitch, lane);
+}
+
+// Paired pe blocks.  When pe % 32 == 0 and nope % 32 == 0 the pe channels of
+// a tile form pe/32 MFMA M-blocks whose 32 rows are 16 first-half channels
+// (nope + 16q ..) and their 16 rotation partners (nope + pe/2 + 16q ..).  In
+// the 32x32 accumulator layout a lane then holds each partner pair in
+// registers r and r + 8 (rows 8(r/4) + 4Q + r%4 and that + 16), so the
+// rotation happens in registers and the results are rounded to bf16 at once:
+// no fp32 scratch, and the store phase is one plain copy for every vector.
+__host__ __device__ __forceinline__ bool pe_pairs_in_blocks(int nope, int pe) {
+    return pe > 0 && pe % 32 == 0 && nope % 32 == 0;
+}
+
+// Rotate a paired block's accumulators and write both halves (bf16) into
+// row-major `out` (pitch in elements) at local pe offset L (first pe channel):
+// first half  i: y = x_i C + sg (x_{i+h2} S),  second half: y = x_{i+h2} C - sg (x_i S),
+// sg = +1 for the inverse rotation (-phi), -1 for the rotation by +phi.
+__device__ __forceinline__ void rotate_paired_block(const f32x16& acc, uint16_t* out, int pitch, int row,
+                                                    int L, int h2, int q, int Q, const float* csl,
+                                                    const float* snl, float sg) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int i = 16 * q + 8 * a + 4 * Q;  // 4 consecutive indices within a half
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(csl + i);
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(snl + i);
+        float y1[4], y2[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x1 = acc[4 * a + e], x2 = acc[4 * a + 8 + e];
+            y1[e] = x1 * c4[e] + sg * (x2 * s4[e]);
+            y2[e] = x2 * c4[e] + (-sg) * (x1 * s4[e]);
+        }
+        uint2 o1, o2;
+        o1.x = pack2(f32_to_bf16_rne(y1[0]), f32_to_bf16_rne(y1[1]));
+        o1.y = pack2(f32_to_bf16_rne(y1[2]), f32_to_bf16_rne(y1[3]));
+        o2.x = pack2(f32_to_bf16_rne(y2[0]), f32_to_bf16_rne(y2[1]));
+        o2.y = pack2(f32_to_bf16_rne(y2[2]), f32_to_bf16_rne(y2[3]));
+        *reinterpret_cast<uint2*>(out + row * pitch + L + i) = o1;
+        *reinterpret_cast<uint2*>(out + row * pitch + L + h2 + i) = o2;
+    }
 }
 
 template <int NH, int CP, int WAVES, bool DX>
@@ -673,6 +720,8 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
         const bool tile_pe = pe > 0 && c_base + CP > nope;
         if (tile_pe && tid < (pe >> 2)) reinterpret_cast<f32x4*>(csl)[tid] = rope_v;  // cos then sin
         __syncthreads();
+        const bool paired = tile_pe && pe_pairs_in_blocks(nope, pe);
+        const int L = nope - c_base;  // local index of the first pe channel (tiles with pe)
 
         for (int b = wave; b < C::MBP; b += WAVES) {
             f32x16 acc[C::NB];
@@ -680,15 +729,25 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
             for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[nb][r] = 0.0f;
+            const bool pb = paired && 32 * b >= L;  // a paired pe block (wave-uniform)
+            const int q = b - (L >> 5);
+            const int clo = pb ? L + 16 * q : 32 * b, chi = pb ? L + h2 + 16 * q : 32 * b + 16;
             bf16x8 af[C::KB];
 #pragma unroll
             for (int kb = 0; kb < C::KB; ++kb)
-                af[kb] = tr_frag(tile + (16 * kb) * C::PITCH + 32 * b, C::PITCH, lane);
+                af[kb] = tr_frag2(tile + (16 * kb) * C::PITCH, clo, chi, C::PITCH, lane);
 #pragma unroll
             for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
                 for (int nb = 0; nb < C::NB; ++nb)
                     acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], wf[kb][nb], acc[nb], 0, 0, 0);
+            if (pb) {
+#pragma unroll
+                for (int nb = 0; nb < C::NB; ++nb)
+                    rotate_paired_block(acc[nb], tile, C::PITCH, 32 * nb + (lane & 31), L, h2, q, Q, csl, snl,
+                                        DX ? -1.0f : 1.0f);
+                continue;
+            }
             // D register r of lane half Q: channel 32b + 8(r/4) + 4Q + r%4, head 32nb + lane%32
 #pragma unroll
             for (int nb = 0; nb < C::NB; ++nb) {
@@ -719,7 +778,7 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
             const int row = q / C::VPR, c8 = q % C::VPR;
             const int cl = 8 * c8, cg = c_base + cl;
             u32x4 o;
-            if (cg < nope) {
+            if (cg < nope || paired) {
                 o = *reinterpret_cast<const u32x4*>(tile + row * C::PITCH + cl);
             } else {
                 const int i = cg - nope;
@@ -1173,20 +1232,26 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         }
 
         // ---- input gradient: M-block mb (channels), N-block nb (heads)
+        const bool paired = chunk_pe && pe_pairs_in_blocks(nope, pe);
+        const int L = nope - c_base;  // local index of the first pe channel (chunks with pe)
         {
             f32x16 acc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+            const bool pb = paired && 32 * mb >= L;  // a paired pe block (wave-uniform)
+            const int q = mb - (L >> 5);
+            const int clo = pb ? L + 16 * q : 32 * mb, chi = pb ? L + h2 + 16 * q : 32 * mb + 16;
             bf16x8 af[C::KB];
 #pragma unroll
             for (int kb = 0; kb < C::KB; ++kb)
-                af[kb] = tr_frag(dyl + (16 * kb) * C::PITCH + 32 * mb, C::PITCH, lane);
+                af[kb] = tr_frag2(dyl + (16 * kb) * C::PITCH, clo, chi, C::PITCH, lane);
 #pragma unroll
             for (int kb = 0; kb < C::KB; ++kb)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], wf[kb], acc, 0, 0, 0);
             const int hrow = 32 * nb + (lane & 31);
+            if (pb) rotate_paired_block(acc, dol, C::PITCH, hrow, L, h2, q, Q, csl, snl, -1.0f);
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
+            for (int a = 0; a < 4 && !pb; ++a) {
                 const int cl = 32 * mb + 8 * a + 4 * Q;
                 const int cg = c_base + cl;
                 if (cg < nope) {
@@ -1214,7 +1279,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             const int row = q / C::VPR, c8 = q % C::VPR;
             const int cl = 8 * c8, cg = c_base + cl;
             u32x4 o;
-            if (cg < nope) {
+            if (cg < nope || paired) {
                 o = *reinterpret_cast<const u32x4*>(dol + row * C::PITCH + cl);
             } else {
                 const int i = cg - nope;
