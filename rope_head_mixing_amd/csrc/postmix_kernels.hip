@@ -882,6 +882,11 @@ __global__ __launch_bounds__(256) void dw_chunk_kernel(
         const int64_t s = s_begin + k / cpt;
         const int part = k % cpt;
         const int64_t rowbase = s * NH * (int64_t)d + part * CH;
+        if (pe > 0 && (part + 1) * CH > nope && tid < (h2 >> 2)) {  // before the chunk loads
+            const int64_t prow = table_row(positions, s, table_rows);
+            cv = reinterpret_cast<const f32x4*>(rcos + prow * h2)[tid];
+            sv = reinterpret_cast<const f32x4*>(rsin + prow * h2)[tid];
+        }
 #pragma unroll
         for (int j = 0; j < C::VPT; ++j) {
             const int q = j * C::NT + tid;
@@ -890,11 +895,6 @@ __global__ __launch_bounds__(256) void dw_chunk_kernel(
             const int row = rem / C::VPR, c8 = rem % C::VPR;
             const uint16_t* src = (op == 0 ? dY : O) + rowbase + row * (int64_t)d + 8 * c8;
             v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-        }
-        if (pe > 0 && (part + 1) * CH > nope && tid < (h2 >> 2)) {
-            const int64_t prow = table_row(positions, s, table_rows);
-            cv = reinterpret_cast<const f32x4*>(rcos + prow * h2)[tid];
-            sv = reinterpret_cast<const f32x4*>(rsin + prow * h2)[tid];
         }
     };
 
@@ -1129,6 +1129,12 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         const int64_t s = s_begin + k / cpt;
         const int part = k % cpt;
         const int64_t rowbase = s * NH * (int64_t)d + part * CH;
+        // the cos/sin load first: whatever it waits on (the position, a
+        // reloaded register) then does not wait for the chunk loads behind it
+        if (pe > 0 && (part + 1) * CH > nope && rope_lane) {
+            const int64_t prow = table_row(positions, s, table_rows);
+            rope_v = reinterpret_cast<const f32x4*>(rtab + prow * h2)[lane];
+        }
 #pragma unroll
         for (int j = 0; j < C::VPT; ++j) {
             const int q = j * C::NT + tid;
@@ -1137,10 +1143,6 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             const int row = rem / C::VPR, c8 = rem % C::VPR;
             const uint16_t* src = (op == 0 ? dY : O) + rowbase + row * (int64_t)d + 8 * c8;
             v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-        }
-        if (pe > 0 && (part + 1) * CH > nope && rope_lane) {
-            const int64_t prow = table_row(positions, s, table_rows);
-            rope_v = reinterpret_cast<const f32x4*>(rtab + prow * h2)[lane];
         }
     };
     auto stage_chunk = [&](int k) {  // registers of chunk k -> LDS
