@@ -14,7 +14,6 @@
 // The products are summed over k, so which 8 k-values sit in which lane half
 // only has to agree between A and B; the kernels assign k freely.
 #include <hip/hip_runtime.h>
-#include <type_traits>
 #include <stdint.h>
 
 #include "postmix_launch.h"
@@ -1079,10 +1078,7 @@ struct BwdCfg {
     static constexpr int MBC = CH / 32;             // M-blocks of the head mix per chunk
     static constexpr int NTILE = NB * NB;           // dW output tiles
     static constexpr int KSET = WAVES / NTILE;      // waves per dW tile
-    static constexpr int WPN = WAVES / NB;          // waves per dx N-block
-    static constexpr int UPW = MBC * NB / WAVES;    // dx units (M-block, N-block) per wave
-    static_assert(NH == 64 && (MBC * NB) % WAVES == 0 && WAVES % NB == 0 && KS % KSET == 0 &&
-                  VPO % NT == 0, "fused shape");
+    static_assert(NH == 64 && MBC * NB == WAVES && KS % KSET == 0 && VPO % NT == 0, "fused shape");
     __host__ __device__ static size_t aux_bytes(int pe) {
         const size_t w = (size_t)NH * WPITCH * 2, p = (size_t)NH * (pe + 4) * 4;
         return w > p ? w : p;
@@ -1093,14 +1089,13 @@ struct BwdCfg {
     }
 };
 
-template <int NH, int CH, int WAVES, int PD, int MINW>
-__global__ __launch_bounds__(64 * WAVES, MINW) void bwd_fused_kernel(
+template <int NH, int CH, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O, const uint16_t* __restrict__ W,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
     const int32_t* __restrict__ positions, int64_t sq, int nope, int pe,
     uint16_t* __restrict__ dO, float* __restrict__ partials, int tokens_per_block) {
     using C = BwdCfg<NH, CH, WAVES>;
-    static_assert(PD == 1 || PD == 2, "one or two chunks in flight");
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint16_t* dyl = smem;                               // [NH][PITCH]
     uint16_t* ol = dyl + NH * C::PITCH;                 // [NH][PITCH]
@@ -1121,18 +1116,16 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void bwd_fused_kernel(
     const float* const rtab = __builtin_amdgcn_readfirstlane(tid >> 6) == 0 ? rcos : rsin;
     const int tile = wave % C::NTILE, kset = wave / C::NTILE;
     const int gb = tile / C::NB, hb = tile % C::NB;
-    const int nb = wave / C::WPN, mb0 = wave % C::WPN;  // dx M-blocks mb0 + u*WPN, u < UPW
+    const int mb = wave % C::MBC, nb = wave / C::MBC;
 
     const int64_t s_begin = (int64_t)blockIdx.x * tokens_per_block;
     int64_t s_end = s_begin + tokens_per_block;
     if (s_end > sq) s_end = sq;
     const int nchunks = (int)(s_end - s_begin) * cpt;
 
-    // PD register sets: chunk k travels in set k % PD
-    u32x4 v[PD][C::VPT];
-    f32x4 rope_v[PD];
-    auto load_chunk = [&](auto S, int k) {
-        constexpr int set = decltype(S)::value;
+    u32x4 v[C::VPT];
+    f32x4 rope_v = {0.f, 0.f, 0.f, 0.f};
+    auto load_chunk = [&](int k) {
         const int64_t s = s_begin + k / cpt;
         const int part = k % cpt;
         const int64_t rowbase = s * NH * (int64_t)d + part * CH;
@@ -1140,7 +1133,7 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void bwd_fused_kernel(
         // reloaded register) then does not wait for the chunk loads behind it
         if (pe > 0 && (part + 1) * CH > nope && rope_lane) {
             const int64_t prow = table_row(positions, s, table_rows);
-            rope_v[set] = reinterpret_cast<const f32x4*>(rtab + prow * h2)[lane];
+            rope_v = reinterpret_cast<const f32x4*>(rtab + prow * h2)[lane];
         }
 #pragma unroll
         for (int j = 0; j < C::VPT; ++j) {
@@ -1149,11 +1142,10 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void bwd_fused_kernel(
             const int rem = q % C::VPO;
             const int row = rem / C::VPR, c8 = rem % C::VPR;
             const uint16_t* src = (op == 0 ? dY : O) + rowbase + row * (int64_t)d + 8 * c8;
-            v[set][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+            v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
         }
     };
-    auto stage_chunk = [&](auto S, int k) {  // registers of chunk k -> LDS
-        constexpr int set = decltype(S)::value;
+    auto stage_chunk = [&](int k) {  // registers of chunk k -> LDS
         const int part = k % cpt;
 #pragma unroll
         for (int j = 0; j < C::VPT; ++j) {
@@ -1161,14 +1153,12 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void bwd_fused_kernel(
             const int op = q / C::VPO;
             const int rem = q % C::VPO;
             const int row = rem / C::VPR, c8 = rem % C::VPR;
-            *reinterpret_cast<u32x4*>((op == 0 ? dyl : ol) + row * C::PITCH + 8 * c8) = v[set][j];
+            *reinterpret_cast<u32x4*>((op == 0 ? dyl : ol) + row * C::PITCH + 8 * c8) = v[j];
         }
         if (pe > 0 && (part + 1) * CH > nope && rope_lane)
-            reinterpret_cast<f32x4*>(rope_l + (k & 1) * pe)[wave * (pe >> 3) + lane] = rope_v[set];
+            reinterpret_cast<f32x4*>(rope_l + (k & 1) * pe)[wave * (pe >> 3) + lane] = rope_v;
     };
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1 % PD>;
-    if (nchunks > 0) load_chunk(S0{}, 0);
+    if (nchunks > 0) load_chunk(0);
 
     // W -> LDS -> this wave's dx B operand (B[k=g][n=h] = W[g][h], N-block nb)
     for (int q = tid; q < NH * NH / 8; q += C::NT) {
@@ -1187,17 +1177,14 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void bwd_fused_kernel(
 
     // Pipeline: chunk k is computed from the dY/O buffers; once every wave is
     // done with them (barrier), chunk k+1 (already in registers) is staged
-    // there and chunk k+1+PD is requested into the freed registers, and only
-    // then are chunk k's dO rows stored (they live in separate buffers).  Two
-    // barriers per chunk; PD chunks are in flight during each compute phase.
+    // there and chunk k+2 is requested, and only then are chunk k's dO rows
+    // stored (they live in separate buffers).  Two barriers per chunk.
     if (nchunks > 0) {
-        stage_chunk(S0{}, 0);
-        if (nchunks > 1) load_chunk(S1{}, 1);
-        if (PD > 1 && nchunks > 2) load_chunk(S0{}, 2);
+        stage_chunk(0);
+        if (nchunks > 1) load_chunk(1);
     }
     __syncthreads();
-    // one chunk; S = the register set of chunk k+1 (and of k+1+PD)
-    auto iteration = [&](auto S, int k) {
+    for (int k = 0; k < nchunks; ++k) {
         const int64_t s = s_begin + k / cpt;
         const int part = k % cpt;
         const int c_base = part * CH;
@@ -1246,12 +1233,10 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void bwd_fused_kernel(
             }
         }
 
-        // ---- input gradient: M-blocks mb0 + u*WPN (channels), N-block nb (heads)
+        // ---- input gradient: M-block mb (channels), N-block nb (heads)
         const bool paired = chunk_pe && pe_pairs_in_blocks(nope, pe);
         const int L = nope - c_base;  // local index of the first pe channel (chunks with pe)
-#pragma unroll
-        for (int u = 0; u < C::UPW; ++u) {
-            const int mb = mb0 + u * C::WPN;
+        {
             f32x16 acc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
@@ -1284,8 +1269,8 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void bwd_fused_kernel(
         }
         __syncthreads();  // dY/O buffers free; dO and the pe scratch complete
         if (k + 1 < nchunks) {
-            stage_chunk(S, k + 1);
-            if (k + 1 + PD < nchunks) load_chunk(S, k + 1 + PD);  // in flight during PD+1 compute phases
+            stage_chunk(k + 1);
+            if (k + 2 < nchunks) load_chunk(k + 2);  // in flight during two compute phases
         }
 
         // ---- dO rows of the chunk; pe pairs turned by +phi
@@ -1324,10 +1309,6 @@ __global__ __launch_bounds__(64 * WAVES, MINW) void bwd_fused_kernel(
             __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(outs + row * (int64_t)d + cl));
         }
         __syncthreads();  // dO buffers read; chunk k+1 staged
-    };
-    for (int k = 0; k < nchunks; k += PD) {
-        iteration(S1{}, k);
-        if (PD > 1 && k + 1 < nchunks) iteration(S0{}, k + 1);
     }
 
     // ---- dW partial: the k-sets of each tile summed in k-set order (fixed)
@@ -1653,10 +1634,10 @@ bool bwd_fused_applies(int nh, int nope, int pe) {
 // chunk width of the fused backward: 256 channels (16 waves) where d allows
 static int bwd_fused_chunk(int d) { return d % 256 == 0 ? 256 : 128; }
 
-template <int CH, int WAVES, int PD, int MINW>
+template <int CH, int WAVES>
 static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int tpb, int64_t nb, hipStream_t stream) {
     using C = BwdCfg<64, CH, WAVES>;
-    auto kern = bwd_fused_kernel<64, CH, WAVES, PD, MINW>;
+    auto kern = bwd_fused_kernel<64, CH, WAVES>;
     static bool attr_done = false;  // idempotent; a race only repeats the call
     if (!attr_done) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1672,9 +1653,8 @@ static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int tpb
 hipError_t launch_bwd_fused(const MixArgs& mx, const DwArgs& a, hipStream_t stream) {
     const int tpb = bwd_fused_tokens_per_block(a.sq, a.nh);
     const int64_t nb = bwd_fused_num_blocks(a.sq, a.nh);
-    hipError_t err = bwd_fused_chunk(a.nope + a.pe) == 256
-                         ? launch_bwd_fused_t<256, 16, 1, 4>(mx, a, tpb, nb, stream)
-                         : launch_bwd_fused_t<128, 8, 1, 4>(mx, a, tpb, nb, stream);
+    hipError_t err = bwd_fused_chunk(a.nope + a.pe) == 256 ? launch_bwd_fused_t<256, 16>(mx, a, tpb, nb, stream)
+                                                          : launch_bwd_fused_t<128, 8>(mx, a, tpb, nb, stream);
     if (err != hipSuccess) return err;
     const int64_t ne = (int64_t)a.nh * a.nh;
     hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((ne + 63) / 64)), dim3(1024), 0, stream,
