@@ -139,6 +139,9 @@ def kernel_policy(request):
     (13, 64, 432, 80, 4000),   # nope not a multiple of 32: an M-block straddles nope
     (6, 128, 192, 64, 17),     # nh = 128 with two 128-channel parts
     (3, 64, 0, 256, 100),      # every channel rotated, pe = one whole part
+    (11, 64, 480, 32, 5),      # pe = 32: one paired pe block (partners 16 apart)
+    (9, 64, 416, 96, 11),      # pe = 96: three paired pe blocks
+    (8, 64, 464, 48, 21),      # nope % 32 != 0: pe rotated through the fp32 scratch
 ])
 def test_small_shapes(sq, nh, nope, pe, off, kernel_policy):
     full_check(synthetic.case(sq, nh, nope, pe, seed=1000 + sq + nh, pos_offset=off))
@@ -174,6 +177,9 @@ def test_tiled_and_general_kernels_agree(sq, nh, nope, pe):
     (33, 64, 192, 64, 7),       # fused path, d = 256
     (70, 64, 384, 128, 3),      # fused path, pe = 128 (one whole chunk rotated)
     (19, 64, 432, 80, 99),      # fused path, nope straddles an M-block
+    (13, 64, 480, 32, 7),       # fused path, pe = 32 (one paired pe block)
+    (9, 64, 416, 96, 11),       # fused path, pe = 96 (three paired pe blocks)
+    (11, 64, 496, 16, 5),       # fused path, pe = 16 (fp32 scratch)
     (21, 32, 448, 64, 5),       # not fused (nh = 32): separate kernels
     (9, 3, 448, 64, 0),         # not fused (nh = 3)
 ])
