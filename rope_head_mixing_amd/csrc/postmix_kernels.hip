@@ -33,16 +33,44 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-// fp32 -> bf16, round to nearest even (finite inputs; NaN kept quiet).
+// fp32 -> bf16, round to nearest even.  gfx950 converts in hardware
+// (v_cvt_pk_bf16_f32); for every finite float its result equals the bit-level
+// definition u += 0x7fff + ((u >> 16) & 1), u >> 16 (checked exhaustively on
+// the device over all 2^32 bit patterns).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// two floats rounded to bf16 and packed, a in the low half (one instruction)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) {
     return (lo16 & 0xffffu) | (hi16 << 16);
+}
+
+// Weight-gradient pe operand of 8 channels: x_k = a_k C_k + b_k S_k (own
+// value a, rotation partner b, S already signed), split into the bf16 pair
+// hi = RNE(x), lo = RNE(x - hi) of the compensated product.
+__device__ __forceinline__ void rotate_split8(const uint32_t* own, const uint32_t* par, const float* cs,
+                                              const float* sn, uint32_t* hi, uint32_t* lo) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        float x[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int k = 2 * jj + e;
+            const float xa = __uint_as_float(e ? (own[jj] & 0xffff0000u) : (own[jj] << 16));
+            const float xb = __uint_as_float(e ? (par[jj] & 0xffff0000u) : (par[jj] << 16));
+            x[e] = xa * cs[k] + xb * sn[k];
+        }
+        const uint32_t h = pack_bf16(x[0], x[1]);
+        hi[jj] = h;
+        lo[jj] = pack_bf16(x[0] - __uint_as_float(h << 16), x[1] - __uint_as_float(h & 0xffff0000u));
+    }
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
@@ -256,14 +284,14 @@ __global__ __launch_bounds__(64) void mix_kernel(
                         u32x4 v;
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj)
-                            v[jj] = pack2(f32_to_bf16_rne(y[2 * jj]), f32_to_bf16_rne(y[2 * jj + 1]));
+                            v[jj] = pack_bf16(y[2 * jj], y[2 * jj + 1]);
                         *reinterpret_cast<u32x4*>(orow + c0) = v;
                     }
                     if (c1 >= 0) {
                         u32x4 v;
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj)
-                            v[jj] = pack2(f32_to_bf16_rne(y[8 + 2 * jj]), f32_to_bf16_rne(y[9 + 2 * jj]));
+                            v[jj] = pack_bf16(y[8 + 2 * jj], y[9 + 2 * jj]);
                         *reinterpret_cast<u32x4*>(orow + c1) = v;
                     }
                 }
@@ -385,24 +413,13 @@ __global__ __launch_bounds__(256) void dw_partial_kernel(
                         if (pe_grp) part = *reinterpret_cast<const u32x4*>(os + h * d + cpart);
                     }
                     u32x4 hi = own, lo = {0u, 0u, 0u, 0u};
-                    if (pe_grp) {
+                    if (pe_grp) {  // first half: a C + b S; second half: a C - b S
+                        uint32_t ow[4], pw[4], hw[4], lw[4];
 #pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-                            uint32_t hw[2], lw[2];
+                        for (int jj = 0; jj < 4; ++jj) { ow[jj] = own[jj]; pw[jj] = part[jj]; }
+                        rotate_split8(ow, pw, cs, sn, hw, lw);
 #pragma unroll
-                            for (int e = 0; e < 2; ++e) {
-                                const int k = 2 * jj + e;
-                                const float xa = bf16_to_f32((own[jj] >> (16 * e)) & 0xffffu);
-                                const float xb = bf16_to_f32((part[jj] >> (16 * e)) & 0xffffu);
-                                // first half: a C + b S; second half: a C - b S
-                                const float x = xa * cs[k] + xb * sn[k];
-                                const uint32_t xh = f32_to_bf16_rne(x);
-                                hw[e] = xh;
-                                lw[e] = f32_to_bf16_rne(x - bf16_to_f32(xh));
-                            }
-                            hi[jj] = pack2(hw[0], hw[1]);
-                            lo[jj] = pack2(lw[0], lw[1]);
-                        }
+                        for (int jj = 0; jj < 4; ++jj) { hi[jj] = hw[jj]; lo[jj] = lw[jj]; }
                     }
                     const bf16x8 bh = as_bf16x8(hi), bl = as_bf16x8(lo);
 #pragma unroll
@@ -632,10 +649,10 @@ __device__ __forceinline__ void rotate_paired_block(const f32x16& acc, uint16_t*
             y2[e] = x2 * c4[e] + (-sg) * (x1 * s4[e]);
         }
         uint2 o1, o2;
-        o1.x = pack2(f32_to_bf16_rne(y1[0]), f32_to_bf16_rne(y1[1]));
-        o1.y = pack2(f32_to_bf16_rne(y1[2]), f32_to_bf16_rne(y1[3]));
-        o2.x = pack2(f32_to_bf16_rne(y2[0]), f32_to_bf16_rne(y2[1]));
-        o2.y = pack2(f32_to_bf16_rne(y2[2]), f32_to_bf16_rne(y2[3]));
+        o1.x = pack_bf16(y1[0], y1[1]);
+        o1.y = pack_bf16(y1[2], y1[3]);
+        o2.x = pack_bf16(y2[0], y2[1]);
+        o2.y = pack_bf16(y2[2], y2[3]);
         *reinterpret_cast<uint2*>(out + row * pitch + L + i) = o1;
         *reinterpret_cast<uint2*>(out + row * pitch + L + h2 + i) = o2;
     }
@@ -758,8 +775,8 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
                     const int cg = c_base + cl;
                     if (cg < nope) {
                         uint2 o;
-                        o.x = pack2(f32_to_bf16_rne(acc[nb][4 * a]), f32_to_bf16_rne(acc[nb][4 * a + 1]));
-                        o.y = pack2(f32_to_bf16_rne(acc[nb][4 * a + 2]), f32_to_bf16_rne(acc[nb][4 * a + 3]));
+                        o.x = pack_bf16(acc[nb][4 * a], acc[nb][4 * a + 1]);
+                        o.y = pack_bf16(acc[nb][4 * a + 2], acc[nb][4 * a + 3]);
                         *reinterpret_cast<uint2*>(tile + g * C::PITCH + cl) = o;
                     } else {
                         f32x4 o = {acc[nb][4 * a], acc[nb][4 * a + 1], acc[nb][4 * a + 2], acc[nb][4 * a + 3]};
@@ -802,7 +819,7 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
                     y[4 + e] = o1[e] * c1[e] + sg * (p1[e] * s1[e]);
                 }
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) o[jj] = pack2(f32_to_bf16_rne(y[2 * jj]), f32_to_bf16_rne(y[2 * jj + 1]));
+                for (int jj = 0; jj < 4; ++jj) o[jj] = pack_bf16(y[2 * jj], y[2 * jj + 1]);
             }
             __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(outs + row * (int64_t)d + cl));
         }
@@ -957,22 +974,12 @@ __global__ __launch_bounds__(256) void dw_chunk_kernel(
                     u32x4 hi = own, lo = {0u, 0u, 0u, 0u};
                     if (pe_grp) {
                         const u32x4 par = *reinterpret_cast<const u32x4*>(ol + h * C::PITCH + cpart);
+                        uint32_t ow[4], pw[4], hw[4], lw[4];
 #pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-                            uint32_t hw[2], lw[2];
+                        for (int jj = 0; jj < 4; ++jj) { ow[jj] = own[jj]; pw[jj] = par[jj]; }
+                        rotate_split8(ow, pw, cs, sn, hw, lw);
 #pragma unroll
-                            for (int e = 0; e < 2; ++e) {
-                                const int kx = 2 * jj + e;
-                                const float xa = bf16_to_f32((own[jj] >> (16 * e)) & 0xffffu);
-                                const float xb = bf16_to_f32((par[jj] >> (16 * e)) & 0xffffu);
-                                const float x = xa * cs[kx] + xb * sn[kx];
-                                const uint32_t xh = f32_to_bf16_rne(x);
-                                hw[e] = xh;
-                                lw[e] = f32_to_bf16_rne(x - bf16_to_f32(xh));
-                            }
-                            hi[jj] = pack2(hw[0], hw[1]);
-                            lo[jj] = pack2(lw[0], lw[1]);
-                        }
+                        for (int jj = 0; jj < 4; ++jj) { hi[jj] = hw[jj]; lo[jj] = lw[jj]; }
                     }
                     const bf16x8 bh = as_bf16x8(hi), bl = as_bf16x8(lo);
 #pragma unroll
@@ -1083,9 +1090,11 @@ struct BwdCfg {
         const size_t w = (size_t)NH * WPITCH * 2, p = (size_t)NH * (pe + 4) * 4;
         return w > p ? w : p;
     }
-    // dY chunk, O chunk, dO chunk, then W / pe scratch, then cos and sin of two chunks
+    static constexpr int RG = 16;                   // tokens per group of staged cos/sin rows
+    // dY chunk, O chunk, dO chunk, then W / pe scratch, then the cos and sin
+    // rows of RG tokens
     __host__ __device__ static size_t lds_bytes(int pe) {
-        return (size_t)3 * NH * PITCH * 2 + aux_bytes(pe) + (size_t)pe * 8;
+        return (size_t)3 * NH * PITCH * 2 + aux_bytes(pe) + (size_t)RG * pe * 4;
     }
 };
 
@@ -1103,17 +1112,13 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     uint16_t* wl = dol + NH * C::PITCH;                 // [NH][WPITCH] bf16, then:
     float* pes = reinterpret_cast<float*>(wl);          // [NH][pe + 4] fp32
     const int pes_pitch = pe + 4;
-    // cos/sin rows of two consecutive chunks: [2][pe] floats (cos then sin each)
-    float* const rope_l = reinterpret_cast<float*>(reinterpret_cast<char*>(wl) + C::aux_bytes(pe));
+    // cos/sin rows of RG consecutive tokens: [RG][pe] floats (cos then sin each)
+    float* const rope_g = reinterpret_cast<float*>(reinterpret_cast<char*>(wl) + C::aux_bytes(pe));
 
     const int d = nope + pe, h2 = pe >> 1;
     const int cpt = d / CH;
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, Q = half;
     const int wave = tid >> 6;
-    // the cos row of a pe chunk is fetched by lanes < pe/8 of wave 0, the sin
-    // row by those of wave 1 (a wave-uniform table pointer)
-    const bool rope_lane = wave < 2 && lane < (pe >> 3);
-    const float* const rtab = __builtin_amdgcn_readfirstlane(tid >> 6) == 0 ? rcos : rsin;
     const int tile = wave % C::NTILE, kset = wave / C::NTILE;
     const int gb = tile / C::NB, hb = tile % C::NB;
     const int mb = wave % C::MBC, nb = wave / C::MBC;
@@ -1124,17 +1129,24 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     const int nchunks = (int)(s_end - s_begin) * cpt;
 
     u32x4 v[C::VPT];
-    f32x4 rope_v = {0.f, 0.f, 0.f, 0.f};
+    // cos and sin rows of tokens s0 .. s0+RG-1 (within the block) -> LDS;
+    // read once per RG tokens instead of once per chunk
+    auto load_rope_group = [&](int64_t s0) {
+        int64_t n = s_end - s0;
+        if (n > C::RG) n = C::RG;
+        const int q4 = pe >> 2, half4 = pe >> 3;  // f32x4 per token row (cos + sin), per table row
+        for (int idx = tid; idx < (int)n * q4; idx += C::NT) {
+            const int t = idx / q4, q = idx - t * q4;
+            const int64_t prow = table_row(positions, s0 + t, table_rows);
+            const float* tab = q < half4 ? rcos : rsin;
+            const int qq = q < half4 ? q : q - half4;
+            reinterpret_cast<f32x4*>(rope_g + t * pe)[q] = reinterpret_cast<const f32x4*>(tab + prow * h2)[qq];
+        }
+    };
     auto load_chunk = [&](int k) {
         const int64_t s = s_begin + k / cpt;
         const int part = k % cpt;
         const int64_t rowbase = s * NH * (int64_t)d + part * CH;
-        // the cos/sin load first: whatever it waits on (the position, a
-        // reloaded register) then does not wait for the chunk loads behind it
-        if (pe > 0 && (part + 1) * CH > nope && rope_lane) {
-            const int64_t prow = table_row(positions, s, table_rows);
-            rope_v = reinterpret_cast<const f32x4*>(rtab + prow * h2)[lane];
-        }
 #pragma unroll
         for (int j = 0; j < C::VPT; ++j) {
             const int q = j * C::NT + tid;
@@ -1145,8 +1157,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
         }
     };
-    auto stage_chunk = [&](int k) {  // registers of chunk k -> LDS
-        const int part = k % cpt;
+    auto stage_chunk = [&]() {  // registers of the next chunk -> LDS
 #pragma unroll
         for (int j = 0; j < C::VPT; ++j) {
             const int q = j * C::NT + tid;
@@ -1155,10 +1166,9 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             const int row = rem / C::VPR, c8 = rem % C::VPR;
             *reinterpret_cast<u32x4*>((op == 0 ? dyl : ol) + row * C::PITCH + 8 * c8) = v[j];
         }
-        if (pe > 0 && (part + 1) * CH > nope && rope_lane)
-            reinterpret_cast<f32x4*>(rope_l + (k & 1) * pe)[wave * (pe >> 3) + lane] = rope_v;
     };
     if (nchunks > 0) load_chunk(0);
+    if (pe > 0 && nchunks > 0) load_rope_group(s_begin);
 
     // W -> LDS -> this wave's dx B operand (B[k=g][n=h] = W[g][h], N-block nb)
     for (int q = tid; q < NH * NH / 8; q += C::NT) {
@@ -1180,7 +1190,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     // there and chunk k+2 is requested, and only then are chunk k's dO rows
     // stored (they live in separate buffers).  Two barriers per chunk.
     if (nchunks > 0) {
-        stage_chunk(0);
+        stage_chunk();
         if (nchunks > 1) load_chunk(1);
     }
     __syncthreads();
@@ -1189,7 +1199,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         const int part = k % cpt;
         const int c_base = part * CH;
         const bool chunk_pe = pe > 0 && c_base + CH > nope;
-        const float* csl = rope_l + (k & 1) * pe;
+        const float* csl = rope_g + ((k / cpt) % C::RG) * pe;
         const float* snl = csl + (pe >> 1);
 
         // ---- weight gradient: tile (gb, hb), k-steps t = kset, kset + 2, ...
@@ -1211,22 +1221,19 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
                     const int i0 = first ? cg - nope : cg - nope - h2;
                     const float sgn = first ? 1.0f : -1.0f;
                     const u32x4 par = *reinterpret_cast<const u32x4*>(ol + h * C::PITCH + (first ? c + h2 : c - h2));
+                    const f32x4 c0 = *reinterpret_cast<const f32x4*>(csl + i0), c1 = *reinterpret_cast<const f32x4*>(csl + i0 + 4);
+                    const f32x4 s0 = *reinterpret_cast<const f32x4*>(snl + i0), s1 = *reinterpret_cast<const f32x4*>(snl + i0 + 4);
+                    float cs[8], sn[8];
+                    uint32_t ow[4], pw[4], hw[4], lw[4];
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        uint32_t hw[2], lw[2];
-#pragma unroll
-                        for (int e = 0; e < 2; ++e) {
-                            const int kx = 2 * jj + e;
-                            const float xa = bf16_to_f32((own[jj] >> (16 * e)) & 0xffffu);
-                            const float xb = bf16_to_f32((par[jj] >> (16 * e)) & 0xffffu);
-                            const float x = xa * csl[i0 + kx] + xb * (sgn * snl[i0 + kx]);
-                            const uint32_t xh = f32_to_bf16_rne(x);
-                            hw[e] = xh;
-                            lw[e] = f32_to_bf16_rne(x - bf16_to_f32(xh));
-                        }
-                        hi[jj] = pack2(hw[0], hw[1]);
-                        lo[jj] = pack2(lw[0], lw[1]);
+                    for (int e = 0; e < 4; ++e) {
+                        cs[e] = c0[e]; cs[4 + e] = c1[e];
+                        sn[e] = sgn * s0[e]; sn[4 + e] = sgn * s1[e];
+                        ow[e] = own[e]; pw[e] = par[e];
                     }
+                    rotate_split8(ow, pw, cs, sn, hw, lw);
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) { hi[jj] = hw[jj]; lo[jj] = lw[jj]; }
                 }
                 acc_w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(hi), acc_w, 0, 0, 0);
                 acc_w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(lo), acc_w, 0, 0, 0);
@@ -1258,8 +1265,8 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
                 const int cg = c_base + cl;
                 if (cg < nope) {
                     uint2 o;
-                    o.x = pack2(f32_to_bf16_rne(acc[4 * a]), f32_to_bf16_rne(acc[4 * a + 1]));
-                    o.y = pack2(f32_to_bf16_rne(acc[4 * a + 2]), f32_to_bf16_rne(acc[4 * a + 3]));
+                    o.x = pack_bf16(acc[4 * a], acc[4 * a + 1]);
+                    o.y = pack_bf16(acc[4 * a + 2], acc[4 * a + 3]);
                     *reinterpret_cast<uint2*>(dol + hrow * C::PITCH + cl) = o;
                 } else {
                     f32x4 o = {acc[4 * a], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]};
@@ -1269,7 +1276,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         }
         __syncthreads();  // dY/O buffers free; dO and the pe scratch complete
         if (k + 1 < nchunks) {
-            stage_chunk(k + 1);
+            stage_chunk();  // chunk k+1
             if (k + 2 < nchunks) load_chunk(k + 2);  // in flight during two compute phases
         }
 
@@ -1304,11 +1311,15 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
                     y[4 + e] = o1[e] * c1[e] + sg * (p1[e] * s1[e]);
                 }
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) o[jj] = pack2(f32_to_bf16_rne(y[2 * jj]), f32_to_bf16_rne(y[2 * jj + 1]));
+                for (int jj = 0; jj < 4; ++jj) o[jj] = pack_bf16(y[2 * jj], y[2 * jj + 1]);
             }
             __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(outs + row * (int64_t)d + cl));
         }
         __syncthreads();  // dO buffers read; chunk k+1 staged
+        if (pe > 0 && k + 1 < nchunks && (k + 1) % cpt == 0 && ((k + 1) / cpt) % C::RG == 0) {
+            load_rope_group(s_begin + (k + 1) / cpt);  // the next RG tokens' cos/sin rows
+            __syncthreads();
+        }
     }
 
     // ---- dW partial: the k-sets of each tile summed in k-set order (fixed)
@@ -1450,7 +1461,7 @@ __global__ __launch_bounds__(512) void rope_apply_kernel(
         u32x4 o;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            uint32_t rr[2];
+            float r[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int k = 2 * jj + e;
@@ -1458,9 +1469,9 @@ __global__ __launch_bounds__(512) void rope_apply_kernel(
                 const float sn = sp * (k < 4 ? s0[k] : s1[k - 4]);
                 const float x = bf16_to_f32((own[jj] >> (16 * e)) & 0xffffu);
                 const float y = bf16_to_f32((par[jj] >> (16 * e)) & 0xffffu);
-                rr[e] = f32_to_bf16_rne(x * c + y * sn);
+                r[e] = x * c + y * sn;
             }
-            o[jj] = pack2(rr[0], rr[1]);
+            o[jj] = pack_bf16(r[0], r[1]);
         }
         __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(Out + base + i0));
     }
