@@ -345,3 +345,12 @@ def test_production_forward_and_backward_sampled():
     """sq=16384, nh=64, 448+64, positions 16384..32767: Y and dO sampled,
     dW sampled and bitwise identical over 10 runs."""
     sampled_check(synthetic.CASES["prod"], ("fwd", "dx", "dw", "bwd"), repeat_dw=10)
+
+
+def test_fused_backward_long_blocks_sampled():
+    """sq=20500, nh=64: the fused backward's token blocks hold 24 tokens (the
+    last one 4), so the staged cos/sin rows are reloaded after 16 tokens inside
+    every block.  dO sampled against the oracle and bitwise equal to bwd_dx;
+    dW sampled against the oracle and repeatable."""
+    c = synthetic.case(20500, 64, 448, 64, seed=6100, pos_offset=7)
+    sampled_check(c, ("dx", "dw", "bwd"), n_samples=2048, repeat_dw=2)
