@@ -572,9 +572,16 @@ __global__ __launch_bounds__(256) void rope_table_kernel(double theta, int pe, i
 //          scratch; the store phase rotates the pe pairs and writes the rows.
 // ---------------------------------------------------------------------------
 
-template <int NH, int CP, int WAVES>
+// pe channels that the MFMA epilogue rotates in registers (paired pe blocks, below)
+__host__ __device__ __forceinline__ bool pe_pairs_in_blocks(int nope, int pe) {
+    return pe > 0 && pe % 32 == 0 && nope % 32 == 0;
+}
+
+template <int NH, int CP, int WAVES, int NS = 1>
 struct PartCfg {
     static constexpr int KB = NH / 16, NB = NH / 32, NT = 64 * WAVES;
+    // NS > 1: wave w computes N-blocks (w % NS)*NBW .. +NBW of M-blocks w/NS, +MSTEP, ...
+    static constexpr int NBW = NB / NS, MSTEP = WAVES / NS;
     static constexpr int PITCH = CP + 8;                 // bf16 elements per LDS tile row
     static constexpr int WPITCH = NH + 8;                // bf16 elements per LDS row of W
     static constexpr int VPR = CP / 8;                   // 16-byte vectors per tile row
@@ -582,13 +589,17 @@ struct PartCfg {
     static constexpr int WVPR = NH / 8;                  // 16-byte vectors per row of W
     static constexpr int WVPT = (NH * WVPR + NT - 1) / NT;
     static constexpr int MBP = CP / 32;                  // M-blocks per part
-    static_assert(NH % 32 == 0 && CP % 32 == 0 && (NH * VPR) % NT == 0, "part tile shape");
-    __host__ __device__ static size_t aux_bytes(int pe) {
-        const size_t w = (size_t)NH * WPITCH * 2, p = (size_t)NH * (pe + 4) * 4;
-        return w > p ? w : p;
+    static_assert(NH % 32 == 0 && CP % 32 == 0 && (NH * VPR) % NT == 0 && CP >= NH, "part tile shape");
+    static_assert(NB % NS == 0 && WAVES % NS == 0 && MBP % MSTEP == 0, "N split");
+    // fp32 pe scratch: only for pe layouts that are not rotated in registers
+    __host__ __device__ static size_t aux_bytes(int nope, int pe) {
+        return pe_pairs_in_blocks(nope, pe) ? 0 : (size_t)NH * (pe + 4) * 4;
     }
-    // tile, then W / pe scratch, then this tile's cos and sin rows (pe/2 floats each)
-    __host__ __device__ static size_t lds_bytes(int pe) { return (size_t)NH * PITCH * 2 + aux_bytes(pe) + (size_t)pe * 4; }
+    // tile (W is staged there first), then the pe scratch, then this tile's
+    // cos and sin rows (pe/2 floats each)
+    __host__ __device__ static size_t lds_bytes(int nope, int pe) {
+        return (size_t)NH * PITCH * 2 + aux_bytes(nope, pe) + (size_t)pe * 4;
+    }
 };
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -625,9 +636,6 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* base, int pitch, int l
 // registers r and r + 8 (rows 8(r/4) + 4Q + r%4 and that + 16), so the
 // rotation happens in registers and the results are rounded to bf16 at once:
 // no fp32 scratch, and the store phase is one plain copy for every vector.
-__host__ __device__ __forceinline__ bool pe_pairs_in_blocks(int nope, int pe) {
-    return pe > 0 && pe % 32 == 0 && nope % 32 == 0;
-}
 
 // Rotate a paired block's accumulators and write both halves (bf16) into
 // row-major `out` (pitch in elements) at local pe offset L (first pe channel):
@@ -658,20 +666,20 @@ __device__ __forceinline__ void rotate_paired_block(const f32x16& acc, uint16_t*
     }
 }
 
-template <int NH, int CP, int WAVES, bool DX>
+template <int NH, int CP, int WAVES, bool DX, int NS>
 __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
     const int32_t* __restrict__ positions, int nope, int pe, int cpt, int64_t n_tiles,
     uint16_t* __restrict__ Out) {
-    using C = PartCfg<NH, CP, WAVES>;
+    using C = PartCfg<NH, CP, WAVES, NS>;
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint16_t* tile = smem;                                   // [NH][PITCH] bf16
-    uint16_t* wl = smem + NH * C::PITCH;                     // [NH][WPITCH] bf16, then:
-    float* pes = reinterpret_cast<float*>(wl);               // [NH][pe + 4] fp32
+    uint16_t* wl = smem;                                     // [NH][WPITCH] bf16 first, in the tile's place
+    float* pes = reinterpret_cast<float*>(smem + NH * C::PITCH);  // [NH][pe + 4] fp32 (unpaired pe)
     const int pes_pitch = pe + 4;
-    float* csl = reinterpret_cast<float*>(reinterpret_cast<char*>(wl) + C::aux_bytes(pe));  // [pe/2]
-    float* snl = csl + (pe >> 1);                                                            // [pe/2]
+    float* csl = reinterpret_cast<float*>(reinterpret_cast<char*>(pes) + C::aux_bytes(nope, pe));  // [pe/2]
+    float* snl = csl + (pe >> 1);                                                                   // [pe/2]
 
     const int d = nope + pe;
     const int h2 = pe >> 1;
@@ -708,19 +716,21 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
         }
     }
     __syncthreads();
-    bf16x8 wf[C::KB][C::NB];
+    const int ng = wave % NS;  // this wave's N-group: N-blocks ng*NBW .. +NBW
+    bf16x8 wf[C::KB][C::NBW];
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
+        for (int j = 0; j < C::NBW; ++j) {
+            const int nb = ng * C::NBW + j;
             if (DX) {  // B[k=g][n=h] = W[g][h]
-                wf[kb][nb] = tr_frag(wl + (16 * kb) * C::WPITCH + 32 * nb, C::WPITCH, lane);
+                wf[kb][j] = tr_frag(wl + (16 * kb) * C::WPITCH + 32 * nb, C::WPITCH, lane);
             } else {   // B[k=h][n=g] = W[g][h]
                 const int g = 32 * nb + (lane & 31), h = 16 * kb + 8 * (lane >> 5);
-                wf[kb][nb] = *reinterpret_cast<const bf16x8*>(wl + g * C::WPITCH + h);
+                wf[kb][j] = *reinterpret_cast<const bf16x8*>(wl + g * C::WPITCH + h);
             }
         }
-    __syncthreads();  // W's LDS becomes the pe scratch
+    __syncthreads();  // W's LDS becomes the tile
 
     const int Q = lane >> 5;
     if (t < n_tiles) {
@@ -740,12 +750,12 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
         const bool paired = tile_pe && pe_pairs_in_blocks(nope, pe);
         const int L = nope - c_base;  // local index of the first pe channel (tiles with pe)
 
-        for (int b = wave; b < C::MBP; b += WAVES) {
-            f32x16 acc[C::NB];
+        for (int b = wave / NS; b < C::MBP; b += C::MSTEP) {
+            f32x16 acc[C::NBW];
 #pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb)
+            for (int j = 0; j < C::NBW; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[nb][r] = 0.0f;
+                for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
             const bool pb = paired && 32 * b >= L;  // a paired pe block (wave-uniform)
             const int q = b - (L >> 5);
             const int clo = pb ? L + 16 * q : 32 * b, chi = pb ? L + h2 + 16 * q : 32 * b + 16;
@@ -756,18 +766,22 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
 #pragma unroll
             for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-                for (int nb = 0; nb < C::NB; ++nb)
-                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], wf[kb][nb], acc[nb], 0, 0, 0);
+                for (int j = 0; j < C::NBW; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], wf[kb][j], acc[j], 0, 0, 0);
+            // with an N split, other waves read this M-block's columns too: all
+            // reads are done before any wave overwrites them with results
+            if (NS > 1) __syncthreads();
             if (pb) {
 #pragma unroll
-                for (int nb = 0; nb < C::NB; ++nb)
-                    rotate_paired_block(acc[nb], tile, C::PITCH, 32 * nb + (lane & 31), L, h2, q, Q, csl, snl,
-                                        DX ? -1.0f : 1.0f);
+                for (int j = 0; j < C::NBW; ++j)
+                    rotate_paired_block(acc[j], tile, C::PITCH, 32 * (ng * C::NBW + j) + (lane & 31), L, h2, q, Q,
+                                        csl, snl, DX ? -1.0f : 1.0f);
                 continue;
             }
             // D register r of lane half Q: channel 32b + 8(r/4) + 4Q + r%4, head 32nb + lane%32
 #pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb) {
+            for (int j = 0; j < C::NBW; ++j) {
+                const int nb = ng * C::NBW + j;
                 const int g = 32 * nb + (lane & 31);
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
@@ -775,11 +789,11 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
                     const int cg = c_base + cl;
                     if (cg < nope) {
                         uint2 o;
-                        o.x = pack_bf16(acc[nb][4 * a], acc[nb][4 * a + 1]);
-                        o.y = pack_bf16(acc[nb][4 * a + 2], acc[nb][4 * a + 3]);
+                        o.x = pack_bf16(acc[j][4 * a], acc[j][4 * a + 1]);
+                        o.y = pack_bf16(acc[j][4 * a + 2], acc[j][4 * a + 3]);
                         *reinterpret_cast<uint2*>(tile + g * C::PITCH + cl) = o;
                     } else {
-                        f32x4 o = {acc[nb][4 * a], acc[nb][4 * a + 1], acc[nb][4 * a + 2], acc[nb][4 * a + 3]};
+                        f32x4 o = {acc[j][4 * a], acc[j][4 * a + 1], acc[j][4 * a + 2], acc[j][4 * a + 3]};
                         *reinterpret_cast<f32x4*>(pes + g * pes_pitch + (cg - nope)) = o;
                     }
                 }
@@ -1516,17 +1530,17 @@ static hipError_t launch_mix_t(const MixArgs& a, hipStream_t stream) {
 }
 
 // token-part kernel: one workgroup per tile = (token, CP-channel part)
-template <int NH, int CP, int WAVES, bool DX>
+template <int NH, int CP, int WAVES, bool DX, int NS = 1>
 static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
-    using C = PartCfg<NH, CP, WAVES>;
+    using C = PartCfg<NH, CP, WAVES, NS>;
     const int d = a.nope + a.pe;
     const int cpt = d / CP;
     const int64_t n_tiles = a.sq * cpt;
-    const size_t lds = C::lds_bytes(a.pe);
-    auto kern = mix_part_kernel<NH, CP, WAVES, DX>;
+    const size_t lds = C::lds_bytes(a.nope, a.pe);
+    auto kern = mix_part_kernel<NH, CP, WAVES, DX, NS>;
     static bool attr_done = false;  // idempotent; a race only repeats the call
     if (!attr_done) {
-        const size_t lds_max = C::lds_bytes(CP);
+        const size_t lds_max = C::lds_bytes(8, CP);  // largest: pe = CP with the scratch
         if (lds_max > 65536) {
             hipError_t e = hipFuncSetAttribute((const void*)kern,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
@@ -1563,7 +1577,7 @@ static hipError_t launch_mix_dx(const MixArgs& a, hipStream_t stream) {
     if (cp == 128 && a.nh == 64) return launch_part_t<64, 128, 4, DX>(a, stream);
     if (cp == 256 && a.nh == 32) return launch_part_t<32, 256, 8, DX>(a, stream);
     if (cp == 128 && a.nh == 32) return launch_part_t<32, 128, 4, DX>(a, stream);
-    if (cp == 128 && a.nh == 128) return launch_part_t<128, 128, 4, DX>(a, stream);
+    if (cp == 128 && a.nh == 128) return launch_part_t<128, 128, 8, DX, 4>(a, stream);  // N split in 4
     if (a.nh <= 16) return launch_mix_t<16, 2, DX>(a, stream);
     if (a.nh <= 32) return launch_mix_t<32, 2, DX>(a, stream);
     if (a.nh <= 64) return launch_mix_t<64, 2, DX>(a, stream);
