@@ -1512,6 +1512,8 @@ hipError_t launch_rope_apply(const uint16_t* X, const float* rcos, const float* 
 // host-side launchers (argument checks are done by the caller)
 // ---------------------------------------------------------------------------
 
+static constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+
 template <int NHP, int MPI, bool DX>
 static hipError_t launch_mix_t(const MixArgs& a, hipStream_t stream) {
     const int d = a.nope + a.pe;
@@ -1540,7 +1542,8 @@ static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
     auto kern = mix_part_kernel<NH, CP, WAVES, DX, NS>;
     static bool attr_done = false;  // idempotent; a race only repeats the call
     if (!attr_done) {
-        const size_t lds_max = C::lds_bytes(8, CP);  // largest: pe = CP with the scratch
+        size_t lds_max = C::lds_bytes(8, CP);  // largest: pe = CP with the scratch
+        if (lds_max > kMaxLds) lds_max = kMaxLds;  // shapes beyond it are not routed here
         if (lds_max > 65536) {
             hipError_t e = hipFuncSetAttribute((const void*)kern,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
@@ -1555,13 +1558,15 @@ static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
 
 // Channel-part width of the token-part kernel for this shape, or 0 when the
 // shape needs the general kernel: nh must be 32, 64 or 128, the part must
-// divide d, hold the whole pe range, and the grid must stay below 2^31.
+// divide d, hold the whole pe range, fit the workgroup's LDS, and the grid
+// must stay below 2^31.
 int mix_part_width(int64_t sq, int nh, int nope, int pe) {
     if (nh != 32 && nh != 64 && nh != 128) return 0;
     const int d = nope + pe;
-    const int cands[2] = {nh == 128 ? 128 : 256, 128};
+    const int cands[2] = {256, 128};
     for (int cp : cands) {
         if (d % cp != 0 || pe > cp) continue;
+        if (nh == 128 && cp == 256 && PartCfg<128, 256, 8, 4>::lds_bytes(nope, pe) > kMaxLds) continue;
         if (sq * (int64_t)(d / cp) >= ((int64_t)1 << 31)) return 0;
         return cp;
     }
@@ -1577,7 +1582,8 @@ static hipError_t launch_mix_dx(const MixArgs& a, hipStream_t stream) {
     if (cp == 128 && a.nh == 64) return launch_part_t<64, 128, 4, DX>(a, stream);
     if (cp == 256 && a.nh == 32) return launch_part_t<32, 256, 8, DX>(a, stream);
     if (cp == 128 && a.nh == 32) return launch_part_t<32, 128, 4, DX>(a, stream);
-    if (cp == 128 && a.nh == 128) return launch_part_t<128, 128, 8, DX, 4>(a, stream);  // N split in 4
+    if (cp == 256 && a.nh == 128) return launch_part_t<128, 256, 8, DX, 4>(a, stream);  // N split in 4
+    if (cp == 128 && a.nh == 128) return launch_part_t<128, 128, 8, DX, 4>(a, stream);
     if (a.nh <= 16) return launch_mix_t<16, 2, DX>(a, stream);
     if (a.nh <= 32) return launch_mix_t<32, 2, DX>(a, stream);
     if (a.nh <= 64) return launch_mix_t<64, 2, DX>(a, stream);

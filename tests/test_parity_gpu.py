@@ -142,6 +142,8 @@ def kernel_policy(request):
     (11, 64, 480, 32, 5),      # pe = 32: one paired pe block (partners 16 apart)
     (9, 64, 416, 96, 11),      # pe = 96: three paired pe blocks
     (8, 64, 464, 48, 21),      # nope % 32 != 0: pe rotated through the fp32 scratch
+    (7, 128, 320, 64, 9),      # nh = 128, d = 384: 128-channel parts, heads split over wave groups
+    (3, 128, 16, 240, 5),      # nh = 128 with an fp32 scratch too large for the LDS: general kernel
 ])
 def test_small_shapes(sq, nh, nope, pe, off, kernel_policy):
     full_check(synthetic.case(sq, nh, nope, pe, seed=1000 + sq + nh, pos_offset=off))
