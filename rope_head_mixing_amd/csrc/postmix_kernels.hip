@@ -860,10 +860,11 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
 
 template <int NH, int CH>
 struct DwCfg {
-    static constexpr int WAVES = 4, NT = 256;
+    // nh <= 64: 4 waves split the k-steps; nh = 128: 8 waves own 2 output tiles each
     static constexpr int NB = NH / 32;
     static constexpr bool SPLIT_K = NB <= 2;
-    static constexpr int TG = SPLIT_K ? NB : 2, TH = TG;
+    static constexpr int WAVES = SPLIT_K ? 4 : 8, NT = 64 * WAVES;
+    static constexpr int TG = SPLIT_K ? NB : 2, TH = SPLIT_K ? NB : NB * NB / (WAVES * TG);
     static constexpr int PITCH = CH + 8;
     static constexpr int VPR = CH / 8;
     static constexpr int VPO = NH * VPR;           // vectors per operand per chunk
@@ -875,7 +876,7 @@ struct DwCfg {
 };
 
 template <int NH, int CH>
-__global__ __launch_bounds__(256) void dw_chunk_kernel(
+__global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
     const int32_t* __restrict__ positions, int64_t sq, int nope, int pe,
@@ -891,8 +892,8 @@ __global__ __launch_bounds__(256) void dw_chunk_kernel(
     const int d = nope + pe, h2 = pe >> 1;
     const int cpt = d / CH;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
-    const int gb0 = C::SPLIT_K ? 0 : 2 * (wave >> 1);
-    const int hb0 = C::SPLIT_K ? 0 : 2 * (wave & 1);
+    const int gb0 = C::SPLIT_K ? 0 : C::TG * (wave / (C::NB / C::TH));
+    const int hb0 = C::SPLIT_K ? 0 : C::TH * (wave % (C::NB / C::TH));
 
     const int64_t s_begin = (int64_t)blockIdx.x * tokens_per_block;
     int64_t s_end = s_begin + tokens_per_block;
@@ -1640,7 +1641,8 @@ static hipError_t launch_dw_t(const DwArgs& a, hipStream_t stream) {
     const int64_t nb = dw_num_blocks(a.sq, a.nh);
     const int ch = a.force_general ? 0 : dw_chunk_width(a.nh, a.nope, a.pe);
     if (ch == 128 && a.nh == NHP && (NHP == 32 || NHP == 64 || NHP == 128)) {
-        hipLaunchKernelGGL((dw_chunk_kernel<(NHP < 32 ? 32 : NHP), 128>), dim3((unsigned)nb), dim3(256), 0,
+        hipLaunchKernelGGL((dw_chunk_kernel<(NHP < 32 ? 32 : NHP), 128>), dim3((unsigned)nb),
+                           dim3(DwCfg<(NHP < 32 ? 32 : NHP), 128>::NT), 0,
                            stream, a.dY, a.O, a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nope,
                            a.pe, a.partials, tpb);
     } else {
