@@ -134,7 +134,8 @@ int postmix_bwd_dw(const pm_bf16 *dY, const pm_bf16 *O, const float *rope_cos,
 /*
  * Backward, both gradients in one call: dO as postmix_bwd_dx and dW as
  * postmix_bwd_dw, from a single pass over dY and O where the shape allows
- * (nh == 64, nope + pe a multiple of 128, pe <= 128): each (token, channel
+ * (nope + pe a multiple of 128, pe <= 128, and nh == 64, or nh == 128 with pe
+ * and nope multiples of 32): each (token, channel
  * chunk) of dY and O is read from HBM once and feeds both the head-mix
  * gradient and the weight-gradient partials.  That is one full read of dY
  * fewer than the two separate calls.  Other shapes (or

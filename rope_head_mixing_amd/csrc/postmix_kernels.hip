@@ -1089,6 +1089,9 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
 template <int NH, int CH, int WAVES>
 struct BwdCfg {
     static constexpr int NT = 64 * WAVES;
+    // nh = 128: W stays in LDS and its fragments are read per use (registers
+    // would not hold them beside the rest); only pe rotated in registers
+    static constexpr bool WRES = NH > 64;
     static constexpr int NB = NH / 32, KB = NH / 16;
     static constexpr int PITCH = CH + 8;
     static constexpr int WPITCH = NH + 8;
@@ -1100,16 +1103,20 @@ struct BwdCfg {
     static constexpr int MBC = CH / 32;             // M-blocks of the head mix per chunk
     static constexpr int NTILE = NB * NB;           // dW output tiles
     static constexpr int KSET = WAVES / NTILE;      // waves per dW tile
-    static_assert(NH == 64 && MBC * NB == WAVES && KS % KSET == 0 && VPO % NT == 0, "fused shape");
-    __host__ __device__ static size_t aux_bytes(int pe) {
-        const size_t w = (size_t)NH * WPITCH * 2, p = (size_t)NH * (pe + 4) * 4;
-        return w > p ? w : p;
+    static_assert((NH == 64 || NH == 128) && MBC * NB == WAVES && KSET >= 1 && KS % KSET == 0 &&
+                  VPO % NT == 0, "fused shape");
+    // W and the fp32 pe scratch, overlapped (W is consumed at set-up) unless W
+    // stays resident; the scratch is not needed for pe rotated in registers
+    __host__ __device__ static size_t aux_bytes(int nope, int pe) {
+        const size_t w = (size_t)NH * WPITCH * 2;
+        const size_t p = pe_pairs_in_blocks(nope, pe) ? 0 : (size_t)NH * (pe + 4) * 4;
+        return WRES ? w + p : (w > p ? w : p);
     }
     static constexpr int RG = 16;                   // tokens per group of staged cos/sin rows
     // dY chunk, O chunk, dO chunk, then W / pe scratch, then the cos and sin
     // rows of RG tokens
-    __host__ __device__ static size_t lds_bytes(int pe) {
-        return (size_t)3 * NH * PITCH * 2 + aux_bytes(pe) + (size_t)RG * pe * 4;
+    __host__ __device__ static size_t lds_bytes(int nope, int pe) {
+        return (size_t)3 * NH * PITCH * 2 + aux_bytes(nope, pe) + (size_t)RG * pe * 4;
     }
 };
 
@@ -1125,10 +1132,10 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     uint16_t* ol = dyl + NH * C::PITCH;                 // [NH][PITCH]
     uint16_t* dol = ol + NH * C::PITCH;                 // [NH][PITCH]
     uint16_t* wl = dol + NH * C::PITCH;                 // [NH][WPITCH] bf16, then:
-    float* pes = reinterpret_cast<float*>(wl);          // [NH][pe + 4] fp32
+    float* pes = reinterpret_cast<float*>(wl + (C::WRES ? NH * C::WPITCH : 0));  // [NH][pe + 4] fp32
     const int pes_pitch = pe + 4;
     // cos/sin rows of RG consecutive tokens: [RG][pe] floats (cos then sin each)
-    float* const rope_g = reinterpret_cast<float*>(reinterpret_cast<char*>(wl) + C::aux_bytes(pe));
+    float* const rope_g = reinterpret_cast<float*>(reinterpret_cast<char*>(wl) + C::aux_bytes(nope, pe));
 
     const int d = nope + pe, h2 = pe >> 1;
     const int cpt = d / CH;
@@ -1191,10 +1198,12 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         *reinterpret_cast<u32x4*>(wl + row * C::WPITCH + 8 * c8) = reinterpret_cast<const u32x4*>(W)[q];
     }
     __syncthreads();
-    bf16x8 wf[C::KB];
+    bf16x8 wf[C::WRES ? 1 : C::KB];  // W fragments in registers, or read from LDS per use
+    if (!C::WRES) {
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) wf[kb] = tr_frag(wl + (16 * kb) * C::WPITCH + 32 * nb, C::WPITCH, lane);
-    __syncthreads();  // W's LDS becomes the pe scratch
+        for (int kb = 0; kb < C::KB; ++kb) wf[kb] = tr_frag(wl + (16 * kb) * C::WPITCH + 32 * nb, C::WPITCH, lane);
+    }
+    __syncthreads();  // W's LDS becomes the pe scratch (unless W stays resident)
 
     f32x16 acc_w;
 #pragma unroll
@@ -1270,8 +1279,11 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             for (int kb = 0; kb < C::KB; ++kb)
                 af[kb] = tr_frag2(dyl + (16 * kb) * C::PITCH, clo, chi, C::PITCH, lane);
 #pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], wf[kb], acc, 0, 0, 0);
+            for (int kb = 0; kb < C::KB; ++kb) {
+                const bf16x8 b = C::WRES ? tr_frag(wl + (16 * kb) * C::WPITCH + 32 * nb, C::WPITCH, lane)
+                                         : wf[C::WRES ? 0 : kb];
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], b, acc, 0, 0, 0);
+            }
             const int hrow = 32 * nb + (lane & 31);
             if (pb) rotate_paired_block(acc, dol, C::PITCH, hrow, L, h2, q, Q, csl, snl, -1.0f);
 #pragma unroll
@@ -1661,24 +1673,28 @@ static hipError_t launch_dw_t(const DwArgs& a, hipStream_t stream) {
 // fused backward (dx + dW partials in one pass), then the fixed-order reduce
 bool bwd_fused_applies(int nh, int nope, int pe) {
     const int d = nope + pe;
-    return nh == 64 && d % 128 == 0 && pe <= 128;
+    if (d % 128 != 0 || pe > 128) return false;
+    return nh == 64 || (nh == 128 && (pe == 0 || pe_pairs_in_blocks(nope, pe)));
 }
 
 // chunk width of the fused backward: 256 channels (16 waves) where d allows
 static int bwd_fused_chunk(int d) { return d % 256 == 0 ? 256 : 128; }
 
-template <int CH, int WAVES>
+template <int NH, int CH, int WAVES>
 static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int tpb, int64_t nb, hipStream_t stream) {
-    using C = BwdCfg<64, CH, WAVES>;
-    auto kern = bwd_fused_kernel<64, CH, WAVES>;
+    using C = BwdCfg<NH, CH, WAVES>;
+    auto kern = bwd_fused_kernel<NH, CH, WAVES>;
     static bool attr_done = false;  // idempotent; a race only repeats the call
     if (!attr_done) {
+        size_t lds_max = C::lds_bytes(8, 128);  // largest: pe = 128 with the scratch
+        if (lds_max > kMaxLds) lds_max = kMaxLds;
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)C::lds_bytes(128));
+                                           (int)lds_max);
         if (e != hipSuccess) return e;
         attr_done = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), C::lds_bytes(a.pe), stream, a.dY, a.O, mx.W,
+    if (C::lds_bytes(a.nope, a.pe) > kMaxLds) return hipErrorInvalidValue;  // excluded by bwd_fused_applies
+    hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), C::lds_bytes(a.nope, a.pe), stream, a.dY, a.O, mx.W,
                        a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nope, a.pe, mx.Out, a.partials, tpb);
     return hipGetLastError();
 }
@@ -1686,8 +1702,12 @@ static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int tpb
 hipError_t launch_bwd_fused(const MixArgs& mx, const DwArgs& a, hipStream_t stream) {
     const int tpb = bwd_fused_tokens_per_block(a.sq, a.nh);
     const int64_t nb = bwd_fused_num_blocks(a.sq, a.nh);
-    hipError_t err = bwd_fused_chunk(a.nope + a.pe) == 256 ? launch_bwd_fused_t<256, 16>(mx, a, tpb, nb, stream)
-                                                          : launch_bwd_fused_t<128, 8>(mx, a, tpb, nb, stream);
+    hipError_t err;
+    if (a.nh == 128)
+        err = launch_bwd_fused_t<128, 128, 16>(mx, a, tpb, nb, stream);
+    else
+        err = bwd_fused_chunk(a.nope + a.pe) == 256 ? launch_bwd_fused_t<64, 256, 16>(mx, a, tpb, nb, stream)
+                                                    : launch_bwd_fused_t<64, 128, 8>(mx, a, tpb, nb, stream);
     if (err != hipSuccess) return err;
     const int64_t ne = (int64_t)a.nh * a.nh;
     hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((ne + 63) / 64)), dim3(1024), 0, stream,
