@@ -560,16 +560,18 @@ __global__ __launch_bounds__(256) void rope_table_kernel(double theta, int pe, i
 // row, read with 16-byte non-temporal loads like a copy and written back the
 // same way.  One workgroup per tile: the tile's loads are issued into
 // registers first, so they are in flight while W is staged.
-//   setup: W -> LDS (rows padded) -> each wave copies its B operand (W^T for
-//          the forward, W for dx) into registers.  W's LDS is then reused as
-//          the fp32 pe scratch.
+//   setup: W -> LDS (in the tile's place, rows padded) -> each wave copies its
+//          B operand (W^T for the forward, W for dx; the N-blocks of its
+//          N-group when the heads are split, NS > 1) into registers.
 //   tile:  registers -> LDS tile; each wave owns M-blocks of 32 channels; the
 //          A operand (rows = channels, k = heads) comes from the gfx950
 //          transposing LDS load ds_read_b64_tr_b16 (in each group of 16
 //          lanes, lane i receives T[k0+e][c0+i], e = 0..3, when source lane j
-//          points at T[k0 + j/4][c0 + 4*(j%4)]); nope results are rounded and
-//          written over the wave's own tile columns, pe results go to the fp32
-//          scratch; the store phase rotates the pe pairs and writes the rows.
+//          points at T[k0 + j/4][c0 + 4*(j%4)]).  Results are rounded and
+//          written over the M-block's own tile columns; pe blocks are rotated
+//          in registers first (paired pe blocks, below), or, for other pe
+//          layouts, go to an fp32 scratch and are rotated in the store phase,
+//          which writes whole rows.
 // ---------------------------------------------------------------------------
 
 // pe channels that the MFMA epilogue rotates in registers (paired pe blocks, below)
@@ -1078,12 +1080,15 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
 //          waves of a tile are added in k-set order (fixed);
 //   - dx:  wave w owns M-block w%(CH/32) and N-block w/(CH/32) of the chunk's head mix
 //          dX[c, h] = sum_g dY[g, c] W[g, h] (A = dY^T by transposing LDS
-//          loads, B = W in registers), writes nope results to an LDS output
-//          chunk and pe results to an fp32 scratch; the store phase rotates
-//          the pe pairs by +phi and writes dO rows with non-temporal stores.
+//          loads, B = W in registers, or read from LDS per use at nh = 128),
+//          rotates paired pe blocks by +phi in registers and writes the
+//          results to an LDS output chunk (other pe layouts: an fp32 scratch,
+//          rotated in the store phase); the store phase writes dO rows with
+//          non-temporal stores.
 // The dx arithmetic (MFMA inputs, k order, rotation expression) is that of
 // the token-part kernel, so dO is bitwise the same as postmix_bwd_dx's.
-// nh = 64, d a multiple of 128, pe <= 128 (all pe channels in a token's last chunk).
+// nh = 64, or nh = 128 with pe rotated in registers (16 waves, one dW tile
+// each); d a multiple of 128, pe <= 128 (all pe channels in a token's last chunk).
 // ---------------------------------------------------------------------------
 
 template <int NH, int CH, int WAVES>
