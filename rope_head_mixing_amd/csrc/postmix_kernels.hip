@@ -1526,6 +1526,210 @@ hipError_t launch_rope_apply(const uint16_t* X, const float* rcos, const float* 
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// small head counts (nh <= 4): plain fp32 vector arithmetic
+//
+// With a handful of heads the head mix is a few multiply-adds per element and
+// 32-row MFMA tiles would be mostly padding, so these kernels use VALU FMAs.
+// Workgroup = R consecutive tokens, R = max(1, 512 / (d/8)).  Work items: the
+// R*nope/8 nope vectors of the R tokens first, then the R*pe/8 pe vectors, so
+// that (at d = 512) whole waves take one path.  A work item is one 8-channel
+// vector position of one token, for all heads: it loads the nh input vectors,
+// forms out[o] = sum_i M[o][i] in[i] in fp32 (M = W for the forward, W^T for
+// dx), and for a pe vector also the partner vector's mix, then turns the pair
+// (-phi forward, +phi dx) and rounds once to bf16.
+// The weight gradient: the same items accumulate
+// sum_c dY[g, c] * inv_rope(O)[h, c] for all (g, h) in fp32 (the rotated
+// operand is formed in fp32, no bf16 split); the workgroup adds its items'
+// sums in a fixed tree and writes one partial per token block.
+// ---------------------------------------------------------------------------
+
+constexpr int SMALL_NH = 4;
+
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4& v, float* f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = __uint_as_float(v[j] << 16);
+        f[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+    }
+}
+
+template <bool DX>
+__global__ __launch_bounds__(512) void small_mix_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+    const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
+    const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe, int tokens_per_wg,
+    uint16_t* __restrict__ Out) {
+    const int d = nope + pe, h2 = pe >> 1, nv = nope >> 3, pv = pe >> 3;
+    float m[SMALL_NH][SMALL_NH];  // m[o][i]
+#pragma unroll
+    for (int o = 0; o < SMALL_NH; ++o)
+#pragma unroll
+        for (int i = 0; i < SMALL_NH; ++i)
+            m[o][i] = (o < nh && i < nh) ? bf16_to_f32(DX ? W[i * nh + o] : W[o * nh + i]) : 0.0f;
+    const int64_t s0 = (int64_t)blockIdx.x * tokens_per_wg;
+    const int n_copy = tokens_per_wg * nv, n_all = tokens_per_wg * (nv + pv);
+    for (int t = threadIdx.x; t < n_all; t += blockDim.x) {
+        const bool is_pe = t >= n_copy;
+        const int u = is_pe ? t - n_copy : t;
+        const int per = is_pe ? pv : nv;
+        const int r = u / per, v = u - r * per;
+        const int64_t s = s0 + r;
+        if (s >= sq) continue;
+        const int c = is_pe ? nope + 8 * v : 8 * v;
+        const uint16_t* xs = X + s * nh * (int64_t)d;
+        uint16_t* os = Out + s * nh * (int64_t)d;
+        float in[SMALL_NH][8];
+#pragma unroll
+        for (int i = 0; i < SMALL_NH; ++i) {
+            if (i < nh) bf16x8_to_f32(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xs + i * d + c)), in[i]);
+        }
+        if (!is_pe) {
+#pragma unroll
+            for (int o = 0; o < SMALL_NH; ++o) {
+                if (o >= nh) break;
+                float y[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float a = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < SMALL_NH; ++i)
+                        if (i < nh) a += m[o][i] * in[i][e];
+                    y[e] = a;
+                }
+                u32x4 w;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w[j] = pack_bf16(y[2 * j], y[2 * j + 1]);
+                __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(os + o * d + c));
+            }
+            continue;
+        }
+        const int i0 = 8 * v;  // index within the pe channels
+        const bool first = i0 < h2;
+        const int ii = first ? i0 : i0 - h2;
+        const int cp = nope + (first ? i0 + h2 : ii);
+        float par[SMALL_NH][8];
+#pragma unroll
+        for (int i = 0; i < SMALL_NH; ++i) {
+            if (i < nh) bf16x8_to_f32(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xs + i * d + cp)), par[i]);
+        }
+        const int64_t prow = table_row(positions, s, table_rows);
+        float cs[8], sn[8];
+        {
+            const f32x4 c0 = *reinterpret_cast<const f32x4*>(rcos + prow * h2 + ii);
+            const f32x4 c1 = *reinterpret_cast<const f32x4*>(rcos + prow * h2 + ii + 4);
+            const f32x4 q0 = *reinterpret_cast<const f32x4*>(rsin + prow * h2 + ii);
+            const f32x4 q1 = *reinterpret_cast<const f32x4*>(rsin + prow * h2 + ii + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { cs[e] = c0[e]; cs[4 + e] = c1[e]; sn[e] = q0[e]; sn[4 + e] = q1[e]; }
+        }
+        // forward (-phi): first half a C + b S, second half a C - b S;  dx (+phi): the signs swapped
+        const float sg = (first != DX) ? 1.0f : -1.0f;
+#pragma unroll
+        for (int o = 0; o < SMALL_NH; ++o) {
+            if (o >= nh) break;
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float a = 0.0f, b = 0.0f;
+#pragma unroll
+                for (int i = 0; i < SMALL_NH; ++i)
+                    if (i < nh) { a += m[o][i] * in[i][e]; b += m[o][i] * par[i][e]; }
+                y[e] = a * cs[e] + sg * (b * sn[e]);
+            }
+            u32x4 w;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[j] = pack_bf16(y[2 * j], y[2 * j + 1]);
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(os + o * d + c));
+        }
+    }
+}
+
+// one weight-gradient partial per block of tokens_per_block tokens; 256 threads
+__global__ __launch_bounds__(256) void small_dw_kernel(
+    const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O,
+    const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
+    const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe, int tokens_per_block,
+    float* __restrict__ partials) {
+    constexpr int NN = SMALL_NH * SMALL_NH;
+    __shared__ float red[NN][256];
+    const int d = nope + pe, h2 = pe >> 1, nv = nope >> 3, pv = pe >> 3;
+    const int64_t s0 = (int64_t)blockIdx.x * tokens_per_block;
+    int64_t s1 = s0 + tokens_per_block;
+    if (s1 > sq) s1 = sq;
+    const int vpr = nv + pv;
+    const int64_t n_items = (s1 - s0) * vpr;
+    float acc[NN];
+#pragma unroll
+    for (int k = 0; k < NN; ++k) acc[k] = 0.0f;
+    for (int64_t it = threadIdx.x; it < n_items; it += 256) {
+        const int64_t r = it / vpr;
+        const int v = (int)(it - r * vpr);
+        const int64_t s = s0 + r;
+        const bool is_pe = v >= nv;
+        const int c = 8 * v;  // nope vectors first, then pe vectors, in channel order
+        const uint16_t* ys = dY + s * nh * (int64_t)d;
+        const uint16_t* os = O + s * nh * (int64_t)d;
+        float g[SMALL_NH][8], x[SMALL_NH][8];
+#pragma unroll
+        for (int i = 0; i < SMALL_NH; ++i) {
+            if (i < nh) {
+                bf16x8_to_f32(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ys + i * d + c)), g[i]);
+                bf16x8_to_f32(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(os + i * d + c)), x[i]);
+            }
+        }
+        if (is_pe) {  // x <- inv_rope(O) for these 8 channels, in fp32
+            const int i0 = c - nope;
+            const bool first = i0 < h2;
+            const int ii = first ? i0 : i0 - h2;
+            const int cp = nope + (first ? i0 + h2 : ii);
+            const int64_t prow = table_row(positions, s, table_rows);
+            float cs[8], sn[8];
+            const f32x4 c0 = *reinterpret_cast<const f32x4*>(rcos + prow * h2 + ii);
+            const f32x4 c1 = *reinterpret_cast<const f32x4*>(rcos + prow * h2 + ii + 4);
+            const f32x4 q0 = *reinterpret_cast<const f32x4*>(rsin + prow * h2 + ii);
+            const f32x4 q1 = *reinterpret_cast<const f32x4*>(rsin + prow * h2 + ii + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { cs[e] = c0[e]; cs[4 + e] = c1[e]; sn[e] = q0[e]; sn[4 + e] = q1[e]; }
+            const float sg = first ? 1.0f : -1.0f;  // -phi: first half a C + b S, second a C - b S
+#pragma unroll
+            for (int i = 0; i < SMALL_NH; ++i) {
+                if (i >= nh) break;
+                float p[8];
+                bf16x8_to_f32(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(os + i * d + cp)), p);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[i][e] = x[i][e] * cs[e] + sg * (p[e] * sn[e]);
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < SMALL_NH; ++a)
+#pragma unroll
+            for (int b = 0; b < SMALL_NH; ++b) {
+                if (a >= nh || b >= nh) continue;
+                float t = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) t += g[a][e] * x[b][e];
+                acc[a * SMALL_NH + b] += t;
+            }
+    }
+    // fixed-order tree over the 256 threads
+#pragma unroll
+    for (int k = 0; k < NN; ++k) red[k][threadIdx.x] = acc[k];
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) {
+#pragma unroll
+            for (int k = 0; k < NN; ++k) red[k][threadIdx.x] += red[k][threadIdx.x + w];
+        }
+        __syncthreads();
+    }
+    if ((int)threadIdx.x < nh * nh) {
+        const int a = threadIdx.x / nh, b = threadIdx.x % nh;
+        partials[(int64_t)blockIdx.x * nh * nh + threadIdx.x] = red[a * SMALL_NH + b][0];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // host-side launchers (argument checks are done by the caller)
 // ---------------------------------------------------------------------------
@@ -1602,6 +1806,16 @@ static hipError_t launch_mix_dx(const MixArgs& a, hipStream_t stream) {
     if (cp == 128 && a.nh == 32) return launch_part_t<32, 128, 4, DX>(a, stream);
     if (cp == 256 && a.nh == 128) return launch_part_t<128, 256, 8, DX, 4>(a, stream);  // N split in 4
     if (cp == 128 && a.nh == 128) return launch_part_t<128, 128, 8, DX, 4>(a, stream);
+    if (!a.force_general && a.nh <= SMALL_NH) {
+        const int vpr = (a.nope + a.pe) / 8;
+        const int tok = vpr >= 512 ? 1 : 512 / vpr;
+        const int64_t grid = (a.sq + tok - 1) / tok;
+        int threads = (tok * vpr + 63) / 64 * 64;
+        if (threads > 512) threads = 512;
+        hipLaunchKernelGGL(small_mix_kernel<DX>, dim3((unsigned)grid), dim3(threads), 0, stream, a.X, a.W,
+                           a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, tok, a.Out);
+        return hipGetLastError();
+    }
     if (a.nh <= 16) return launch_mix_t<16, 2, DX>(a, stream);
     if (a.nh <= 32) return launch_mix_t<32, 2, DX>(a, stream);
     if (a.nh <= 64) return launch_mix_t<64, 2, DX>(a, stream);
@@ -1657,7 +1871,10 @@ static hipError_t launch_dw_t(const DwArgs& a, hipStream_t stream) {
     const int tpb = dw_tokens_per_block(a.sq, a.nh);
     const int64_t nb = dw_num_blocks(a.sq, a.nh);
     const int ch = a.force_general ? 0 : dw_chunk_width(a.nh, a.nope, a.pe);
-    if (ch == 128 && a.nh == NHP && (NHP == 32 || NHP == 64 || NHP == 128)) {
+    if (!a.force_general && a.nh <= SMALL_NH) {
+        hipLaunchKernelGGL(small_dw_kernel, dim3((unsigned)nb), dim3(256), 0, stream, a.dY, a.O, a.rcos,
+                           a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, tpb, a.partials);
+    } else if (ch == 128 && a.nh == NHP && (NHP == 32 || NHP == 64 || NHP == 128)) {
         hipLaunchKernelGGL((dw_chunk_kernel<(NHP < 32 ? 32 : NHP), 128>), dim3((unsigned)nb),
                            dim3(DwCfg<(NHP < 32 ? 32 : NHP), 128>::NT), 0,
                            stream, a.dY, a.O, a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nope,
