@@ -281,8 +281,9 @@ def test_empty_token_range():
     assert torch.equal(dW.cpu(), torch.zeros(4, 4))
 
 
-def test_dw_repeatable_bitwise_small():
-    c = synthetic.case(300, 64, 448, 64, seed=444, pos_offset=100)
+@pytest.mark.parametrize("nh", [64, 3])   # MFMA tiles; fp32 vector kernel for small nh
+def test_dw_repeatable_bitwise_small(nh):
+    c = synthetic.case(300, nh, 448, 64, seed=444, pos_offset=100)
     dv = Dev(c)
     first = dv.dw().cpu().numpy()
     for _ in range(9):
