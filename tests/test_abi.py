@@ -298,3 +298,18 @@ def test_kv_remap_empty_and_in_place_pass_validation():
     assert remap(topk=0, idx=0, out=0)[0] == pm.PM_OK
     rc, msg = remap(out=A)  # in place: validation passes, then the device check decides
     assert rc not in (pm.PM_ERR_NULL, pm.PM_ERR_SHAPE, pm.PM_ERR_ALIGN, pm.PM_ERR_OVERLAP), msg
+
+
+def test_benchmark_kernel_names_exist_in_the_library():
+    """bench.py attributes trace and counter rows to ops by kernel name; every
+    name it uses must be a kernel the library actually contains."""
+    import shutil
+    import subprocess
+    import bench
+    from rope_head_mixing_amd import postmix as pm
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-C", pm.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    for op, names in bench.KERNELS_NH64.items():
+        for name in (n.strip() for n in names.split("+")):
+            assert f"pm::{name}(" in out, f"{op}: kernel {name!r} not in {pm.LIB_PATH}"
