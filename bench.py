@@ -35,10 +35,10 @@ KERNEL_SOURCE = os.path.join(ROOT, "rope_head_mixing_amd", "csrc", "postmix_kern
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # kernels behind each op at nh=64, d=512 (tiled path)
 KERNELS_NH64 = {
-    "fwd": "mix_part_kernel<64, 256, 8, false, 1>",
+    "fwd": "mix_part_kernel<64, 256, 8, false, 1, false>",
     "bwd": "bwd_fused_kernel<64, 256, 16> + dw_reduce_kernel",
-    "bwd_dx": "mix_part_kernel<64, 256, 8, true, 1>",
-    "bwd_dw": "dw_chunk_kernel<64, 128> + dw_reduce_kernel",
+    "bwd_dx": "mix_part_kernel<64, 256, 8, true, 1, false>",
+    "bwd_dw": "dw_chunk_kernel<64, 128, false> + dw_reduce_kernel",
 }
 STEP_OPS = ("fwd", "bwd")          # the timed step
 EXTRA_OPS = ("bwd_dx", "bwd_dw")   # the separate backward entry points, timed after

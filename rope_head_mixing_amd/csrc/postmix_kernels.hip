@@ -668,12 +668,14 @@ __device__ __forceinline__ void rotate_paired_block(const f32x16& acc, uint16_t*
     }
 }
 
-template <int NH, int CP, int WAVES, bool DX, int NS>
+template <int NH, int CP, int WAVES, bool DX, int NS, bool PAD>
 __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
-    const int32_t* __restrict__ positions, int nope, int pe, int cpt, int64_t n_tiles,
+    const int32_t* __restrict__ positions, int nh, int nope, int pe, int cpt, int64_t n_tiles,
     uint16_t* __restrict__ Out) {
+    // PAD: nh < NH, rows nh .. NH-1 of the tile and of W are zero padding
+    // (never loaded from or stored to HBM); otherwise nh == NH
     using C = PartCfg<NH, CP, WAVES, NS>;
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint16_t* tile = smem;                                   // [NH][PITCH] bf16
@@ -693,7 +695,7 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
     auto load_tile = [&](int64_t tt) {
         const int64_t s = tt / cpt;
         const int part = (int)(tt - s * cpt);
-        const uint16_t* xs = X + s * NH * (int64_t)d + part * CP;
+        const uint16_t* xs = X + s * nh * (int64_t)d + part * CP;
         if (pe > 0 && (part + 1) * CP > nope && tid < (pe >> 2)) {
             const int64_t prow = table_row(positions, s, table_rows);
             const int q4 = tid % (pe >> 3);
@@ -703,18 +705,28 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
         for (int j = 0; j < C::VPT; ++j) {
             const int q = j * C::NT + tid;
             const int row = q / C::VPR, c8 = q % C::VPR;
-            v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xs + row * (int64_t)d + 8 * c8));
+            if (!PAD || row < nh)
+                v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xs + row * (int64_t)d + 8 * c8));
+            else
+                v[j] = u32x4{0u, 0u, 0u, 0u};
         }
     };
     if (t < n_tiles) load_tile(t);  // the tile's loads overlap the W setup
 
     // setup: W -> LDS -> B operand in registers
+    if (!PAD) {  // 16-byte rows
 #pragma unroll
-    for (int j = 0; j < C::WVPT; ++j) {
-        const int q = j * C::NT + tid;
-        if (q < NH * C::WVPR) {
-            const int row = q / C::WVPR, c8 = q % C::WVPR;
-            *reinterpret_cast<u32x4*>(wl + row * C::WPITCH + 8 * c8) = reinterpret_cast<const u32x4*>(W)[q];
+        for (int j = 0; j < C::WVPT; ++j) {
+            const int q = j * C::NT + tid;
+            if (q < NH * C::WVPR) {
+                const int row = q / C::WVPR, c8 = q % C::WVPR;
+                *reinterpret_cast<u32x4*>(wl + row * C::WPITCH + 8 * c8) = reinterpret_cast<const u32x4*>(W)[q];
+            }
+        }
+    } else {  // element by element, zero outside [nh, nh]
+        for (int q = tid; q < NH * NH; q += C::NT) {
+            const int row = q / NH, col = q % NH;
+            wl[row * C::WPITCH + col] = (row < nh && col < nh) ? W[row * nh + col] : (uint16_t)0;
         }
     }
     __syncthreads();
@@ -804,11 +816,12 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
         __syncthreads();
 
         // store phase: whole rows of the part; pe pairs rotated here
-        uint16_t* outs = Out + s * NH * (int64_t)d + c_base;
+        uint16_t* outs = Out + s * nh * (int64_t)d + c_base;
 #pragma unroll
         for (int j = 0; j < C::VPT; ++j) {
             const int q = j * C::NT + tid;
             const int row = q / C::VPR, c8 = q % C::VPR;
+            if (PAD && row >= nh) continue;  // padding rows
             const int cl = 8 * c8, cg = c_base + cl;
             u32x4 o;
             if (cg < nope || paired) {
@@ -877,12 +890,14 @@ struct DwCfg {
     static_assert(VPO % NT == 0 && KS % WAVES == 0, "chunk shape");
 };
 
-template <int NH, int CH>
+template <int NH, int CH, bool PAD>
 __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
-    const int32_t* __restrict__ positions, int64_t sq, int nope, int pe,
+    const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe,
     float* __restrict__ partials, int tokens_per_block) {
+    // PAD: nh < NH, rows nh .. NH-1 are zero padding (not loaded) and only
+    // the [nh, nh] part of the partial is written; otherwise nh == NH
     using C = DwCfg<NH, CH>;
     // one array: dY chunk, then O chunk; reused at the end for the wave sums
     __shared__ __attribute__((aligned(16))) uint16_t lbuf[2 * NH * C::PITCH];
@@ -915,7 +930,7 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
     auto load_chunk = [&](int k) {
         const int64_t s = s_begin + k / cpt;
         const int part = k % cpt;
-        const int64_t rowbase = s * NH * (int64_t)d + part * CH;
+        const int64_t rowbase = s * nh * (int64_t)d + part * CH;
         if (pe > 0 && (part + 1) * CH > nope && tid < (h2 >> 2)) {  // before the chunk loads
             const int64_t prow = table_row(positions, s, table_rows);
             cv = reinterpret_cast<const f32x4*>(rcos + prow * h2)[tid];
@@ -928,7 +943,8 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
             const int rem = q % C::VPO;
             const int row = rem / C::VPR, c8 = rem % C::VPR;
             const uint16_t* src = (op == 0 ? dY : O) + rowbase + row * (int64_t)d + 8 * c8;
-            v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+            v[j] = (!PAD || row < nh) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src))
+                                      : u32x4{0u, 0u, 0u, 0u};
         }
     };
 
@@ -1009,7 +1025,7 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
         }
     }
 
-    float* part_out = partials + (int64_t)blockIdx.x * NH * NH;
+    float* part_out = partials + (int64_t)blockIdx.x * nh * nh;
     if constexpr (C::SPLIT_K) {
         // fixed-order sum of the four waves, (w0 + w2) + (w1 + w3), in the
         // chunk buffers (2 x TG x TH x 16 x 64 floats fit in dyl + ol)
@@ -1062,7 +1078,7 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int g = 32 * (gb0 + tg) + 8 * (r >> 2) + 4 * half + (r & 3);
-                part_out[g * NH + h] = acc[tg][th][r];
+                if (!PAD || (g < nh && h < nh)) part_out[g * nh + h] = acc[tg][th][r];
             }
         }
 }
@@ -1761,9 +1777,10 @@ static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
     const int cpt = d / CP;
     const int64_t n_tiles = a.sq * cpt;
     const size_t lds = C::lds_bytes(a.nope, a.pe);
-    auto kern = mix_part_kernel<NH, CP, WAVES, DX, NS>;
-    static bool attr_done = false;  // idempotent; a race only repeats the call
-    if (!attr_done) {
+    const bool pad = a.nh != NH;
+    auto kern = pad ? mix_part_kernel<NH, CP, WAVES, DX, NS, true> : mix_part_kernel<NH, CP, WAVES, DX, NS, false>;
+    static bool attr_done[2] = {false, false};  // idempotent; a race only repeats the call
+    if (!attr_done[pad]) {
         size_t lds_max = C::lds_bytes(8, CP);  // largest: pe = CP with the scratch
         if (lds_max > kMaxLds) lds_max = kMaxLds;  // shapes beyond it are not routed here
         if (lds_max > 65536) {
@@ -1771,24 +1788,28 @@ static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
             if (e != hipSuccess) return e;
         }
-        attr_done = true;
+        attr_done[pad] = true;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)n_tiles), dim3(64 * WAVES), lds, stream, a.X, a.W, a.rcos,
-                       a.rsin, a.table_rows, a.positions, a.nope, a.pe, cpt, n_tiles, a.Out);
+                       a.rsin, a.table_rows, a.positions, a.nh, a.nope, a.pe, cpt, n_tiles, a.Out);
     return hipGetLastError();
 }
 
+// Head rows of the token-part tile for nh heads: 32, 64 or 128 (padded with zeros).
+int mix_padded_heads(int nh) { return nh <= 32 ? 32 : (nh <= 64 ? 64 : 128); }
+
 // Channel-part width of the token-part kernel for this shape, or 0 when the
-// shape needs the general kernel: nh must be 32, 64 or 128, the part must
+// shape needs another kernel: 4 < nh <= 128 (padded to 32, 64 or 128), the part must
 // divide d, hold the whole pe range, fit the workgroup's LDS, and the grid
 // must stay below 2^31.
 int mix_part_width(int64_t sq, int nh, int nope, int pe) {
-    if (nh != 32 && nh != 64 && nh != 128) return 0;
+    if (nh <= SMALL_NH || nh > 128) return 0;
+    const int nhp = mix_padded_heads(nh);
     const int d = nope + pe;
     const int cands[2] = {256, 128};
     for (int cp : cands) {
         if (d % cp != 0 || pe > cp) continue;
-        if (nh == 128 && cp == 256 && PartCfg<128, 256, 8, 4>::lds_bytes(nope, pe) > kMaxLds) continue;
+        if (nhp == 128 && cp == 256 && PartCfg<128, 256, 8, 4>::lds_bytes(nope, pe) > kMaxLds) continue;
         if (sq * (int64_t)(d / cp) >= ((int64_t)1 << 31)) return 0;
         return cp;
     }
@@ -1797,15 +1818,16 @@ int mix_part_width(int64_t sq, int nh, int nope, int pe) {
 
 template <bool DX>
 static hipError_t launch_mix_dx(const MixArgs& a, hipStream_t stream) {
-    // the tiled kernels read W with 16-byte loads
     const bool w16 = ((uintptr_t)a.W & 15u) == 0;
-    const int cp = (a.force_general || !w16) ? 0 : mix_part_width(a.sq, a.nh, a.nope, a.pe);
-    if (cp == 256 && a.nh == 64) return launch_part_t<64, 256, 8, DX>(a, stream);
-    if (cp == 128 && a.nh == 64) return launch_part_t<64, 128, 4, DX>(a, stream);
-    if (cp == 256 && a.nh == 32) return launch_part_t<32, 256, 8, DX>(a, stream);
-    if (cp == 128 && a.nh == 32) return launch_part_t<32, 128, 4, DX>(a, stream);
-    if (cp == 256 && a.nh == 128) return launch_part_t<128, 256, 8, DX, 4>(a, stream);  // N split in 4
-    if (cp == 128 && a.nh == 128) return launch_part_t<128, 128, 8, DX, 4>(a, stream);
+    // the tiled kernels read W with 16-byte loads when nh fills the padded rows exactly
+    const int nhp = mix_padded_heads(a.nh);
+    const int cp = (a.force_general || (!w16 && a.nh == nhp)) ? 0 : mix_part_width(a.sq, a.nh, a.nope, a.pe);
+    if (cp == 256 && nhp == 64) return launch_part_t<64, 256, 8, DX>(a, stream);
+    if (cp == 128 && nhp == 64) return launch_part_t<64, 128, 4, DX>(a, stream);
+    if (cp == 256 && nhp == 32) return launch_part_t<32, 256, 8, DX>(a, stream);
+    if (cp == 128 && nhp == 32) return launch_part_t<32, 128, 4, DX>(a, stream);
+    if (cp == 256 && nhp == 128) return launch_part_t<128, 256, 8, DX, 4>(a, stream);  // N split in 4
+    if (cp == 128 && nhp == 128) return launch_part_t<128, 128, 8, DX, 4>(a, stream);
     if (!a.force_general && a.nh <= SMALL_NH) {
         const int vpr = (a.nope + a.pe) / 8;
         const int tok = vpr >= 512 ? 1 : 512 / vpr;
@@ -1861,7 +1883,7 @@ int64_t bwd_fused_num_blocks(int64_t sq, int nh) {
 
 // Chunk width of the LDS-staged weight-gradient kernel, or 0 for the direct kernel.
 int dw_chunk_width(int nh, int nope, int pe) {
-    if (nh != 32 && nh != 64 && nh != 128) return 0;
+    if (nh <= SMALL_NH || nh > 128) return 0;  // padded to 32, 64 or 128 rows
     const int d = nope + pe;
     return (d % 128 == 0 && pe <= 128) ? 128 : 0;
 }
@@ -1874,11 +1896,11 @@ static hipError_t launch_dw_t(const DwArgs& a, hipStream_t stream) {
     if (!a.force_general && a.nh <= SMALL_NH) {
         hipLaunchKernelGGL(small_dw_kernel, dim3((unsigned)nb), dim3(256), 0, stream, a.dY, a.O, a.rcos,
                            a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, tpb, a.partials);
-    } else if (ch == 128 && a.nh == NHP && (NHP == 32 || NHP == 64 || NHP == 128)) {
-        hipLaunchKernelGGL((dw_chunk_kernel<(NHP < 32 ? 32 : NHP), 128>), dim3((unsigned)nb),
-                           dim3(DwCfg<(NHP < 32 ? 32 : NHP), 128>::NT), 0,
-                           stream, a.dY, a.O, a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nope,
-                           a.pe, a.partials, tpb);
+    } else if (ch == 128 && mix_padded_heads(a.nh) == (NHP < 32 ? 32 : NHP)) {
+        constexpr int NHC = NHP < 32 ? 32 : NHP;
+        auto kern = a.nh != NHC ? dw_chunk_kernel<NHC, 128, true> : dw_chunk_kernel<NHC, 128, false>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(DwCfg<NHC, 128>::NT), 0, stream, a.dY, a.O, a.rcos,
+                           a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, a.partials, tpb);
     } else {
         hipLaunchKernelGGL((dw_partial_kernel<NHP>), dim3((unsigned)nb), dim3(256), 0, stream, a.dY,
                            a.O, a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe,
