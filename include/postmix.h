@@ -40,8 +40,9 @@
  *  - Limits: 1 <= nh <= 128; nope >= 0 with nope % 8 == 0; pe >= 0 with
  *    pe % 16 == 0; nope + pe > 0; sq >= 0.  sq == 0 is a successful no-op.
  *  - Activation, table and workspace pointers must be 16-byte aligned; W must
- *    be 2-byte aligned (the tiled kernels, which read W in 16-byte vectors,
- *    are used only when W is 16-byte aligned).
+ *    be 2-byte aligned (for nh of 32, 64 or 128 the tiled kernels read W in
+ *    16-byte vectors and are used only when W is 16-byte aligned; other head
+ *    counts read W element by element).
  *  - Return 0 on success, else a negative PM_ERR_* code; a thread-local
  *    message naming the offending argument is available from
  *    postmix_last_error().  Arguments are validated before any HIP call.
@@ -134,8 +135,8 @@ int postmix_bwd_dw(const pm_bf16 *dY, const pm_bf16 *O, const float *rope_cos,
 /*
  * Backward, both gradients in one call: dO as postmix_bwd_dx and dW as
  * postmix_bwd_dw, from a single pass over dY and O where the shape allows
- * (nope + pe a multiple of 128, pe <= 128, and nh == 64, or nh == 128 with pe
- * and nope multiples of 32): each (token, channel
+ * (nope + pe a multiple of 128, pe <= 128, and 32 < nh <= 64, or
+ * 64 < nh <= 128 with pe and nope multiples of 32): each (token, channel
  * chunk) of dY and O is read from HBM once and feeds both the head-mix
  * gradient and the weight-gradient partials.  That is one full read of dY
  * fewer than the two separate calls.  Other shapes (or

@@ -1141,12 +1141,14 @@ struct BwdCfg {
     }
 };
 
-template <int NH, int CH, int WAVES>
+template <int NH, int CH, int WAVES, bool PAD>
 __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O, const uint16_t* __restrict__ W,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
-    const int32_t* __restrict__ positions, int64_t sq, int nope, int pe,
+    const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe,
     uint16_t* __restrict__ dO, float* __restrict__ partials, int tokens_per_block) {
+    // PAD: nh < NH, head rows nh .. NH-1 are zero padding (never loaded or
+    // stored; only the [nh, nh] part of the partial is written); otherwise nh == NH
     using C = BwdCfg<NH, CH, WAVES>;
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint16_t* dyl = smem;                               // [NH][PITCH]
@@ -1189,7 +1191,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     auto load_chunk = [&](int k) {
         const int64_t s = s_begin + k / cpt;
         const int part = k % cpt;
-        const int64_t rowbase = s * NH * (int64_t)d + part * CH;
+        const int64_t rowbase = s * nh * (int64_t)d + part * CH;
 #pragma unroll
         for (int j = 0; j < C::VPT; ++j) {
             const int q = j * C::NT + tid;
@@ -1197,7 +1199,8 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             const int rem = q % C::VPO;
             const int row = rem / C::VPR, c8 = rem % C::VPR;
             const uint16_t* src = (op == 0 ? dY : O) + rowbase + row * (int64_t)d + 8 * c8;
-            v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+            v[j] = (!PAD || row < nh) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src))
+                                      : u32x4{0u, 0u, 0u, 0u};
         }
     };
     auto stage_chunk = [&]() {  // registers of the next chunk -> LDS
@@ -1214,9 +1217,16 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     if (pe > 0 && nchunks > 0) load_rope_group(s_begin);
 
     // W -> LDS -> this wave's dx B operand (B[k=g][n=h] = W[g][h], N-block nb)
-    for (int q = tid; q < NH * NH / 8; q += C::NT) {
-        const int row = q / (NH / 8), c8 = q % (NH / 8);
-        *reinterpret_cast<u32x4*>(wl + row * C::WPITCH + 8 * c8) = reinterpret_cast<const u32x4*>(W)[q];
+    if (!PAD) {
+        for (int q = tid; q < NH * NH / 8; q += C::NT) {
+            const int row = q / (NH / 8), c8 = q % (NH / 8);
+            *reinterpret_cast<u32x4*>(wl + row * C::WPITCH + 8 * c8) = reinterpret_cast<const u32x4*>(W)[q];
+        }
+    } else {
+        for (int q = tid; q < NH * NH; q += C::NT) {
+            const int row = q / NH, col = q % NH;
+            wl[row * C::WPITCH + col] = (row < nh && col < nh) ? W[row * nh + col] : (uint16_t)0;
+        }
     }
     __syncthreads();
     bf16x8 wf[C::WRES ? 1 : C::KB];  // W fragments in registers, or read from LDS per use
@@ -1329,11 +1339,12 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         }
 
         // ---- dO rows of the chunk; pe pairs turned by +phi
-        uint16_t* outs = dO + s * NH * (int64_t)d + c_base;
+        uint16_t* outs = dO + s * nh * (int64_t)d + c_base;
 #pragma unroll
         for (int j = 0; j < C::OPT; ++j) {
             const int q = j * C::NT + tid;
             const int row = q / C::VPR, c8 = q % C::VPR;
+            if (PAD && row >= nh) continue;  // padding rows
             const int cl = 8 * c8, cg = c_base + cl;
             u32x4 o;
             if (cg < nope || paired) {
@@ -1382,12 +1393,12 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     for (int k = 1; k < C::KSET; ++k)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_w[r] += red[(((k - 1) * C::NTILE + tile) * 16 + r) * 64 + lane];
-    float* part_out = partials + (int64_t)blockIdx.x * NH * NH;
+    float* part_out = partials + (int64_t)blockIdx.x * nh * nh;
     const int h = 32 * hb + (lane & 31);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int g = 32 * gb + 8 * (r >> 2) + 4 * half + (r & 3);
-        part_out[g * NH + h] = acc_w[r];
+        if (!PAD || (g < nh && h < nh)) part_out[g * nh + h] = acc_w[r];
     }
 }
 
@@ -1918,7 +1929,8 @@ static hipError_t launch_dw_t(const DwArgs& a, hipStream_t stream) {
 bool bwd_fused_applies(int nh, int nope, int pe) {
     const int d = nope + pe;
     if (d % 128 != 0 || pe > 128) return false;
-    return nh == 64 || (nh == 128 && (pe == 0 || pe_pairs_in_blocks(nope, pe)));
+    // head rows padded to 64 (32 < nh <= 64) or to 128 (pe rotated in registers only)
+    return (nh > 32 && nh <= 64) || (nh > 64 && nh <= 128 && (pe == 0 || pe_pairs_in_blocks(nope, pe)));
 }
 
 // chunk width of the fused backward: 256 channels (16 waves) where d allows
@@ -1927,19 +1939,21 @@ static int bwd_fused_chunk(int d) { return d % 256 == 0 ? 256 : 128; }
 template <int NH, int CH, int WAVES>
 static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int tpb, int64_t nb, hipStream_t stream) {
     using C = BwdCfg<NH, CH, WAVES>;
-    auto kern = bwd_fused_kernel<NH, CH, WAVES>;
-    static bool attr_done = false;  // idempotent; a race only repeats the call
-    if (!attr_done) {
+    const bool pad = a.nh != NH;
+    auto kern = pad ? bwd_fused_kernel<NH, CH, WAVES, true> : bwd_fused_kernel<NH, CH, WAVES, false>;
+    static bool attr_done[2] = {false, false};  // idempotent; a race only repeats the call
+    if (!attr_done[pad]) {
         size_t lds_max = C::lds_bytes(8, 128);  // largest: pe = 128 with the scratch
         if (lds_max > kMaxLds) lds_max = kMaxLds;
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)lds_max);
         if (e != hipSuccess) return e;
-        attr_done = true;
+        attr_done[pad] = true;
     }
     if (C::lds_bytes(a.nope, a.pe) > kMaxLds) return hipErrorInvalidValue;  // excluded by bwd_fused_applies
     hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), C::lds_bytes(a.nope, a.pe), stream, a.dY, a.O, mx.W,
-                       a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nope, a.pe, mx.Out, a.partials, tpb);
+                       a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, mx.Out, a.partials,
+                       tpb);
     return hipGetLastError();
 }
 
@@ -1947,7 +1961,7 @@ hipError_t launch_bwd_fused(const MixArgs& mx, const DwArgs& a, hipStream_t stre
     const int tpb = bwd_fused_tokens_per_block(a.sq, a.nh);
     const int64_t nb = bwd_fused_num_blocks(a.sq, a.nh);
     hipError_t err;
-    if (a.nh == 128)
+    if (a.nh > 64)
         err = launch_bwd_fused_t<128, 128, 16>(mx, a, tpb, nb, stream);
     else
         err = bwd_fused_chunk(a.nope + a.pe) == 256 ? launch_bwd_fused_t<64, 256, 16>(mx, a, tpb, nb, stream)

@@ -186,6 +186,10 @@ def test_tiled_and_general_kernels_agree(sq, nh, nope, pe):
     (9, 128, 192, 64, 3),       # fused path, nh = 128, d = 256
     (7, 128, 384, 128, 11),     # fused path, nh = 128, pe = 128
     (5, 128, 432, 80, 2),       # not fused (nh = 128 with pe = 80): separate kernels
+    (11, 48, 448, 64, 3),       # fused path, nh = 48 (head rows padded to 64)
+    (9, 33, 192, 64, 1),        # fused path, nh = 33, d = 256
+    (7, 96, 448, 64, 5),        # fused path, nh = 96 (head rows padded to 128)
+    (6, 100, 432, 80, 9),       # not fused (padded to 128 with pe = 80): separate kernels
     (21, 32, 448, 64, 5),       # not fused (nh = 32): separate kernels
     (9, 3, 448, 64, 0),         # not fused (nh = 3)
 ])
