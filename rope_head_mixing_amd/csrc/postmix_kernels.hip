@@ -723,10 +723,23 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
                 *reinterpret_cast<u32x4*>(wl + row * C::WPITCH + 8 * c8) = reinterpret_cast<const u32x4*>(W)[q];
             }
         }
-    } else {  // element by element, zero outside [nh, nh]
-        for (int q = tid; q < NH * NH; q += C::NT) {
-            const int row = q / NH, col = q % NH;
-            wl[row * C::WPITCH + col] = (row < nh && col < nh) ? W[row * nh + col] : (uint16_t)0;
+    } else {  // zero the padded rows, then scatter W's nh*nh elements (16-byte loads when aligned)
+        for (int q = tid; q < NH * C::WPITCH / 8; q += C::NT) reinterpret_cast<u32x4*>(wl)[q] = u32x4{0u, 0u, 0u, 0u};
+        __syncthreads();
+        const int n = nh * nh;
+        const int nvec = ((uintptr_t)W & 15u) == 0 ? n / 8 : 0;
+        for (int q = tid; q < nvec; q += C::NT) {
+            const u32x4 x = reinterpret_cast<const u32x4*>(W)[q];
+            int row = (8 * q) / nh, col = 8 * q - row * nh;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                wl[row * C::WPITCH + col] = (uint16_t)(x[e >> 1] >> (16 * (e & 1)));
+                if (++col == nh) { col = 0; ++row; }
+            }
+        }
+        for (int idx = 8 * nvec + tid; idx < n; idx += C::NT) {
+            const int row = idx / nh;
+            wl[row * C::WPITCH + (idx - row * nh)] = W[idx];
         }
     }
     __syncthreads();
@@ -1809,6 +1822,10 @@ static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
 // Head rows of the token-part tile for nh heads: 32, 64 or 128 (padded with zeros).
 int mix_padded_heads(int nh) { return nh <= 32 ? 32 : (nh <= 64 ? 64 : 128); }
 
+// Head rows of the forward/dx tile: also 96 (three 32-head N-blocks, split over
+// 3 wave groups of 2 waves)
+static int mix_tile_heads(int nh) { return nh <= 64 ? mix_padded_heads(nh) : (nh <= 96 ? 96 : 128); }
+
 // Channel-part width of the token-part kernel for this shape, or 0 when the
 // shape needs another kernel: 4 < nh <= 128 (padded to 32, 64 or 128), the part must
 // divide d, hold the whole pe range, fit the workgroup's LDS, and the grid
@@ -1831,12 +1848,14 @@ template <bool DX>
 static hipError_t launch_mix_dx(const MixArgs& a, hipStream_t stream) {
     const bool w16 = ((uintptr_t)a.W & 15u) == 0;
     // the tiled kernels read W with 16-byte loads when nh fills the padded rows exactly
-    const int nhp = mix_padded_heads(a.nh);
+    const int nhp = mix_tile_heads(a.nh);
     const int cp = (a.force_general || (!w16 && a.nh == nhp)) ? 0 : mix_part_width(a.sq, a.nh, a.nope, a.pe);
     if (cp == 256 && nhp == 64) return launch_part_t<64, 256, 8, DX>(a, stream);
     if (cp == 128 && nhp == 64) return launch_part_t<64, 128, 4, DX>(a, stream);
     if (cp == 256 && nhp == 32) return launch_part_t<32, 256, 8, DX>(a, stream);
     if (cp == 128 && nhp == 32) return launch_part_t<32, 128, 4, DX>(a, stream);
+    if (cp == 256 && nhp == 96) return launch_part_t<96, 256, 6, DX, 3>(a, stream);   // N split in 3
+    if (cp == 128 && nhp == 96) return launch_part_t<96, 128, 6, DX, 3>(a, stream);
     if (cp == 256 && nhp == 128) return launch_part_t<128, 256, 8, DX, 4>(a, stream);  // N split in 4
     if (cp == 128 && nhp == 128) return launch_part_t<128, 128, 8, DX, 4>(a, stream);
     if (!a.force_general && a.nh <= SMALL_NH) {

@@ -144,6 +144,11 @@ def kernel_policy(request):
     (8, 64, 464, 48, 21),      # nope % 32 != 0: pe rotated through the fp32 scratch
     (7, 128, 320, 64, 9),      # nh = 128, d = 384: 128-channel parts, heads split over wave groups
     (3, 128, 16, 240, 5),      # nh = 128 with an fp32 scratch too large for the LDS: general kernel
+    (13, 20, 448, 64, 7),      # nh = 20: head rows padded to 32
+    (5, 7, 448, 64, 2),        # nh = 7: padded to 32
+    (9, 80, 448, 64, 3),       # nh = 80: padded to 96 (three wave groups)
+    (7, 72, 192, 64, 11),      # nh = 72, d = 256: padded to 96
+    (6, 96, 448, 64, 4000),    # nh = 96: 96-row tiles
 ])
 def test_small_shapes(sq, nh, nope, pe, off, kernel_policy):
     full_check(synthetic.case(sq, nh, nope, pe, seed=1000 + sq + nh, pos_offset=off))
@@ -255,13 +260,14 @@ def test_out_of_range_positions_are_clamped_not_read_out_of_bounds():
     gu.check_bf16(gu.host_bits(Y), ref, "clamped positions")
 
 
-def test_unaligned_W_takes_the_general_path():
-    """W that is 2-byte but not 16-byte aligned: same results as an aligned copy."""
+@pytest.mark.parametrize("nh", [64, 20])  # general kernels; padded tiles reading W element-wise
+def test_unaligned_W(nh):
+    """W that is 2-byte but not 16-byte aligned: results on the oracle."""
     import torch
-    c = synthetic.case(29, 64, 448, 64, seed=909, pos_offset=300)
+    c = synthetic.case(29, nh, 448, 64, seed=909, pos_offset=300)
     dv = Dev(c)
-    store = torch.empty(64 * 64 + 1, dtype=torch.bfloat16, device="cuda")
-    Wv = store[1:].view(64, 64)
+    store = torch.empty(nh * nh + 1, dtype=torch.bfloat16, device="cuda")
+    Wv = store[1:].view(nh, nh)
     Wv.copy_(dv.dW_)
     assert Wv.data_ptr() % 16 == 2
     Y = P().postmix_fwd(dv.dO_, Wv, dv.cos, dv.sin, dv.dpos, c.nope, c.pe)
