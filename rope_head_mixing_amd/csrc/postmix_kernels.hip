@@ -597,10 +597,17 @@ struct PartCfg {
     __host__ __device__ static size_t aux_bytes(int nope, int pe) {
         return pe_pairs_in_blocks(nope, pe) ? 0 : (size_t)NH * (pe + 4) * 4;
     }
-    // tile (W is staged there first), then the pe scratch, then this tile's
-    // cos and sin rows (pe/2 floats each)
-    __host__ __device__ static size_t lds_bytes(int nope, int pe) {
-        return (size_t)NH * PITCH * 2 + aux_bytes(nope, pe) + (size_t)pe * 4;
+    // tile (W is staged there first), then the pe scratch, then the cos and
+    // sin rows (pe/2 floats each) of the tile's tp tokens
+    __host__ __device__ static size_t lds_bytes(int nope, int pe, int tp = 1) {
+        return (size_t)NH * PITCH * 2 + aux_bytes(nope, pe) + (size_t)tp * pe * 4;
+    }
+    // tokens per tile for nh < NH heads: as many as fill the rows, while each
+    // cos/sin quad of every token has a thread to load it
+    __host__ __device__ static int tokens_per_tile(int nh, int pe) {
+        int tp = NH / nh;
+        if (pe > 0 && tp * (pe / 4) > NT) tp = NT / (pe / 4);
+        return tp < 1 ? 1 : tp;
     }
 };
 
@@ -672,18 +679,23 @@ template <int NH, int CP, int WAVES, bool DX, int NS, bool PAD>
 __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
-    const int32_t* __restrict__ positions, int nh, int nope, int pe, int cpt, int64_t n_tiles,
-    uint16_t* __restrict__ Out) {
-    // PAD: nh < NH, rows nh .. NH-1 of the tile and of W are zero padding
-    // (never loaded from or stored to HBM); otherwise nh == NH
+    const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe, int cpt, int ptok,
+    int64_t n_tiles, uint16_t* __restrict__ Out) {
+    // PAD: nh < NH.  A tile then holds ptok consecutive tokens (their ptok*nh
+    // head rows are consecutive rows of the [sq*nh, d] array) and W is staged
+    // block-diagonally, one copy per token; rows beyond the tokens' rows are
+    // zero padding, never loaded from or stored to HBM.  Otherwise nh == NH
+    // and ptok == 1.
+    const int tp = PAD ? ptok : 1;
     using C = PartCfg<NH, CP, WAVES, NS>;
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint16_t* tile = smem;                                   // [NH][PITCH] bf16
     uint16_t* wl = smem;                                     // [NH][WPITCH] bf16 first, in the tile's place
     float* pes = reinterpret_cast<float*>(smem + NH * C::PITCH);  // [NH][pe + 4] fp32 (unpaired pe)
     const int pes_pitch = pe + 4;
-    float* csl = reinterpret_cast<float*>(reinterpret_cast<char*>(pes) + C::aux_bytes(nope, pe));  // [pe/2]
-    float* snl = csl + (pe >> 1);                                                                   // [pe/2]
+    // cos and sin rows of the tile's tokens: [tp][pe] floats (cos then sin)
+    float* csl = reinterpret_cast<float*>(reinterpret_cast<char*>(pes) + C::aux_bytes(nope, pe));
+    float* snl = csl + (pe >> 1);
 
     const int d = nope + pe;
     const int h2 = pe >> 1;
@@ -691,21 +703,29 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
 
     int64_t t = blockIdx.x;
     u32x4 v[C::VPT];
-    f32x4 rope_v = {0.f, 0.f, 0.f, 0.f};  // cos (tid < pe/8) or sin (pe/8 <= tid < pe/4) of this tile
+    // thread tid < tp*pe/4 carries quad tid%(pe/4) of token tid/(pe/4)'s cos
+    // (first pe/8 quads) or sin row
+    f32x4 rope_v = {0.f, 0.f, 0.f, 0.f};
+    int rows_valid = NH;  // head rows of this tile backed by tokens < sq
     auto load_tile = [&](int64_t tt) {
-        const int64_t s = tt / cpt;
-        const int part = (int)(tt - s * cpt);
-        const uint16_t* xs = X + s * nh * (int64_t)d + part * CP;
-        if (pe > 0 && (part + 1) * CP > nope && tid < (pe >> 2)) {
-            const int64_t prow = table_row(positions, s, table_rows);
-            const int q4 = tid % (pe >> 3);
-            rope_v = reinterpret_cast<const f32x4*>((tid < (pe >> 3) ? rcos : rsin) + prow * h2)[q4];
+        const int64_t grp = tt / cpt;
+        const int part = (int)(tt - grp * cpt);
+        const int64_t s0 = grp * tp;
+        const int64_t ntok = sq - s0 < tp ? sq - s0 : tp;
+        rows_valid = PAD ? (int)ntok * nh : NH;
+        const uint16_t* xs = X + s0 * nh * (int64_t)d + part * CP;
+        const int q4n = pe >> 2;
+        if (pe > 0 && (part + 1) * CP > nope && tid < (int)ntok * q4n) {
+            const int p = tid / q4n, q = tid - p * q4n;
+            const int64_t prow = table_row(positions, s0 + p, table_rows);
+            const int half4 = pe >> 3;
+            rope_v = reinterpret_cast<const f32x4*>((q < half4 ? rcos : rsin) + prow * h2)[q < half4 ? q : q - half4];
         }
 #pragma unroll
         for (int j = 0; j < C::VPT; ++j) {
             const int q = j * C::NT + tid;
             const int row = q / C::VPR, c8 = q % C::VPR;
-            if (!PAD || row < nh)
+            if (!PAD || row < rows_valid)
                 v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xs + row * (int64_t)d + 8 * c8));
             else
                 v[j] = u32x4{0u, 0u, 0u, 0u};
@@ -728,18 +748,21 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
         __syncthreads();
         const int n = nh * nh;
         const int nvec = ((uintptr_t)W & 15u) == 0 ? n / 8 : 0;
+        const int bd = nh * (C::WPITCH + 1);  // one block-diagonal step: nh rows and nh columns
         for (int q = tid; q < nvec; q += C::NT) {
             const u32x4 x = reinterpret_cast<const u32x4*>(W)[q];
             int row = (8 * q) / nh, col = 8 * q - row * nh;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                wl[row * C::WPITCH + col] = (uint16_t)(x[e >> 1] >> (16 * (e & 1)));
+                const uint16_t w = (uint16_t)(x[e >> 1] >> (16 * (e & 1)));
+                for (int p = 0; p < tp; ++p) wl[p * bd + row * C::WPITCH + col] = w;
                 if (++col == nh) { col = 0; ++row; }
             }
         }
         for (int idx = 8 * nvec + tid; idx < n; idx += C::NT) {
             const int row = idx / nh;
-            wl[row * C::WPITCH + (idx - row * nh)] = W[idx];
+            const uint16_t w = W[idx];
+            for (int p = 0; p < tp; ++p) wl[p * bd + row * C::WPITCH + (idx - row * nh)] = w;
         }
     }
     __syncthreads();
@@ -761,8 +784,9 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
 
     const int Q = lane >> 5;
     if (t < n_tiles) {
-        const int64_t s = t / cpt;
-        const int part = (int)(t - s * cpt);
+        const int64_t grp = t / cpt;
+        const int part = (int)(t - grp * cpt);
+        const int64_t s0 = grp * tp;  // first token of the tile
         const int c_base = part * CP;
 
 #pragma unroll
@@ -772,7 +796,7 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
             *reinterpret_cast<u32x4*>(tile + row * C::PITCH + 8 * c8) = v[j];
         }
         const bool tile_pe = pe > 0 && c_base + CP > nope;
-        if (tile_pe && tid < (pe >> 2)) reinterpret_cast<f32x4*>(csl)[tid] = rope_v;  // cos then sin
+        if (tile_pe && tid < tp * (pe >> 2)) reinterpret_cast<f32x4*>(csl)[tid] = rope_v;  // [tp][cos, sin]
         __syncthreads();
         const bool paired = tile_pe && pe_pairs_in_blocks(nope, pe);
         const int L = nope - c_base;  // local index of the first pe channel (tiles with pe)
@@ -800,9 +824,13 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
             if (NS > 1) __syncthreads();
             if (pb) {
 #pragma unroll
-                for (int j = 0; j < C::NBW; ++j)
-                    rotate_paired_block(acc[j], tile, C::PITCH, 32 * (ng * C::NBW + j) + (lane & 31), L, h2, q, Q,
-                                        csl, snl, DX ? -1.0f : 1.0f);
+                for (int j = 0; j < C::NBW; ++j) {
+                    const int g = 32 * (ng * C::NBW + j) + (lane & 31);
+                    int p = PAD ? g / nh : 0;  // the row's token within the tile
+                    p = p < tp ? p : tp - 1;   // (padding rows: any staged row)
+                    rotate_paired_block(acc[j], tile, C::PITCH, g, L, h2, q, Q, csl + p * pe, snl + p * pe,
+                                        DX ? -1.0f : 1.0f);
+                }
                 continue;
             }
             // D register r of lane half Q: channel 32b + 8(r/4) + 4Q + r%4, head 32nb + lane%32
@@ -829,12 +857,12 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
         __syncthreads();
 
         // store phase: whole rows of the part; pe pairs rotated here
-        uint16_t* outs = Out + s * nh * (int64_t)d + c_base;
+        uint16_t* outs = Out + s0 * nh * (int64_t)d + c_base;
 #pragma unroll
         for (int j = 0; j < C::VPT; ++j) {
             const int q = j * C::NT + tid;
             const int row = q / C::VPR, c8 = q % C::VPR;
-            if (PAD && row >= nh) continue;  // padding rows
+            if (PAD && row >= rows_valid) continue;  // padding rows
             const int cl = 8 * c8, cg = c_base + cl;
             u32x4 o;
             if (cg < nope || paired) {
@@ -845,20 +873,21 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
                 const int ii = first ? i : i - h2;
                 const float* own = pes + row * pes_pitch + i;
                 const float* par = pes + row * pes_pitch + (first ? i + h2 : i - h2);
+                const int rp = PAD ? (row / nh) * pe : 0;  // the row's token's cos/sin
                 const f32x4 o0 = reinterpret_cast<const f32x4*>(own)[0], o1 = reinterpret_cast<const f32x4*>(own)[1];
                 const f32x4 p0 = reinterpret_cast<const f32x4*>(par)[0], p1 = reinterpret_cast<const f32x4*>(par)[1];
-                const f32x4 c0 = reinterpret_cast<const f32x4*>(csl + ii)[0];
-                const f32x4 c1 = reinterpret_cast<const f32x4*>(csl + ii)[1];
-                const f32x4 s0 = reinterpret_cast<const f32x4*>(snl + ii)[0];
-                const f32x4 s1 = reinterpret_cast<const f32x4*>(snl + ii)[1];
+                const f32x4 c0 = reinterpret_cast<const f32x4*>(csl + rp + ii)[0];
+                const f32x4 c1 = reinterpret_cast<const f32x4*>(csl + rp + ii)[1];
+                const f32x4 sn0 = reinterpret_cast<const f32x4*>(snl + rp + ii)[0];
+                const f32x4 sn1 = reinterpret_cast<const f32x4*>(snl + rp + ii)[1];
                 // forward (turn by -phi): first half  a C + b S, second half b C - a S
                 // dx      (turn by +phi): first half  a C - b S, second half b C + a S
                 const float sg = (first != DX) ? 1.0f : -1.0f;
                 float y[8];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    y[e] = o0[e] * c0[e] + sg * (p0[e] * s0[e]);
-                    y[4 + e] = o1[e] * c1[e] + sg * (p1[e] * s1[e]);
+                    y[e] = o0[e] * c0[e] + sg * (p0[e] * sn0[e]);
+                    y[4 + e] = o1[e] * c1[e] + sg * (p1[e] * sn1[e]);
                 }
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) o[jj] = pack_bf16(y[2 * jj], y[2 * jj + 1]);
@@ -908,16 +937,22 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
     const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe,
-    float* __restrict__ partials, int tokens_per_block) {
-    // PAD: nh < NH, rows nh .. NH-1 are zero padding (not loaded) and only
-    // the [nh, nh] part of the partial is written; otherwise nh == NH
+    float* __restrict__ partials, int tokens_per_block, int ptok) {
+    // PAD: nh < NH.  A chunk then holds ptok consecutive tokens (ptok*nh
+    // consecutive rows of the [sq*nh, d] arrays), the rest of its rows are
+    // zero padding (not loaded), and the partial is the sum of the ptok
+    // diagonal [nh, nh] blocks of the chunk products; otherwise nh == NH and
+    // ptok == 1.
     using C = DwCfg<NH, CH>;
+    const int tp = PAD ? ptok : 1;
+    // cos and sin rows of the chunk's tokens: [tp][pe/2] each
+    constexpr int CSN = PAD ? 4 * C::NT : C::MAX_H2;
     // one array: dY chunk, then O chunk; reused at the end for the wave sums
     __shared__ __attribute__((aligned(16))) uint16_t lbuf[2 * NH * C::PITCH];
     uint16_t* const dyl = lbuf;
     uint16_t* const ol = lbuf + NH * C::PITCH;
-    __shared__ __attribute__((aligned(16))) float csl[C::MAX_H2];
-    __shared__ __attribute__((aligned(16))) float snl[C::MAX_H2];
+    __shared__ __attribute__((aligned(16))) float csl[CSN];
+    __shared__ __attribute__((aligned(16))) float snl[CSN];
 
     const int d = nope + pe, h2 = pe >> 1;
     const int cpt = d / CH;
@@ -928,7 +963,7 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
     const int64_t s_begin = (int64_t)blockIdx.x * tokens_per_block;
     int64_t s_end = s_begin + tokens_per_block;
     if (s_end > sq) s_end = sq;
-    const int nchunks = (int)(s_end - s_begin) * cpt;
+    const int nchunks = (int)((s_end - s_begin + tp - 1) / tp) * cpt;
 
     f32x16 acc[C::TG][C::TH];
 #pragma unroll
@@ -941,13 +976,17 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
     u32x4 v[C::VPT];
     f32x4 cv = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
     auto load_chunk = [&](int k) {
-        const int64_t s = s_begin + k / cpt;
+        const int64_t s = s_begin + (int64_t)(k / cpt) * tp;  // first token of the chunk
         const int part = k % cpt;
+        const int ntok = (int)(s_end - s < tp ? s_end - s : tp);
+        const int rows_valid = PAD ? ntok * nh : NH;
         const int64_t rowbase = s * nh * (int64_t)d + part * CH;
-        if (pe > 0 && (part + 1) * CH > nope && tid < (h2 >> 2)) {  // before the chunk loads
-            const int64_t prow = table_row(positions, s, table_rows);
-            cv = reinterpret_cast<const f32x4*>(rcos + prow * h2)[tid];
-            sv = reinterpret_cast<const f32x4*>(rsin + prow * h2)[tid];
+        const int q4n = h2 >> 2;
+        if (pe > 0 && (part + 1) * CH > nope && tid < ntok * q4n) {  // before the chunk loads
+            const int p = tid / q4n, q = tid - p * q4n;
+            const int64_t prow = table_row(positions, s + p, table_rows);
+            cv = reinterpret_cast<const f32x4*>(rcos + prow * h2)[q];
+            sv = reinterpret_cast<const f32x4*>(rsin + prow * h2)[q];
         }
 #pragma unroll
         for (int j = 0; j < C::VPT; ++j) {
@@ -956,7 +995,7 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
             const int rem = q % C::VPO;
             const int row = rem / C::VPR, c8 = rem % C::VPR;
             const uint16_t* src = (op == 0 ? dY : O) + rowbase + row * (int64_t)d + 8 * c8;
-            v[j] = (!PAD || row < nh) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src))
+            v[j] = (!PAD || row < rows_valid) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src))
                                       : u32x4{0u, 0u, 0u, 0u};
         }
     };
@@ -974,7 +1013,7 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
             *reinterpret_cast<u32x4*>((op == 0 ? dyl : ol) + row * C::PITCH + 8 * c8) = v[j];
         }
         const bool chunk_pe = pe > 0 && (part + 1) * CH > nope;
-        if (chunk_pe && tid < (h2 >> 2)) {
+        if (chunk_pe && tid < tp * (h2 >> 2)) {
             reinterpret_cast<f32x4*>(csl)[tid] = cv;
             reinterpret_cast<f32x4*>(snl)[tid] = sv;
         }
@@ -1006,7 +1045,7 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
                 const int cpart = first ? c + h2 : c - h2;
                 const float sgn = first ? 1.0f : -1.0f;
                 float cs[8], sn[8];
-                if (pe_grp) {
+                if (pe_grp && !PAD) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         cs[e] = csl[i0 + e];
@@ -1018,6 +1057,15 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
                     const int h = 32 * (hb0 + th) + (lane & 31);
                     const u32x4 own = *reinterpret_cast<const u32x4*>(ol + h * C::PITCH + c);
                     u32x4 hi = own, lo = {0u, 0u, 0u, 0u};
+                    if (pe_grp && PAD) {  // the angles of row h's token
+                        int p = h / nh;
+                        p = p < tp ? p : tp - 1;  // (padding rows: any staged row)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            cs[e] = csl[p * h2 + i0 + e];
+                            sn[e] = sgn * snl[p * h2 + i0 + e];
+                        }
+                    }
                     if (pe_grp) {
                         const u32x4 par = *reinterpret_cast<const u32x4*>(ol + h * C::PITCH + cpart);
                         uint32_t ow[4], pw[4], hw[4], lw[4];
@@ -1082,6 +1130,30 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
             for (int th = 0; th < C::TH; ++th)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[tg][th][r] += slot(0, tg, th, r);
+        if (PAD && tp > 1) {
+            // several tokens per chunk: the partial is the sum of the diagonal
+            // [nh, nh] blocks, p = 0, 1, .. in order, through an [NH][NH+1] matrix
+            // in LDS (only this wave is left; its LDS accesses complete in order)
+            float* m = reinterpret_cast<float*>(lbuf);
+            static_assert(NH * (NH + 1) * 4 <= (int)sizeof(lbuf), "diagonal-block area");
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int tg = 0; tg < C::TG; ++tg)
+#pragma unroll
+                for (int th = 0; th < C::TH; ++th)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        m[(32 * tg + 8 * (r >> 2) + 4 * half + (r & 3)) * (NH + 1) + 32 * th + (lane & 31)] =
+                            acc[tg][th][r];
+            __builtin_amdgcn_wave_barrier();
+            for (int idx = lane; idx < nh * nh; idx += 64) {
+                const int g = idx / nh, h = idx - g * nh;
+                float sum = m[g * (NH + 1) + h];
+                for (int p = 1; p < tp; ++p) sum += m[(p * nh + g) * (NH + 1) + p * nh + h];
+                part_out[idx] = sum;
+            }
+            return;
+        }
     }
 #pragma unroll
     for (int tg = 0; tg < C::TG; ++tg)
@@ -1799,13 +1871,14 @@ static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
     using C = PartCfg<NH, CP, WAVES, NS>;
     const int d = a.nope + a.pe;
     const int cpt = d / CP;
-    const int64_t n_tiles = a.sq * cpt;
-    const size_t lds = C::lds_bytes(a.nope, a.pe);
     const bool pad = a.nh != NH;
+    const int tp = pad ? C::tokens_per_tile(a.nh, a.pe) : 1;
+    const int64_t n_tiles = (a.sq + tp - 1) / tp * cpt;
+    const size_t lds = C::lds_bytes(a.nope, a.pe, tp);
     auto kern = pad ? mix_part_kernel<NH, CP, WAVES, DX, NS, true> : mix_part_kernel<NH, CP, WAVES, DX, NS, false>;
     static bool attr_done[2] = {false, false};  // idempotent; a race only repeats the call
     if (!attr_done[pad]) {
-        size_t lds_max = C::lds_bytes(8, CP);  // largest: pe = CP with the scratch
+        size_t lds_max = C::lds_bytes(8, CP) + (size_t)C::NT * 16;  // largest: pe = CP with the scratch
         if (lds_max > kMaxLds) lds_max = kMaxLds;  // shapes beyond it are not routed here
         if (lds_max > 65536) {
             hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -1815,23 +1888,30 @@ static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
         attr_done[pad] = true;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)n_tiles), dim3(64 * WAVES), lds, stream, a.X, a.W, a.rcos,
-                       a.rsin, a.table_rows, a.positions, a.nh, a.nope, a.pe, cpt, n_tiles, a.Out);
+                       a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, cpt, tp, n_tiles, a.Out);
     return hipGetLastError();
 }
 
 // Head rows of the token-part tile for nh heads: 32, 64 or 128 (padded with zeros).
 int mix_padded_heads(int nh) { return nh <= 32 ? 32 : (nh <= 64 ? 64 : 128); }
 
-// Head rows of the forward/dx tile: also 96 (three 32-head N-blocks, split over
-// 3 wave groups of 2 waves)
-static int mix_tile_heads(int nh) { return nh <= 64 ? mix_padded_heads(nh) : (nh <= 96 ? 96 : 128); }
+// Head rows of the forward/dx tile: 64 for nh <= 64 (several tokens per tile
+// when nh <= 32; 32 rows when the angle rows would leave a 64-row tile half
+// empty anyway), 96 (three 32-head N-blocks, split over 3 wave groups of 2
+// waves) or 128.
+static int mix_tile_heads(int nh, int pe, int cp) {
+    if (nh > 64) return nh <= 96 ? 96 : 128;
+    if (nh == 32) return 32;  // exact rows and 16-byte W loads beat two tokens per 64-row tile
+    const int tp = cp == 256 ? PartCfg<64, 256, 8>::tokens_per_tile(nh, pe) : PartCfg<64, 128, 4>::tokens_per_tile(nh, pe);
+    return tp * nh <= 32 ? 32 : 64;
+}
 
 // Channel-part width of the token-part kernel for this shape, or 0 when the
 // shape needs another kernel: 4 < nh <= 128 (padded to 32, 64 or 128), the part must
 // divide d, hold the whole pe range, fit the workgroup's LDS, and the grid
 // must stay below 2^31.
 int mix_part_width(int64_t sq, int nh, int nope, int pe) {
-    if (nh <= SMALL_NH || nh > 128) return 0;
+    if (nh < 1 || nh > 128) return 0;
     const int nhp = mix_padded_heads(nh);
     const int d = nope + pe;
     const int cands[2] = {256, 128};
@@ -1848,8 +1928,9 @@ template <bool DX>
 static hipError_t launch_mix_dx(const MixArgs& a, hipStream_t stream) {
     const bool w16 = ((uintptr_t)a.W & 15u) == 0;
     // the tiled kernels read W with 16-byte loads when nh fills the padded rows exactly
-    const int nhp = mix_tile_heads(a.nh);
-    const int cp = (a.force_general || (!w16 && a.nh == nhp)) ? 0 : mix_part_width(a.sq, a.nh, a.nope, a.pe);
+    int cp = a.force_general ? 0 : mix_part_width(a.sq, a.nh, a.nope, a.pe);
+    const int nhp = cp ? mix_tile_heads(a.nh, a.pe, cp) : 0;
+    if (!w16 && a.nh == nhp) cp = 0;
     if (cp == 256 && nhp == 64) return launch_part_t<64, 256, 8, DX>(a, stream);
     if (cp == 128 && nhp == 64) return launch_part_t<64, 128, 4, DX>(a, stream);
     if (cp == 256 && nhp == 32) return launch_part_t<32, 256, 8, DX>(a, stream);
@@ -1878,11 +1959,13 @@ hipError_t launch_mix(const MixArgs& a, bool dx, hipStream_t stream) {
     return dx ? launch_mix_dx<true>(a, stream) : launch_mix_dx<false>(a, stream);
 }
 
-// Tokens per weight-gradient block: sq*nh/32768 rounded up to a multiple of 4
-// (at least 4).  At sq=16384, nh=64 that is 32 tokens, 512 blocks: two
-// resident workgroups on each of 256 CUs, one round.
+// Tokens per weight-gradient block: sq*max(nh, 64)/32768 rounded up to a
+// multiple of 4 (at least 4).  At sq=16384, nh=64 that is 32 tokens, 512
+// blocks: two resident workgroups on each of 256 CUs, one round.  Below 64
+// heads the chunks hold several tokens, so the block count stays at 512 for
+// the same number of chunks per block.
 int dw_tokens_per_block(int64_t sq, int nh) {
-    int64_t t = (sq * nh + 32767) / 32768;
+    int64_t t = (sq * (nh < 64 ? 64 : nh) + 32767) / 32768;
     t = (t + 3) / 4 * 4;
     if (t < 4) t = 4;
     if (t > (1 << 20)) t = 1 << 20;
@@ -1913,9 +1996,38 @@ int64_t bwd_fused_num_blocks(int64_t sq, int nh) {
 
 // Chunk width of the LDS-staged weight-gradient kernel, or 0 for the direct kernel.
 int dw_chunk_width(int nh, int nope, int pe) {
-    if (nh <= SMALL_NH || nh > 128) return 0;  // padded to 32, 64 or 128 rows
+    if (nh < 1 || nh > 128) return 0;  // padded to 32, 64 or 128 rows
     const int d = nope + pe;
     return (d % 128 == 0 && pe <= 128) ? 128 : 0;
+}
+
+// Tokens per chunk of the weight-gradient kernel with NH head rows: as many
+// as fill the rows, while each quad of every token's cos and sin rows has a
+// thread to load it.
+template <int NH>
+static int dw_tokens_per_chunk(int nh, int pe) {
+    if (nh >= NH) return 1;
+    int tp = NH / nh;
+    const int cap = pe > 0 ? 8 * DwCfg<NH, 128>::NT / pe : tp;
+    return tp < cap ? tp : (cap < 1 ? 1 : cap);
+}
+
+// Head rows of the weight-gradient chunk: 64 (several tokens per chunk when
+// nh <= 32), 32 when the angle rows would leave a 64-row chunk half empty
+// anyway, 128 for nh > 64.
+static int dw_tile_heads(int nh, int pe) {
+    if (nh > 64) return 128;
+    return dw_tokens_per_chunk<64>(nh, pe) * nh <= 32 ? 32 : 64;
+}
+
+template <int NHC>
+static hipError_t launch_dw_chunk_t(const DwArgs& a, int tpb, int64_t nb, hipStream_t stream) {
+    const bool pad = a.nh != NHC;
+    const int tp = pad ? dw_tokens_per_chunk<NHC>(a.nh, a.pe) : 1;
+    auto kern = pad ? dw_chunk_kernel<NHC, 128, true> : dw_chunk_kernel<NHC, 128, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(DwCfg<NHC, 128>::NT), 0, stream, a.dY, a.O, a.rcos,
+                       a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, a.partials, tpb, tp);
+    return hipGetLastError();
 }
 
 template <int NHP>
@@ -1923,14 +2035,15 @@ static hipError_t launch_dw_t(const DwArgs& a, hipStream_t stream) {
     const int tpb = dw_tokens_per_block(a.sq, a.nh);
     const int64_t nb = dw_num_blocks(a.sq, a.nh);
     const int ch = a.force_general ? 0 : dw_chunk_width(a.nh, a.nope, a.pe);
-    if (!a.force_general && a.nh <= SMALL_NH) {
+    if (ch == 128) {
+        const int nhc = dw_tile_heads(a.nh, a.pe);
+        const hipError_t e = nhc == 32   ? launch_dw_chunk_t<32>(a, tpb, nb, stream)
+                             : nhc == 64 ? launch_dw_chunk_t<64>(a, tpb, nb, stream)
+                                         : launch_dw_chunk_t<128>(a, tpb, nb, stream);
+        if (e != hipSuccess) return e;
+    } else if (!a.force_general && a.nh <= SMALL_NH) {
         hipLaunchKernelGGL(small_dw_kernel, dim3((unsigned)nb), dim3(256), 0, stream, a.dY, a.O, a.rcos,
                            a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, tpb, a.partials);
-    } else if (ch == 128 && mix_padded_heads(a.nh) == (NHP < 32 ? 32 : NHP)) {
-        constexpr int NHC = NHP < 32 ? 32 : NHP;
-        auto kern = a.nh != NHC ? dw_chunk_kernel<NHC, 128, true> : dw_chunk_kernel<NHC, 128, false>;
-        hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(DwCfg<NHC, 128>::NT), 0, stream, a.dY, a.O, a.rcos,
-                           a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, a.partials, tpb);
     } else {
         hipLaunchKernelGGL((dw_partial_kernel<NHP>), dim3((unsigned)nb), dim3(256), 0, stream, a.dY,
                            a.O, a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe,

@@ -177,7 +177,8 @@ def test_workspace_size_is_a_function_of_the_shape():
     assert L.postmix_bwd_dw_workspace_bytes(16384, 64, 448, 64) == 1024 * 64 * 64 * 4
     # otherwise the weight-gradient kernels' 512 blocks of 32 tokens
     assert L.postmix_bwd_dw_workspace_bytes(16384, 64, 440, 64) == 512 * 64 * 64 * 4
-    assert L.postmix_bwd_dw_workspace_bytes(16384, 32, 448, 64) == 1024 * 32 * 32 * 4  # 16-token blocks
+    assert L.postmix_bwd_dw_workspace_bytes(16384, 32, 448, 64) == 512 * 32 * 32 * 4  # 32-token blocks
+    assert L.postmix_bwd_dw_workspace_bytes(131072, 8, 448, 64) == 512 * 8 * 8 * 4  # 256-token blocks
     # nh = 128 with pe rotated in registers: the single-pass backward's 512 blocks
     assert L.postmix_bwd_dw_workspace_bytes(8192, 128, 448, 64) == 512 * 128 * 128 * 4
     # nh = 128 with pe = 80 (not fused): the weight-gradient kernels' 256 blocks

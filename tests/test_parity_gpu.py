@@ -149,6 +149,19 @@ def kernel_policy(request):
     (9, 80, 448, 64, 3),       # nh = 80: padded to 96 (three wave groups)
     (7, 72, 192, 64, 11),      # nh = 72, d = 256: padded to 96
     (6, 96, 448, 64, 4000),    # nh = 96: 96-row tiles
+    (37, 8, 448, 64, 3),       # nh = 8: four tokens per 32-row tile, last tile one token
+    (23, 12, 192, 64, 9),      # nh = 12: two tokens per tile, d = 256
+    (19, 16, 432, 80, 5),      # nh = 16: two tokens per tile, pe through the fp32 scratch
+    (14, 5, 448, 64, 1),       # nh = 5: six tokens per tile (30 of 32 rows)
+    (17, 5, 320, 64, 11),      # nh = 5, d = 384: 128-channel parts
+    (9, 5, 256, 128, 4),       # nh = 5, pe = 128 in 128-channel parts
+    (7, 6, 0, 256, 3),         # nh = 6, every channel rotated: five tokens' cos/sin rows
+    (21, 8, 512, 0, 0),        # nh = 8, pe = 0
+    (70, 2, 192, 64, 5),       # nh = 2: 32 tokens per 64-row tile, ragged last tile
+    (40, 3, 320, 64, 1),       # nh = 3, 128-channel parts: the angle rows cap the tile at 16 tokens
+    (45, 1, 448, 64, 3),       # nh = 1: 32 tokens per 32-row tile
+    (29, 12, 448, 64, 8),      # nh = 12: five tokens per 64-row tile
+    (33, 32, 448, 64, 2),      # nh = 32: exact 32-row mix tiles, two tokens per weight-gradient chunk
 ])
 def test_small_shapes(sq, nh, nope, pe, off, kernel_policy):
     full_check(synthetic.case(sq, nh, nope, pe, seed=1000 + sq + nh, pos_offset=off))
@@ -260,7 +273,7 @@ def test_out_of_range_positions_are_clamped_not_read_out_of_bounds():
     gu.check_bf16(gu.host_bits(Y), ref, "clamped positions")
 
 
-@pytest.mark.parametrize("nh", [64, 20])  # general kernels; padded tiles reading W element-wise
+@pytest.mark.parametrize("nh", [64, 20, 8])  # general kernels; padded (and token-packed) tiles reading W element-wise
 def test_unaligned_W(nh):
     """W that is 2-byte but not 16-byte aligned: results on the oracle."""
     import torch
