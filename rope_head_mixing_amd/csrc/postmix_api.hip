@@ -198,7 +198,7 @@ size_t postmix_bwd_dw_workspace_bytes(int64_t sq, int32_t nh, int32_t nope, int3
     if (rc || sq == 0) return 0;
     int64_t blocks = pm::dw_num_blocks(sq, nh);
     if (pm::bwd_fused_applies(nh, nope, pe)) {  // postmix_bwd's single pass has its own blocks
-        const int64_t fb = pm::bwd_fused_num_blocks(sq, nh);
+        const int64_t fb = pm::bwd_fused_num_blocks(sq, nh, nope, pe);
         if (fb > blocks) blocks = fb;
     }
     const size_t bytes = (size_t)blocks * nh * nh * sizeof(float);

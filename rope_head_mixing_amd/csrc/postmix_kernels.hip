@@ -1218,11 +1218,14 @@ struct BwdCfg {
         const size_t p = pe_pairs_in_blocks(nope, pe) ? 0 : (size_t)NH * (pe + 4) * 4;
         return WRES ? w + p : (w > p ? w : p);
     }
-    static constexpr int RG = 16;                   // tokens per group of staged cos/sin rows
-    // dY chunk, O chunk, dO chunk, then W / pe scratch, then the cos and sin
-    // rows of RG tokens
-    __host__ __device__ static size_t lds_bytes(int nope, int pe) {
-        return (size_t)3 * NH * PITCH * 2 + aux_bytes(nope, pe) + (size_t)RG * pe * 4;
+    // tokens per group of staged cos/sin rows: whole chunks of tp tokens, at
+    // least 16 tokens; at most 32
+    __host__ __device__ static int rope_group(int tp) { return tp * ((16 + tp - 1) / tp); }
+    static constexpr int RG_MAX = 32;
+    // dY chunk, O chunk, dO chunk, then W / pe scratch, then two buffers of
+    // the cos and sin rows of rgt tokens
+    __host__ __device__ static size_t lds_bytes(int nope, int pe, int rgt = 16) {
+        return (size_t)3 * NH * PITCH * 2 + aux_bytes(nope, pe) + (size_t)2 * rgt * pe * 4;
     }
 };
 
@@ -1231,10 +1234,15 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O, const uint16_t* __restrict__ W,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
     const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe,
-    uint16_t* __restrict__ dO, float* __restrict__ partials, int tokens_per_block) {
-    // PAD: nh < NH, head rows nh .. NH-1 are zero padding (never loaded or
-    // stored; only the [nh, nh] part of the partial is written); otherwise nh == NH
+    uint16_t* __restrict__ dO, float* __restrict__ partials, int tokens_per_block, int ptok, int rgt) {
+    // PAD: nh < NH.  A chunk then holds ptok consecutive tokens (ptok*nh
+    // consecutive rows of the [sq*nh, d] arrays; W staged block-diagonally,
+    // one copy per token, exactly as in the token-part kernel), the other rows
+    // are zero padding (never loaded or stored), and the partial is the sum of
+    // the ptok diagonal [nh, nh] blocks.  Otherwise nh == NH and ptok == 1.
     using C = BwdCfg<NH, CH, WAVES>;
+    const int tp = PAD ? ptok : 1;
+    // rgt: tokens per staged group of cos/sin rows, a multiple of tp
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint16_t* dyl = smem;                               // [NH][PITCH]
     uint16_t* ol = dyl + NH * C::PITCH;                 // [NH][PITCH]
@@ -1252,54 +1260,83 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     const int tile = wave % C::NTILE, kset = wave / C::NTILE;
     const int gb = tile / C::NB, hb = tile % C::NB;
     const int mb = wave % C::MBC, nb = wave / C::MBC;
+    // offsets into a chunk's cos/sin rows of the tokens of this lane's dW row
+    // (32*hb + lane%32) and dx row (32*nb + lane%32); padding rows take any
+    // staged token's
+    int ph = PAD ? (32 * hb + (lane & 31)) / nh : 0, pr = PAD ? (32 * nb + (lane & 31)) / nh : 0;
+    const int ph_off = (ph < tp ? ph : tp - 1) * pe, pr_off = (pr < tp ? pr : tp - 1) * pe;
 
     const int64_t s_begin = (int64_t)blockIdx.x * tokens_per_block;
     int64_t s_end = s_begin + tokens_per_block;
     if (s_end > sq) s_end = sq;
-    const int nchunks = (int)(s_end - s_begin) * cpt;
+    const int nchunks = (int)((s_end - s_begin + tp - 1) / tp) * cpt;
 
     u32x4 v[C::VPT];
-    // cos and sin rows of tokens s0 .. s0+RG-1 (within the block) -> LDS;
-    // read once per RG tokens instead of once per chunk
-    auto load_rope_group = [&](int64_t s0) {
+    // cos and sin rows of tokens s0 .. s0+rgt-1 (within the block) -> LDS
+    // buffer `buf`; read once per rgt tokens instead of once per chunk.  Rows
+    // past the last token are zeros: the padding rows of a partial chunk
+    // rotate zeros with them, and their products must stay exact zeros.
+    auto load_rope_group = [&](int64_t s0, int buf) {
+        float* const rg = rope_g + buf * rgt * pe;
         int64_t n = s_end - s0;
-        if (n > C::RG) n = C::RG;
+        if (n > rgt) n = rgt;
         const int q4 = pe >> 2, half4 = pe >> 3;  // f32x4 per token row (cos + sin), per table row
-        for (int idx = tid; idx < (int)n * q4; idx += C::NT) {
+        for (int idx = tid; idx < rgt * q4; idx += C::NT) {
             const int t = idx / q4, q = idx - t * q4;
-            const int64_t prow = table_row(positions, s0 + t, table_rows);
-            const float* tab = q < half4 ? rcos : rsin;
-            const int qq = q < half4 ? q : q - half4;
-            reinterpret_cast<f32x4*>(rope_g + t * pe)[q] = reinterpret_cast<const f32x4*>(tab + prow * h2)[qq];
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (t < n) {
+                const int64_t prow = table_row(positions, s0 + t, table_rows);
+                const float* tab = q < half4 ? rcos : rsin;
+                const int qq = q < half4 ? q : q - half4;
+                x = reinterpret_cast<const f32x4*>(tab + prow * h2)[qq];
+            }
+            reinterpret_cast<f32x4*>(rg + t * pe)[q] = x;
         }
     };
+    // head rows of chunk k backed by tokens < s_end
+    auto chunk_rows = [&](int k) -> int {
+        if (!PAD) return NH;
+        const int64_t left = s_end - (s_begin + (int64_t)(k / cpt) * tp);
+        return (int)(left < tp ? left : tp) * nh;
+    };
+    // The loads are unconditional: padding rows re-read the chunk's last row
+    // (an L2 hit) and are zeroed when staged.  Exec-masked loads would need
+    // their addresses live across the loop, and a spill reload there waits
+    // for every load in flight (scratch and global loads share one counter),
+    // which serialises the prefetch.  In-chunk offsets fit 32 bits (d <= 2^24).
     auto load_chunk = [&](int k) {
-        const int64_t s = s_begin + k / cpt;
+        const int64_t s = s_begin + (int64_t)(k / cpt) * tp;  // first token of the chunk
         const int part = k % cpt;
+        const int rows = chunk_rows(k);
         const int64_t rowbase = s * nh * (int64_t)d + part * CH;
+        const uint16_t* const dyb = dY + rowbase;
+        const uint16_t* const ob = O + rowbase;
 #pragma unroll
         for (int j = 0; j < C::VPT; ++j) {
             const int q = j * C::NT + tid;
             const int op = q / C::VPO;               // 0: dY, 1: O (compile-time per j)
             const int rem = q % C::VPO;
-            const int row = rem / C::VPR, c8 = rem % C::VPR;
-            const uint16_t* src = (op == 0 ? dY : O) + rowbase + row * (int64_t)d + 8 * c8;
-            v[j] = (!PAD || row < nh) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src))
-                                      : u32x4{0u, 0u, 0u, 0u};
+            int row = rem / C::VPR;
+            const int c8 = rem % C::VPR;
+            if (PAD) row = row < rows ? row : rows - 1;
+            const uint32_t off = (uint32_t)row * (uint32_t)d + 8u * (uint32_t)c8;
+            v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>((op == 0 ? dyb : ob) + off));
         }
     };
-    auto stage_chunk = [&]() {  // registers of the next chunk -> LDS
+    auto stage_chunk = [&](int k) {  // registers of chunk k -> LDS (padding rows as zeros)
+        const int rows = chunk_rows(k);
 #pragma unroll
         for (int j = 0; j < C::VPT; ++j) {
             const int q = j * C::NT + tid;
             const int op = q / C::VPO;
             const int rem = q % C::VPO;
             const int row = rem / C::VPR, c8 = rem % C::VPR;
-            *reinterpret_cast<u32x4*>((op == 0 ? dyl : ol) + row * C::PITCH + 8 * c8) = v[j];
+            const u32x4 x = (!PAD || row < rows) ? v[j] : u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>((op == 0 ? dyl : ol) + row * C::PITCH + 8 * c8) = x;
         }
     };
     if (nchunks > 0) load_chunk(0);
-    if (pe > 0 && nchunks > 0) load_rope_group(s_begin);
+    if (pe > 0 && nchunks > 0) load_rope_group(s_begin, 0);
 
     // W -> LDS -> this wave's dx B operand (B[k=g][n=h] = W[g][h], N-block nb)
     if (!PAD) {
@@ -1307,10 +1344,12 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             const int row = q / (NH / 8), c8 = q % (NH / 8);
             *reinterpret_cast<u32x4*>(wl + row * C::WPITCH + 8 * c8) = reinterpret_cast<const u32x4*>(W)[q];
         }
-    } else {
+    } else {  // block-diagonal: W at rows and columns p*nh .. p*nh+nh-1 for p < tp, zeros elsewhere
         for (int q = tid; q < NH * NH; q += C::NT) {
             const int row = q / NH, col = q % NH;
-            wl[row * C::WPITCH + col] = (row < nh && col < nh) ? W[row * nh + col] : (uint16_t)0;
+            const int p = row / nh, pc = col / nh;
+            wl[row * C::WPITCH + col] =
+                (p == pc && p < tp) ? W[(row - p * nh) * nh + (col - p * nh)] : (uint16_t)0;
         }
     }
     __syncthreads();
@@ -1330,16 +1369,18 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     // there and chunk k+2 is requested, and only then are chunk k's dO rows
     // stored (they live in separate buffers).  Two barriers per chunk.
     if (nchunks > 0) {
-        stage_chunk();
+        stage_chunk(0);
         if (nchunks > 1) load_chunk(1);
     }
     __syncthreads();
     for (int k = 0; k < nchunks; ++k) {
-        const int64_t s = s_begin + k / cpt;
+        const int64_t s = s_begin + (int64_t)(k / cpt) * tp;  // first token of the chunk
         const int part = k % cpt;
         const int c_base = part * CH;
         const bool chunk_pe = pe > 0 && c_base + CH > nope;
-        const float* csl = rope_g + ((k / cpt) % C::RG) * pe;
+        // cos/sin rows of the chunk's first token; a row r of the chunk uses those of token r / nh
+        const int tok = (k / cpt) * tp;  // the chunk's first token within the block
+        const float* csl = rope_g + (((tok / rgt) & 1) * rgt + tok % rgt) * pe;
         const float* snl = csl + (pe >> 1);
 
         // ---- weight gradient: tile (gb, hb), k-steps t = kset, kset + 2, ...
@@ -1360,9 +1401,11 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
                     const bool first = cg < nope + h2;
                     const int i0 = first ? cg - nope : cg - nope - h2;
                     const float sgn = first ? 1.0f : -1.0f;
+                    const float* cr = csl + ph_off + i0;
+                    const float* sr = snl + ph_off + i0;
                     const u32x4 par = *reinterpret_cast<const u32x4*>(ol + h * C::PITCH + (first ? c + h2 : c - h2));
-                    const f32x4 c0 = *reinterpret_cast<const f32x4*>(csl + i0), c1 = *reinterpret_cast<const f32x4*>(csl + i0 + 4);
-                    const f32x4 s0 = *reinterpret_cast<const f32x4*>(snl + i0), s1 = *reinterpret_cast<const f32x4*>(snl + i0 + 4);
+                    const f32x4 c0 = *reinterpret_cast<const f32x4*>(cr), c1 = *reinterpret_cast<const f32x4*>(cr + 4);
+                    const f32x4 s0 = *reinterpret_cast<const f32x4*>(sr), s1 = *reinterpret_cast<const f32x4*>(sr + 4);
                     float cs[8], sn[8];
                     uint32_t ow[4], pw[4], hw[4], lw[4];
 #pragma unroll
@@ -1401,7 +1444,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], b, acc, 0, 0, 0);
             }
             const int hrow = 32 * nb + (lane & 31);
-            if (pb) rotate_paired_block(acc, dol, C::PITCH, hrow, L, h2, q, Q, csl, snl, -1.0f);
+            if (pb) rotate_paired_block(acc, dol, C::PITCH, hrow, L, h2, q, Q, csl + pr_off, snl + pr_off, -1.0f);
 #pragma unroll
             for (int a = 0; a < 4 && !pb; ++a) {
                 const int cl = 32 * mb + 8 * a + 4 * Q;
@@ -1419,17 +1462,24 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         }
         __syncthreads();  // dY/O buffers free; dO and the pe scratch complete
         if (k + 1 < nchunks) {
-            stage_chunk();  // chunk k+1
+            // a new group of cos/sin rows goes to the other buffer (the one of
+            // the group before this chunk's), ahead of the chunk prefetch, so
+            // waiting for the table rows waits for nothing else in flight
+            // but chunk k+1, which the staging needs anyway
+            const int tok1 = ((k + 1) / cpt) * tp;
+            if (pe > 0 && (k + 1) % cpt == 0 && tok1 % rgt == 0) load_rope_group(s_begin + tok1, (tok1 / rgt) & 1);
+            stage_chunk(k + 1);
             if (k + 2 < nchunks) load_chunk(k + 2);  // in flight during two compute phases
         }
 
         // ---- dO rows of the chunk; pe pairs turned by +phi
         uint16_t* outs = dO + s * nh * (int64_t)d + c_base;
+        const int rows_k = chunk_rows(k);
 #pragma unroll
         for (int j = 0; j < C::OPT; ++j) {
             const int q = j * C::NT + tid;
             const int row = q / C::VPR, c8 = q % C::VPR;
-            if (PAD && row >= nh) continue;  // padding rows
+            if (PAD && row >= rows_k) continue;  // padding rows
             const int cl = 8 * c8, cg = c_base + cl;
             u32x4 o;
             if (cg < nope || paired) {
@@ -1440,12 +1490,13 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
                 const int ii = first ? i : i - h2;
                 const float* own = pes + row * pes_pitch + i;
                 const float* par = pes + row * pes_pitch + (first ? i + h2 : i - h2);
+                const int rp = PAD ? (row / nh) * pe : 0;  // the row's token's cos/sin
                 const f32x4 o0 = reinterpret_cast<const f32x4*>(own)[0], o1 = reinterpret_cast<const f32x4*>(own)[1];
                 const f32x4 p0 = reinterpret_cast<const f32x4*>(par)[0], p1 = reinterpret_cast<const f32x4*>(par)[1];
-                const f32x4 c0 = reinterpret_cast<const f32x4*>(csl + ii)[0];
-                const f32x4 c1 = reinterpret_cast<const f32x4*>(csl + ii)[1];
-                const f32x4 s0 = reinterpret_cast<const f32x4*>(snl + ii)[0];
-                const f32x4 s1 = reinterpret_cast<const f32x4*>(snl + ii)[1];
+                const f32x4 c0 = reinterpret_cast<const f32x4*>(csl + rp + ii)[0];
+                const f32x4 c1 = reinterpret_cast<const f32x4*>(csl + rp + ii)[1];
+                const f32x4 s0 = reinterpret_cast<const f32x4*>(snl + rp + ii)[0];
+                const f32x4 s1 = reinterpret_cast<const f32x4*>(snl + rp + ii)[1];
                 // +phi: first half a C - b S, second half b C + a S
                 const float sg = first ? -1.0f : 1.0f;
                 float y[8];
@@ -1459,11 +1510,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             }
             __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(outs + row * (int64_t)d + cl));
         }
-        __syncthreads();  // dO buffers read; chunk k+1 staged
-        if (pe > 0 && k + 1 < nchunks && (k + 1) % cpt == 0 && ((k + 1) / cpt) % C::RG == 0) {
-            load_rope_group(s_begin + (k + 1) / cpt);  // the next RG tokens' cos/sin rows
-            __syncthreads();
-        }
+        __syncthreads();  // dO buffers read; chunk k+1 and its cos/sin rows staged
     }
 
     // ---- dW partial: the k-sets of each tile summed in k-set order (fixed)
@@ -1473,6 +1520,32 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         for (int r = 0; r < 16; ++r) red[(((kset - 1) * C::NTILE + tile) * 16 + r) * 64 + lane] = acc_w[r];
     }
     __syncthreads();
+    if constexpr (PAD) {
+        // the full [NH, NH] sum goes to LDS (after the k-set area), then the
+        // partial is the sum of the tp diagonal [nh, nh] blocks, p = 0, 1, ..
+        // in order (tp = 1: the block itself)
+        constexpr int RED = (C::KSET - 1) * C::NTILE * 16 * 64;  // floats of the k-set area
+        static_assert((RED + NH * (NH + 1)) * 4 <= 3 * NH * C::PITCH * 2, "diagonal-block area");
+        float* m = red + RED;
+        if (kset == 0) {
+#pragma unroll
+            for (int k = 1; k < C::KSET; ++k)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc_w[r] += red[(((k - 1) * C::NTILE + tile) * 16 + r) * 64 + lane];
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                m[(32 * gb + 8 * (r >> 2) + 4 * half + (r & 3)) * (NH + 1) + 32 * hb + (lane & 31)] = acc_w[r];
+        }
+        __syncthreads();
+        float* part_out = partials + (int64_t)blockIdx.x * nh * nh;
+        for (int idx = tid; idx < nh * nh; idx += C::NT) {
+            const int g = idx / nh, h = idx - g * nh;
+            float sum = m[g * (NH + 1) + h];
+            for (int p = 1; p < tp; ++p) sum += m[(p * nh + g) * (NH + 1) + p * nh + h];
+            part_out[idx] = sum;
+        }
+        return;
+    }
     if (kset != 0) return;
 #pragma unroll
     for (int k = 1; k < C::KSET; ++k)
@@ -1483,7 +1556,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int g = 32 * gb + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (!PAD || (g < nh && h < nh)) part_out[g * nh + h] = acc_w[r];
+        part_out[g * nh + h] = acc_w[r];
     }
 }
 
@@ -1895,15 +1968,23 @@ static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
 // Head rows of the token-part tile for nh heads: 32, 64 or 128 (padded with zeros).
 int mix_padded_heads(int nh) { return nh <= 32 ? 32 : (nh <= 64 ? 64 : 128); }
 
+// Tokens per 64-row tile of the token-part kernel with CP-channel parts.
+static int mix_tokens_per_tile64(int nh, int pe, int cp) {
+    return cp == 256 ? PartCfg<64, 256, 8>::tokens_per_tile(nh, pe) : PartCfg<64, 128, 4>::tokens_per_tile(nh, pe);
+}
+
 // Head rows of the forward/dx tile: 64 for nh <= 64 (several tokens per tile
-// when nh <= 32; 32 rows when the angle rows would leave a 64-row tile half
-// empty anyway), 96 (three 32-head N-blocks, split over 3 wave groups of 2
-// waves) or 128.
-static int mix_tile_heads(int nh, int pe, int cp) {
+// when nh <= 32), 96 (three 32-head N-blocks, split over 3 wave groups of 2
+// waves) or 128.  The forward also takes 32-row tiles where they measured
+// faster: nh = 32 (exact rows, 16-byte W loads), and where the angle rows
+// would leave a 64-row tile half empty anyway (nh = 1).  dx keeps 64 rows:
+// the fused backward computes dO in the same tiles (same tokens per tile,
+// same MFMA inputs and order), so the two agree bit for bit.
+static int mix_tile_heads(int nh, int pe, int cp, bool dx) {
     if (nh > 64) return nh <= 96 ? 96 : 128;
-    if (nh == 32) return 32;  // exact rows and 16-byte W loads beat two tokens per 64-row tile
-    const int tp = cp == 256 ? PartCfg<64, 256, 8>::tokens_per_tile(nh, pe) : PartCfg<64, 128, 4>::tokens_per_tile(nh, pe);
-    return tp * nh <= 32 ? 32 : 64;
+    if (dx) return 64;
+    if (nh == 32) return 32;
+    return mix_tokens_per_tile64(nh, pe, cp) * nh <= 32 ? 32 : 64;
 }
 
 // Channel-part width of the token-part kernel for this shape, or 0 when the
@@ -1929,7 +2010,7 @@ static hipError_t launch_mix_dx(const MixArgs& a, hipStream_t stream) {
     const bool w16 = ((uintptr_t)a.W & 15u) == 0;
     // the tiled kernels read W with 16-byte loads when nh fills the padded rows exactly
     int cp = a.force_general ? 0 : mix_part_width(a.sq, a.nh, a.nope, a.pe);
-    const int nhp = cp ? mix_tile_heads(a.nh, a.pe, cp) : 0;
+    const int nhp = cp ? mix_tile_heads(a.nh, a.pe, cp, DX) : 0;
     if (!w16 && a.nh == nhp) cp = 0;
     if (cp == 256 && nhp == 64) return launch_part_t<64, 256, 8, DX>(a, stream);
     if (cp == 128 && nhp == 64) return launch_part_t<64, 128, 4, DX>(a, stream);
@@ -1977,20 +2058,33 @@ int64_t dw_num_blocks(int64_t sq, int nh) {
     return (sq + t - 1) / t;
 }
 
-// The fused backward uses blocks of half as many tokens (sq*nh/65536 rounded
-// up to a multiple of 4, at least 4): its one 16-wave workgroup per CU then
-// works through four rounds of blocks at the production shape, which balances
-// better than two.
-int bwd_fused_tokens_per_block(int64_t sq, int nh) {
-    int64_t t = (sq * nh + 65535) / 65536;
+// chunk width of the fused backward: 256 channels (16 waves) where d allows
+static int bwd_fused_chunk(int d) { return d % 256 == 0 ? 256 : 128; }
+
+// Tokens per chunk of the fused backward: nh <= 32 packs the tokens of the
+// dx tile (the token-part kernel's 64-row tile with parts as wide as the
+// chunks), so the two compute dO identically; otherwise one.
+static int bwd_fused_tokens_per_chunk(int nh, int nope, int pe) {
+    return nh <= 32 ? mix_tokens_per_tile64(nh, pe, bwd_fused_chunk(nope + pe)) : 1;
+}
+
+// The fused backward uses blocks of half as many tokens as the weight
+// gradient: sq*max(nh, 64)/65536 rounded up to a multiple of 4 (at least 4),
+// then to a multiple of the tokens per chunk (whole chunks, aligned with the
+// dx tiles).  Its one 16-wave workgroup per CU then works through four rounds
+// of blocks at the production shape, which balances better than two.
+int bwd_fused_tokens_per_block(int64_t sq, int nh, int nope, int pe) {
+    int64_t t = (sq * (nh < 64 ? 64 : nh) + 65535) / 65536;
     t = (t + 3) / 4 * 4;
     if (t < 4) t = 4;
     if (t > (1 << 20)) t = 1 << 20;
+    const int tp = bwd_fused_tokens_per_chunk(nh, nope, pe);
+    t = (t + tp - 1) / tp * tp;
     return (int)t;
 }
 
-int64_t bwd_fused_num_blocks(int64_t sq, int nh) {
-    const int t = bwd_fused_tokens_per_block(sq, nh);
+int64_t bwd_fused_num_blocks(int64_t sq, int nh, int nope, int pe) {
+    const int t = bwd_fused_tokens_per_block(sq, nh, nope, pe);
     return (sq + t - 1) / t;
 }
 
@@ -2060,44 +2154,56 @@ static hipError_t launch_dw_t(const DwArgs& a, hipStream_t stream) {
 // fused backward (dx + dW partials in one pass), then the fixed-order reduce
 bool bwd_fused_applies(int nh, int nope, int pe) {
     const int d = nope + pe;
-    if (d % 128 != 0 || pe > 128) return false;
-    // head rows padded to 64 (32 < nh <= 64) or to 128 (pe rotated in registers only)
-    return (nh > 32 && nh <= 64) || (nh > 64 && nh <= 128 && (pe == 0 || pe_pairs_in_blocks(nope, pe)));
+    if (nh < 1 || d % 128 != 0 || pe > 128 || d > (1 << 24)) return false;
+    // several tokens per 64-row chunk (nh <= 32; at most a cos/sin group of them),
+    // head rows padded to 64 (32 < nh <= 64), or to 128 (pe rotated in registers only)
+    size_t lds;
+    if (nh <= 64) {
+        const int tp = bwd_fused_tokens_per_chunk(nh, nope, pe);
+        if (tp > BwdCfg<64, 128, 8>::RG_MAX) return false;
+        const int rgt = BwdCfg<64, 128, 8>::rope_group(tp);
+        lds = bwd_fused_chunk(d) == 256 ? BwdCfg<64, 256, 16>::lds_bytes(nope, pe, rgt)
+                                        : BwdCfg<64, 128, 8>::lds_bytes(nope, pe, rgt);
+    } else {
+        if (!(pe == 0 || pe_pairs_in_blocks(nope, pe))) return false;
+        lds = BwdCfg<128, 128, 16>::lds_bytes(nope, pe, BwdCfg<128, 128, 16>::rope_group(1));
+    }
+    return lds <= kMaxLds;
 }
 
-// chunk width of the fused backward: 256 channels (16 waves) where d allows
-static int bwd_fused_chunk(int d) { return d % 256 == 0 ? 256 : 128; }
-
 template <int NH, int CH, int WAVES>
-static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int tpb, int64_t nb, hipStream_t stream) {
+static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int tpb, int64_t nb, int tp,
+                                     hipStream_t stream) {
     using C = BwdCfg<NH, CH, WAVES>;
     const bool pad = a.nh != NH;
     auto kern = pad ? bwd_fused_kernel<NH, CH, WAVES, true> : bwd_fused_kernel<NH, CH, WAVES, false>;
     static bool attr_done[2] = {false, false};  // idempotent; a race only repeats the call
     if (!attr_done[pad]) {
-        size_t lds_max = C::lds_bytes(8, 128);  // largest: pe = 128 with the scratch
+        size_t lds_max = C::lds_bytes(8, 128, C::RG_MAX);  // largest: pe = 128 with the scratch
         if (lds_max > kMaxLds) lds_max = kMaxLds;
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)lds_max);
         if (e != hipSuccess) return e;
         attr_done[pad] = true;
     }
-    if (C::lds_bytes(a.nope, a.pe) > kMaxLds) return hipErrorInvalidValue;  // excluded by bwd_fused_applies
-    hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), C::lds_bytes(a.nope, a.pe), stream, a.dY, a.O, mx.W,
-                       a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, mx.Out, a.partials,
-                       tpb);
+    const int rgt = C::rope_group(tp);
+    const size_t lds = C::lds_bytes(a.nope, a.pe, rgt);
+    if (lds > kMaxLds) return hipErrorInvalidValue;  // excluded by bwd_fused_applies
+    hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), lds, stream, a.dY, a.O, mx.W, a.rcos, a.rsin,
+                       a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, mx.Out, a.partials, tpb, tp, rgt);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_fused(const MixArgs& mx, const DwArgs& a, hipStream_t stream) {
-    const int tpb = bwd_fused_tokens_per_block(a.sq, a.nh);
-    const int64_t nb = bwd_fused_num_blocks(a.sq, a.nh);
+    const int tpb = bwd_fused_tokens_per_block(a.sq, a.nh, a.nope, a.pe);
+    const int64_t nb = bwd_fused_num_blocks(a.sq, a.nh, a.nope, a.pe);
+    const int tp = bwd_fused_tokens_per_chunk(a.nh, a.nope, a.pe);
     hipError_t err;
     if (a.nh > 64)
-        err = launch_bwd_fused_t<128, 128, 16>(mx, a, tpb, nb, stream);
+        err = launch_bwd_fused_t<128, 128, 16>(mx, a, tpb, nb, 1, stream);
     else
-        err = bwd_fused_chunk(a.nope + a.pe) == 256 ? launch_bwd_fused_t<64, 256, 16>(mx, a, tpb, nb, stream)
-                                                    : launch_bwd_fused_t<64, 128, 8>(mx, a, tpb, nb, stream);
+        err = bwd_fused_chunk(a.nope + a.pe) == 256 ? launch_bwd_fused_t<64, 256, 16>(mx, a, tpb, nb, tp, stream)
+                                                    : launch_bwd_fused_t<64, 128, 8>(mx, a, tpb, nb, tp, stream);
     if (err != hipSuccess) return err;
     const int64_t ne = (int64_t)a.nh * a.nh;
     hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((ne + 63) / 64)), dim3(1024), 0, stream,

@@ -51,8 +51,8 @@ hipError_t launch_rope_table(double theta, int pe, int64_t rows, float* cos_out,
 // summation order (and therefore every bit of dW) does not depend on the GPU.
 int dw_tokens_per_block(int64_t sq, int nh);
 int64_t dw_num_blocks(int64_t sq, int nh);
-int bwd_fused_tokens_per_block(int64_t sq, int nh);
-int64_t bwd_fused_num_blocks(int64_t sq, int nh);
+int bwd_fused_tokens_per_block(int64_t sq, int nh, int nope, int pe);
+int64_t bwd_fused_num_blocks(int64_t sq, int nh, int nope, int pe);
 int dw_chunk_width(int nh, int nope, int pe);
 
 // Fused backward: dx (into mx.Out) and the dW partials from one pass over dY

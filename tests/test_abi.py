@@ -177,8 +177,15 @@ def test_workspace_size_is_a_function_of_the_shape():
     assert L.postmix_bwd_dw_workspace_bytes(16384, 64, 448, 64) == 1024 * 64 * 64 * 4
     # otherwise the weight-gradient kernels' 512 blocks of 32 tokens
     assert L.postmix_bwd_dw_workspace_bytes(16384, 64, 440, 64) == 512 * 64 * 64 * 4
-    assert L.postmix_bwd_dw_workspace_bytes(16384, 32, 448, 64) == 512 * 32 * 32 * 4  # 32-token blocks
-    assert L.postmix_bwd_dw_workspace_bytes(131072, 8, 448, 64) == 512 * 8 * 8 * 4  # 256-token blocks
+    # nh <= 32: several tokens per chunk; block sizes as for 64 heads, so the
+    # single-pass backward's 1024 blocks again (16 and 128 tokens)
+    assert L.postmix_bwd_dw_workspace_bytes(16384, 32, 448, 64) == 1024 * 32 * 32 * 4
+    assert L.postmix_bwd_dw_workspace_bytes(131072, 8, 448, 64) == 1024 * 8 * 8 * 4
+    # nh = 3: 21 tokens per chunk, so the single pass takes blocks of 21 tokens
+    # (391 blocks); the weight-gradient kernels' 512 blocks of 16 are more
+    assert L.postmix_bwd_dw_workspace_bytes(8192, 3, 448, 64) == 512 * 3 * 3 * 4
+    # not fused (nh = 1 with pe = 16): the weight-gradient kernels' blocks
+    assert L.postmix_bwd_dw_workspace_bytes(16384, 1, 496, 16) == 512 * 1 * 1 * 4
     # nh = 128 with pe rotated in registers: the single-pass backward's 512 blocks
     assert L.postmix_bwd_dw_workspace_bytes(8192, 128, 448, 64) == 512 * 128 * 128 * 4
     # nh = 128 with pe = 80 (not fused): the weight-gradient kernels' 256 blocks

@@ -208,8 +208,17 @@ def test_tiled_and_general_kernels_agree(sq, nh, nope, pe):
     (9, 33, 192, 64, 1),        # fused path, nh = 33, d = 256
     (7, 96, 448, 64, 5),        # fused path, nh = 96 (head rows padded to 128)
     (6, 100, 432, 80, 9),       # not fused (padded to 128 with pe = 80): separate kernels
-    (21, 32, 448, 64, 5),       # not fused (nh = 32): separate kernels
-    (9, 3, 448, 64, 0),         # not fused (nh = 3)
+    (21, 32, 448, 64, 5),       # fused path, nh = 32: two tokens per 64-row chunk
+    (9, 3, 448, 64, 0),         # fused path, nh = 3: one partial chunk of 9 of 21 tokens
+    (300, 3, 448, 64, 7),       # fused path, nh = 3: 15 blocks of 21 tokens, the last one partial
+    (37, 8, 192, 64, 2),        # fused path, nh = 8, d = 256: eight tokens per chunk
+    (29, 5, 320, 64, 3),        # fused path, nh = 5, d = 384: 128-channel chunks, 12 tokens each
+    (23, 20, 496, 16, 9),       # fused path, nh = 20, pe = 16: pe through the fp32 scratch
+    (41, 1, 448, 64, 11),       # fused path, nh = 1: 32 tokens per chunk (the cos/sin group)
+    # (not sq = 40: with that seed the nope and pe sums of the single dW entry
+    # cancel to 6e-5 of the sum of |terms|, below what an fp32 accumulation
+    # can resolve to 1e-4 relative)
+    (12, 1, 496, 16, 1),        # not fused (nh = 1, pe = 16: 64 tokens would exceed the cos/sin group)
 ])
 def test_fused_backward_matches_oracle_and_separate_calls(sq, nh, nope, pe, off):
     c = synthetic.case(sq, nh, nope, pe, seed=4000 + sq, pos_offset=off)
