@@ -1186,9 +1186,10 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
 //          results to an LDS output chunk (other pe layouts: an fp32 scratch,
 //          rotated in the store phase); the store phase writes dO rows with
 //          non-temporal stores.
-// The dx arithmetic (MFMA inputs, k order, rotation expression) is that of
-// the token-part kernel, so dO is bitwise the same as postmix_bwd_dx's.
-// nh = 64, or nh = 128 with pe rotated in registers (16 waves, one dW tile
+// The dx arithmetic (MFMA inputs, k order, rotation expression, tokens per
+// tile) is that of the token-part kernel, so dO is bitwise the same as
+// postmix_bwd_dx's.  64 head rows (nh <= 32: several tokens per chunk; up to
+// 64: padded), or 128 with pe rotated in registers (16 waves, one dW tile
 // each); d a multiple of 128, pe <= 128 (all pe channels in a token's last chunk).
 // ---------------------------------------------------------------------------
 
@@ -1250,7 +1251,8 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     uint16_t* wl = dol + NH * C::PITCH;                 // [NH][WPITCH] bf16, then:
     float* pes = reinterpret_cast<float*>(wl + (C::WRES ? NH * C::WPITCH : 0));  // [NH][pe + 4] fp32
     const int pes_pitch = pe + 4;
-    // cos/sin rows of RG consecutive tokens: [RG][pe] floats (cos then sin each)
+    // two buffers of the cos/sin rows of rgt consecutive tokens: [2][rgt][pe]
+    // floats (cos then sin each); consecutive groups alternate
     float* const rope_g = reinterpret_cast<float*>(reinterpret_cast<char*>(wl) + C::aux_bytes(nope, pe));
 
     const int d = nope + pe, h2 = pe >> 1;
@@ -1715,8 +1717,11 @@ hipError_t launch_rope_apply(const uint16_t* X, const float* rcos, const float* 
 // ---------------------------------------------------------------------------
 // small head counts (nh <= 4): plain fp32 vector arithmetic
 //
-// With a handful of heads the head mix is a few multiply-adds per element and
-// 32-row MFMA tiles would be mostly padding, so these kernels use VALU FMAs.
+// With a handful of heads the head mix is a few multiply-adds per element, so
+// these kernels use VALU FMAs.  The tiled kernels pack several tokens per
+// MFMA tile instead and are faster where they apply (channels in 128- or
+// 256-channel parts); these serve the other shapes (d not a multiple of 128,
+// or pe wider than a part).
 // Workgroup = R consecutive tokens, R = max(1, 512 / (d/8)).  Work items: the
 // R*nope/8 nope vectors of the R tokens first, then the R*pe/8 pe vectors, so
 // that (at d = 512) whole waves take one path.  A work item is one 8-channel
@@ -2156,7 +2161,8 @@ bool bwd_fused_applies(int nh, int nope, int pe) {
     const int d = nope + pe;
     if (nh < 1 || d % 128 != 0 || pe > 128 || d > (1 << 24)) return false;
     // several tokens per 64-row chunk (nh <= 32; at most a cos/sin group of them),
-    // head rows padded to 64 (32 < nh <= 64), or to 128 (pe rotated in registers only)
+    // head rows padded to 64 (32 < nh <= 64), or to 128 (pe rotated in registers only);
+    // the LDS (chunk buffers, W or the pe scratch, two cos/sin groups) must fit
     size_t lds;
     if (nh <= 64) {
         const int tp = bwd_fused_tokens_per_chunk(nh, nope, pe);
