@@ -136,7 +136,7 @@ int postmix_bwd_dw(const pm_bf16 *dY, const pm_bf16 *O, const float *rope_cos,
  * Backward, both gradients in one call: dO as postmix_bwd_dx and dW as
  * postmix_bwd_dw, from a single pass over dY and O where the shape allows
  * (nope + pe a multiple of 128 and at most 2^24, pe <= 128, W 16-byte
- * aligned, and nh <= 64 with at most 32 tokens per 64-row chunk (for nh = 1
+ * aligned if nh is 64 or 128, and nh <= 64 with at most 32 tokens per 64-row chunk (for nh = 1
  * that needs pe >= 64, or pe >= 32 with 128-channel chunks, i.e. nope + pe
  * not a multiple of 256), or 64 < nh <= 128 with pe and nope multiples of
  * 32): each (token, channel chunk) of dY and O is read from HBM

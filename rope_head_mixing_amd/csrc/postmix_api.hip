@@ -342,7 +342,10 @@ int postmix_bwd(const pm_bf16* dY, const pm_bf16* O, const pm_bf16* W, const flo
     a.partials = (float*)workspace;
     a.force_general = mx.force_general;
     hipError_t e;
-    if (!mx.force_general && ((uintptr_t)W & 15u) == 0 && pm::bwd_fused_applies(nh, nope, pe)) {
+    // the fused kernel reads W with 16-byte loads only when nh fills its 64 or
+    // 128 head rows exactly; padded and packed head counts read it element-wise
+    const bool w_ok = ((uintptr_t)W & 15u) == 0 || (nh != 64 && nh != 128);
+    if (!mx.force_general && w_ok && pm::bwd_fused_applies(nh, nope, pe)) {
         e = pm::launch_bwd_fused(mx, a, (hipStream_t)stream);
     } else {
         e = pm::launch_mix(mx, true, (hipStream_t)stream);

@@ -282,7 +282,9 @@ def test_out_of_range_positions_are_clamped_not_read_out_of_bounds():
     gu.check_bf16(gu.host_bits(Y), ref, "clamped positions")
 
 
-@pytest.mark.parametrize("nh", [64, 20, 8])  # general kernels; padded (and token-packed) tiles reading W element-wise
+# nh = 64: general dx kernel and two separate calls; nh = 20 and 8: padded or
+# token-packed tiles and the fused backward, reading W element-wise
+@pytest.mark.parametrize("nh", [64, 20, 8])
 def test_unaligned_W(nh):
     """W that is 2-byte but not 16-byte aligned: results on the oracle."""
     import torch
@@ -296,6 +298,8 @@ def test_unaligned_W(nh):
     gu.check_bf16(gu.host_bits(Y), oracle.fwd(dv.O, dv.W, dv.pos, c.theta, c.nope, c.pe), "Y, W+2")
     dO, dW = P().postmix_bwd(dv.ddY_, dv.dO_, Wv, dv.cos, dv.sin, dv.dpos, c.nope, c.pe)
     gu.check_bf16(gu.host_bits(dO), oracle.bwd_dx(dv.dY, dv.W, dv.pos, c.theta, c.nope, c.pe), "dO, W+2")
+    dO_dx = P().postmix_bwd_dx(dv.ddY_, Wv, dv.cos, dv.sin, dv.dpos, c.nope, c.pe)
+    np.testing.assert_array_equal(gu.host_bits(dO), gu.host_bits(dO_dx))
     gu.check_dw(dW.cpu().numpy(), oracle.bwd_dw(dv.dY, dv.O, dv.pos, c.theta, c.nope, c.pe), "dW, W+2")
 
 
