@@ -1223,14 +1223,21 @@ struct BwdCfg {
     // least 16 tokens; at most 32
     __host__ __device__ static int rope_group(int tp) { return tp * ((16 + tp - 1) / tp); }
     static constexpr int RG_MAX = 32;
-    // dY chunk, O chunk, dO chunk, then W / pe scratch, then two buffers of
-    // the cos and sin rows of rgt tokens
-    __host__ __device__ static size_t lds_bytes(int nope, int pe, int rgt = 16) {
-        return (size_t)3 * NH * PITCH * 2 + aux_bytes(nope, pe) + (size_t)2 * rgt * pe * 4;
+    // buffers of staged cos/sin groups: two (the next group is fetched while
+    // the store phase of the current chunk may still read its rows); one at
+    // NH = 128, whose pe is always rotated in registers, so its store phase
+    // reads none
+    static constexpr int NBUF = NH == 128 ? 1 : 2;
+    // dY chunk, O chunk, dO chunk, then W / pe scratch, then the buffers of
+    // the cos and sin rows of rgt tokens, then (ps) the lo parts of the
+    // weight gradient's rotated pe operand, [NH][pe + 8] bf16
+    __host__ __device__ static size_t lds_bytes(int nope, int pe, int rgt, bool ps) {
+        return (size_t)3 * NH * PITCH * 2 + aux_bytes(nope, pe) + (size_t)NBUF * rgt * pe * 4 +
+               (ps && pe > 0 ? (size_t)NH * (pe + 8) * 2 : 0);
     }
 };
 
-template <int NH, int CH, int WAVES, bool PAD>
+template <int NH, int CH, int WAVES, bool PAD, bool PS>
 __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O, const uint16_t* __restrict__ W,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
@@ -1244,6 +1251,9 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     using C = BwdCfg<NH, CH, WAVES>;
     const int tp = PAD ? ptok : 1;
     // rgt: tokens per staged group of cos/sin rows, a multiple of tp
+    // PS: the weight gradient's rotated pe operand is formed once per chunk
+    // (hi in place of the staged O, lo in lol) instead of in each k-step
+    // that reads it, i.e. by every wave of the tile's row block
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint16_t* dyl = smem;                               // [NH][PITCH]
     uint16_t* ol = dyl + NH * C::PITCH;                 // [NH][PITCH]
@@ -1256,6 +1266,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     float* const rope_g = reinterpret_cast<float*>(reinterpret_cast<char*>(wl) + C::aux_bytes(nope, pe));
 
     const int d = nope + pe, h2 = pe >> 1;
+    const int lpitch = pe + 8;
     const int cpt = d / CH;
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, Q = half;
     const int wave = tid >> 6;
@@ -1279,7 +1290,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     // past the last token are zeros: the padding rows of a partial chunk
     // rotate zeros with them, and their products must stay exact zeros.
     auto load_rope_group = [&](int64_t s0, int buf) {
-        float* const rg = rope_g + buf * rgt * pe;
+        float* const rg = rope_g + (C::NBUF == 2 ? buf : 0) * rgt * pe;
         int64_t n = s_end - s0;
         if (n > rgt) n = rgt;
         const int q4 = pe >> 2, half4 = pe >> 3;  // f32x4 per token row (cos + sin), per table row
@@ -1382,8 +1393,44 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         const bool chunk_pe = pe > 0 && c_base + CH > nope;
         // cos/sin rows of the chunk's first token; a row r of the chunk uses those of token r / nh
         const int tok = (k / cpt) * tp;  // the chunk's first token within the block
-        const float* csl = rope_g + (((tok / rgt) & 1) * rgt + tok % rgt) * pe;
+        const float* csl = rope_g + ((C::NBUF == 2 ? (tok / rgt) & 1 : 0) * rgt + tok % rgt) * pe;
         const float* snl = csl + (pe >> 1);
+        uint16_t* const lol = reinterpret_cast<uint16_t*>(rope_g + C::NBUF * rgt * pe);  // [NH][pe + 8]
+
+        // ---- PS: the chunk's rotated pe operand, once.  A task is a row and
+        // 8 channels i .. i+7 of the first half with their partners i+h2 ..:
+        // both halves are read and written by the same thread.
+        if (PS && chunk_pe) {
+            const int L0 = nope - c_base;  // local first pe channel (the whole pe range is in this chunk)
+            const int vh = h2 >> 3;
+            for (int task = tid; task < NH * vh; task += C::NT) {
+                const int row = task / vh, i = 8 * (task - row * vh);
+                uint16_t* const o1 = ol + row * C::PITCH + L0 + i;
+                uint16_t* const o2 = o1 + h2;
+                const u32x4 a = *reinterpret_cast<const u32x4*>(o1), b = *reinterpret_cast<const u32x4*>(o2);
+                int p = PAD ? row / nh : 0;
+                p = p < tp ? p : tp - 1;
+                const float* cr = csl + p * pe + i;
+                const f32x4 c0 = *reinterpret_cast<const f32x4*>(cr), c1 = *reinterpret_cast<const f32x4*>(cr + 4);
+                const f32x4 s0 = *reinterpret_cast<const f32x4*>(cr + h2), s1 = *reinterpret_cast<const f32x4*>(cr + h2 + 4);
+                float cs[8], sp[8], sm[8];
+                uint32_t aw[4], bw[4], h1[4], l1[4], hh2[4], ll2[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    cs[e] = c0[e]; cs[4 + e] = c1[e];
+                    sp[e] = s0[e]; sp[4 + e] = s1[e];
+                    sm[e] = -s0[e]; sm[4 + e] = -s1[e];
+                    aw[e] = a[e]; bw[e] = b[e];
+                }
+                rotate_split8(aw, bw, cs, sp, h1, l1);   // first half: a C + b S
+                rotate_split8(bw, aw, cs, sm, hh2, ll2);  // second half: b C - a S
+                *reinterpret_cast<u32x4*>(o1) = u32x4{h1[0], h1[1], h1[2], h1[3]};
+                *reinterpret_cast<u32x4*>(o2) = u32x4{hh2[0], hh2[1], hh2[2], hh2[3]};
+                *reinterpret_cast<u32x4*>(lol + row * lpitch + i) = u32x4{l1[0], l1[1], l1[2], l1[3]};
+                *reinterpret_cast<u32x4*>(lol + row * lpitch + h2 + i) = u32x4{ll2[0], ll2[1], ll2[2], ll2[3]};
+            }
+            __syncthreads();
+        }
 
         // ---- weight gradient: tile (gb, hb), k-steps t = kset, kset + 2, ...
 #pragma unroll
@@ -1397,6 +1444,11 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             const bool step_pe = chunk_pe && c_base + 16 * t + 16 > nope;  // wave-uniform
             if (!step_pe) {
                 acc_w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(own), acc_w, 0, 0, 0);
+            } else if (PS) {  // hi formed in place of O, lo beside it
+                u32x4 lo = {0u, 0u, 0u, 0u};
+                if (cg >= nope) lo = *reinterpret_cast<const u32x4*>(lol + h * lpitch + (cg - nope));
+                acc_w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(own), acc_w, 0, 0, 0);
+                acc_w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(lo), acc_w, 0, 0, 0);
             } else {
                 u32x4 hi = own, lo = {0u, 0u, 0u, 0u};
                 if (cg >= nope) {
@@ -2168,11 +2220,11 @@ bool bwd_fused_applies(int nh, int nope, int pe) {
         const int tp = bwd_fused_tokens_per_chunk(nh, nope, pe);
         if (tp > BwdCfg<64, 128, 8>::RG_MAX) return false;
         const int rgt = BwdCfg<64, 128, 8>::rope_group(tp);
-        lds = bwd_fused_chunk(d) == 256 ? BwdCfg<64, 256, 16>::lds_bytes(nope, pe, rgt)
-                                        : BwdCfg<64, 128, 8>::lds_bytes(nope, pe, rgt);
+        lds = bwd_fused_chunk(d) == 256 ? BwdCfg<64, 256, 16>::lds_bytes(nope, pe, rgt, false)
+                                        : BwdCfg<64, 128, 8>::lds_bytes(nope, pe, rgt, false);
     } else {
         if (!(pe == 0 || pe_pairs_in_blocks(nope, pe))) return false;
-        lds = BwdCfg<128, 128, 16>::lds_bytes(nope, pe, BwdCfg<128, 128, 16>::rope_group(1));
+        lds = BwdCfg<128, 128, 16>::lds_bytes(nope, pe, BwdCfg<128, 128, 16>::rope_group(1), false);
     }
     return lds <= kMaxLds;
 }
@@ -2182,18 +2234,26 @@ static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int tpb
                                      hipStream_t stream) {
     using C = BwdCfg<NH, CH, WAVES>;
     const bool pad = a.nh != NH;
-    auto kern = pad ? bwd_fused_kernel<NH, CH, WAVES, true> : bwd_fused_kernel<NH, CH, WAVES, false>;
-    static bool attr_done[2] = {false, false};  // idempotent; a race only repeats the call
-    if (!attr_done[pad]) {
-        size_t lds_max = C::lds_bytes(8, 128, C::RG_MAX);  // largest: pe = 128 with the scratch
+    const int rgt = C::rope_group(tp);
+    // The pe operand formed once per chunk (where its lo area fits the LDS):
+    // at NH = 128 four waves per row block each rotated it in four k-steps
+    // per chunk (rotation 70 us of 721 us at sq = 8192), and this takes the
+    // backward from 732 to 712 us.  At NH = 64 its registers pushed spill
+    // reloads into the chunk loop (535 -> 730 us), so it is not compiled there.
+    constexpr bool PS_OK = NH == 128;
+    const bool ps = PS_OK && C::lds_bytes(a.nope, a.pe, rgt, true) <= kMaxLds;
+    auto kern = pad ? (ps ? bwd_fused_kernel<NH, CH, WAVES, true, PS_OK> : bwd_fused_kernel<NH, CH, WAVES, true, false>)
+                    : (ps ? bwd_fused_kernel<NH, CH, WAVES, false, PS_OK> : bwd_fused_kernel<NH, CH, WAVES, false, false>);
+    static bool attr_done[2][2] = {{false, false}, {false, false}};  // idempotent; a race only repeats the call
+    if (!attr_done[pad][ps]) {
+        size_t lds_max = C::lds_bytes(8, 128, C::RG_MAX, true);  // largest: pe = 128 with the scratch
         if (lds_max > kMaxLds) lds_max = kMaxLds;
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)lds_max);
         if (e != hipSuccess) return e;
-        attr_done[pad] = true;
+        attr_done[pad][ps] = true;
     }
-    const int rgt = C::rope_group(tp);
-    const size_t lds = C::lds_bytes(a.nope, a.pe, rgt);
+    const size_t lds = C::lds_bytes(a.nope, a.pe, rgt, ps);
     if (lds > kMaxLds) return hipErrorInvalidValue;  // excluded by bwd_fused_applies
     hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), lds, stream, a.dY, a.O, mx.W, a.rcos, a.rsin,
                        a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, mx.Out, a.partials, tpb, tp, rgt);
