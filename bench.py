@@ -36,7 +36,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # kernels behind each op at nh=64, d=512 (tiled path)
 KERNELS_NH64 = {
     "fwd": "mix_part_kernel<64, 256, 8, false, 1, false>",
-    "bwd": "bwd_fused_kernel<64, 256, 16, false> + dw_reduce_kernel",
+    "bwd": "bwd_fused_kernel<64, 256, 16, false, false> + dw_reduce_kernel",
     "bwd_dx": "mix_part_kernel<64, 256, 8, true, 1, false>",
     "bwd_dw": "dw_chunk_kernel<64, 128, false> + dw_reduce_kernel",
 }
