@@ -1,0 +1,62 @@
+"""Seeded random shapes through every route of the gfx950 path, against the
+fp64 oracle.
+
+The hand-picked cases of test_parity_gpu.py aim at one route each; this sweep
+draws head counts from 2 to 128 (padded rows, several tokens per tile, 96- and
+128-row tiles), channel splits with and without d a multiple of 128 (tiled and
+general kernels), pe from 0 to 256 and short ragged token counts.  Each shape
+runs the forward, dx, dW and the single-call backward, each checked against
+the oracle, and the single-call dO must equal postmix_bwd_dx's bit for bit.
+
+nh = 1 is left to its own cases: a single dW entry can cancel to far below
+the sum of its terms' magnitudes, where no fp32 accumulation meets a relative
+tolerance (see the near-cancelled case in test_parity_gpu.py).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from rope_head_mixing_amd import synthetic
+from tests import gpu_util as gu
+from tests.test_parity_gpu import Dev
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gu.has_gfx950(), reason="needs an MI355X (gfx950)")]
+
+
+def _shapes(n: int, seed: int = 20261202):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        nh = int(rng.integers(2, 129))
+        if rng.random() < 0.6:  # d a multiple of 128: the tiled kernels
+            d = int(rng.choice([128, 256, 384, 512, 640]))
+            pe = 16 * int(rng.integers(0, min(d, 256) // 16 + 1))
+        else:
+            d = 8 * int(rng.integers(1, 80))
+            pe = 16 * int(rng.integers(0, min(d, 256) // 16 + 1))
+        nope = d - pe
+        sq = int(rng.integers(1, 61 if nh <= 64 else 21))
+        off = int(rng.integers(0, 30000))
+        out.append((sq, nh, nope, pe, off))
+    return out
+
+
+SHAPES = _shapes(120)
+
+
+@pytest.mark.parametrize("sq,nh,nope,pe,off", SHAPES)
+def test_random_shape(sq, nh, nope, pe, off):
+    c = synthetic.case(sq, nh, nope, pe, seed=7000 + 13 * sq + nh, pos_offset=off)
+    print(f"\n[parity] random {c.name} off={off}", flush=True)
+    dv = Dev(c)
+    Y = gu.host_bits(dv.fwd())
+    gu.check_bf16(Y, oracle.fwd(dv.O, dv.W, dv.pos, c.theta, nope, pe), f"{c.name} Y")
+    dO_dx = gu.host_bits(dv.dx())
+    ref_dO = oracle.bwd_dx(dv.dY, dv.W, dv.pos, c.theta, nope, pe)
+    gu.check_bf16(dO_dx, ref_dO, f"{c.name} dO")
+    ref_dW = oracle.bwd_dw(dv.dY, dv.O, dv.pos, c.theta, nope, pe)
+    gu.check_dw(dv.dw().cpu().numpy(), ref_dW, f"{c.name} dW")
+    dO, dW = dv.bwd()
+    np.testing.assert_array_equal(gu.host_bits(dO), dO_dx)
+    gu.check_dw(dW.cpu().numpy(), ref_dW, f"{c.name} bwd dW")
