@@ -1351,8 +1351,19 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     if (nchunks > 0) load_chunk(0);
     if (pe > 0 && nchunks > 0) load_rope_group(s_begin, 0);
 
-    // W -> LDS -> this wave's dx B operand (B[k=g][n=h] = W[g][h], N-block nb)
-    if (!PAD) {
+    // W -> LDS -> this wave's dx B operand (B[k=g][n=h] = W[g][h], N-block nb).
+    // W resident in LDS (NH = 128) is stored transposed, [h][g]: a lane's B
+    // fragment (column h, 8 consecutive g) is then one 16-byte read per use.
+    if (C::WRES) {
+        for (int q = tid; q < NH * NH; q += C::NT) {
+            const int row = q / NH, col = q % NH;  // W[row][col] -> wl[col][row]
+            const int p = row / nh, pc = col / nh;
+            uint16_t w = 0;
+            if (!PAD) w = W[q];
+            else if (p == pc && p < tp) w = W[(row - p * nh) * nh + (col - p * nh)];
+            wl[col * C::WPITCH + row] = w;
+        }
+    } else if (!PAD) {
         for (int q = tid; q < NH * NH / 8; q += C::NT) {
             const int row = q / (NH / 8), c8 = q % (NH / 8);
             *reinterpret_cast<u32x4*>(wl + row * C::WPITCH + 8 * c8) = reinterpret_cast<const u32x4*>(W)[q];
@@ -1493,7 +1504,8 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
                 af[kb] = tr_frag2(dyl + (16 * kb) * C::PITCH, clo, chi, C::PITCH, lane);
 #pragma unroll
             for (int kb = 0; kb < C::KB; ++kb) {
-                const bf16x8 b = C::WRES ? tr_frag(wl + (16 * kb) * C::WPITCH + 32 * nb, C::WPITCH, lane)
+                const bf16x8 b = C::WRES ? *reinterpret_cast<const bf16x8*>(wl + (32 * nb + (lane & 31)) * C::WPITCH +
+                                                                            16 * kb + 8 * (lane >> 5))
                                          : wf[C::WRES ? 0 : kb];
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], b, acc, 0, 0, 0);
             }
