@@ -14,9 +14,9 @@ Entry points keep the C names:
     postmix_rope_table(theta, pe, table_rows, device=None)
     postmix_kv_index_remap(idx, sq, seqlen_kv, pad_value=-1, out=None)
     postmix_rope_apply(X, rope_cos, rope_sin, positions, nope, pe, direction, out=None)
+    postmix_set_general_kernels(enable)
 The unfused comparison route (unfused_fwd, unfused_bwd) is composed of these
 entry points only.
-    postmix_set_general_kernels(enable)
 Tensors: O/Y/dY/dO bfloat16 [sq, nh, nope+pe]; W bfloat16 [nh, nh] (W[g,h], g =
 output head); rope_cos/rope_sin float32 [rows, pe/2]; positions int32 [sq];
 dW float32 [nh, nh].  Dtype mismatches raise ValueError naming the tensor (the
