@@ -699,7 +699,8 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
 
     const int d = nope + pe;
     const int h2 = pe >> 1;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
 
     int64_t t = blockIdx.x;
     u32x4 v[C::VPT];
@@ -956,7 +957,8 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
 
     const int d = nope + pe, h2 = pe >> 1;
     const int cpt = d / CH;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
     const int gb0 = C::SPLIT_K ? 0 : C::TG * (wave / (C::NB / C::TH));
     const int hb0 = C::SPLIT_K ? 0 : C::TH * (wave % (C::NB / C::TH));
 
@@ -1269,7 +1271,11 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     const int lpitch = pe + 8;
     const int cpt = d / CH;
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, Q = half;
-    const int wave = tid >> 6;
+    // the wave index in a scalar register frees the vector registers of its
+    // derived indices (tile, k-set, blocks), which otherwise spill at 64 rows;
+    // at 128 rows the compiler then spills other values inside the chunk
+    // loop, so the index stays a vector value there
+    const int wave = C::WRES ? tid >> 6 : __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile = wave % C::NTILE, kset = wave / C::NTILE;
     const int gb = tile / C::NB, hb = tile % C::NB;
     const int mb = wave % C::MBC, nb = wave / C::MBC;
