@@ -52,13 +52,15 @@ __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) {
     return (lo16 & 0xffffu) | (hi16 << 16);
 }
 
-// Weight-gradient pe operand of 8 channels: x_k = a_k C_k + b_k S_k (own
-// value a, rotation partner b, S already signed), split into the bf16 pair
-// hi = RNE(x), lo = RNE(x - hi) of the compensated product.
-__device__ __forceinline__ void rotate_split8(const uint32_t* own, const uint32_t* par, const float* cs,
-                                              const float* sn, uint32_t* hi, uint32_t* lo) {
+// Weight-gradient pe operand of 2*NW channels (NW packed bf16 pairs):
+// x_k = a_k C_k + b_k S_k (own value a, rotation partner b, S already
+// signed), split into the bf16 pair hi = RNE(x), lo = RNE(x - hi) of the
+// compensated product.
+template <int NW>
+__device__ __forceinline__ void rotate_split(const uint32_t* own, const uint32_t* par, const float* cs,
+                                             const float* sn, uint32_t* hi, uint32_t* lo) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
+    for (int jj = 0; jj < NW; ++jj) {
         float x[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -71,6 +73,11 @@ __device__ __forceinline__ void rotate_split8(const uint32_t* own, const uint32_
         hi[jj] = h;
         lo[jj] = pack_bf16(x[0] - __uint_as_float(h << 16), x[1] - __uint_as_float(h & 0xffff0000u));
     }
+}
+
+__device__ __forceinline__ void rotate_split8(const uint32_t* own, const uint32_t* par, const float* cs,
+                                              const float* sn, uint32_t* hi, uint32_t* lo) {
+    rotate_split<4>(own, par, cs, sn, hi, lo);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
@@ -1198,9 +1205,15 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
 template <int NH, int CH, int WAVES>
 struct BwdCfg {
     static constexpr int NT = 64 * WAVES;
-    // nh = 128: W stays in LDS and its fragments are read per use (registers
-    // would not hold them beside the rest); only pe rotated in registers
-    static constexpr bool WRES = NH > 64;
+    // nh = 128: the waves split by gradient.  Waves 0 .. WAVES/2-1 own two dW
+    // tiles each, (g-blocks 2(v/4), 2(v/4)+1; h-block v%4), over every
+    // k-step; waves WAVES/2 .. own two dx M-blocks each (2(v/4), 2(v/4)+1;
+    // N-block v%4) with their N-block's W fragments in registers.  Both keep
+    // 32 registers across the chunk loop (two accumulators, or eight W
+    // fragments), in one shared array.  Against one dW tile and one dx block
+    // on every wave with W read from LDS per use, the compute phase reads
+    // ~40% less LDS.  Only pe rotated in registers.
+    static constexpr bool SPLIT = NH == 128;
     static constexpr int NB = NH / 32, KB = NH / 16;
     static constexpr int PITCH = CH + 8;
     static constexpr int WPITCH = NH + 8;
@@ -1214,12 +1227,12 @@ struct BwdCfg {
     static constexpr int KSET = WAVES / NTILE;      // waves per dW tile
     static_assert((NH == 64 || NH == 128) && MBC * NB == WAVES && KSET >= 1 && KS % KSET == 0 &&
                   VPO % NT == 0, "fused shape");
-    // W and the fp32 pe scratch, overlapped (W is consumed at set-up) unless W
-    // stays resident; the scratch is not needed for pe rotated in registers
+    // W and the fp32 pe scratch, overlapped (W is consumed at set-up); the
+    // scratch is not needed for pe rotated in registers
     __host__ __device__ static size_t aux_bytes(int nope, int pe) {
         const size_t w = (size_t)NH * WPITCH * 2;
         const size_t p = pe_pairs_in_blocks(nope, pe) ? 0 : (size_t)NH * (pe + 4) * 4;
-        return WRES ? w + p : (w > p ? w : p);
+        return w > p ? w : p;
     }
     // tokens per group of staged cos/sin rows: whole chunks of tp tokens, at
     // least 16 tokens; at most 32
@@ -1261,7 +1274,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     uint16_t* ol = dyl + NH * C::PITCH;                 // [NH][PITCH]
     uint16_t* dol = ol + NH * C::PITCH;                 // [NH][PITCH]
     uint16_t* wl = dol + NH * C::PITCH;                 // [NH][WPITCH] bf16, then:
-    float* pes = reinterpret_cast<float*>(wl + (C::WRES ? NH * C::WPITCH : 0));  // [NH][pe + 4] fp32
+    float* pes = reinterpret_cast<float*>(wl);          // [NH][pe + 4] fp32, after set-up
     const int pes_pitch = pe + 4;
     // two buffers of the cos/sin rows of rgt consecutive tokens: [2][rgt][pe]
     // floats (cos then sin each); consecutive groups alternate
@@ -1272,13 +1285,15 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     const int cpt = d / CH;
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, Q = half;
     // the wave index in a scalar register frees the vector registers of its
-    // derived indices (tile, k-set, blocks), which otherwise spill at 64 rows;
-    // at 128 rows the compiler then spills other values inside the chunk
-    // loop, so the index stays a vector value there
-    const int wave = C::WRES ? tid >> 6 : __builtin_amdgcn_readfirstlane(tid >> 6);
+    // derived indices (tile, k-set, blocks), which otherwise spill
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile = wave % C::NTILE, kset = wave / C::NTILE;
-    const int gb = tile / C::NB, hb = tile % C::NB;
-    const int mb = wave % C::MBC, nb = wave / C::MBC;
+    // SPLIT: dw_role waves own dW tiles (gb, hb), (gb + 1, hb); the others
+    // dx M-blocks mb, mb + 1 of N-block nb
+    const bool dw_role = !C::SPLIT || wave < WAVES / 2;
+    const int vs = wave % (WAVES / 2);
+    const int gb = C::SPLIT ? 2 * (vs / C::NB) : tile / C::NB, hb = C::SPLIT ? vs % C::NB : tile % C::NB;
+    const int mb = C::SPLIT ? 2 * (vs / C::NB) : wave % C::MBC, nb = C::SPLIT ? vs % C::NB : wave / C::MBC;
     // offsets into a chunk's cos/sin rows of the tokens of this lane's dW row
     // (32*hb + lane%32) and dx row (32*nb + lane%32); padding rows take any
     // staged token's
@@ -1358,9 +1373,9 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     if (pe > 0 && nchunks > 0) load_rope_group(s_begin, 0);
 
     // W -> LDS -> this wave's dx B operand (B[k=g][n=h] = W[g][h], N-block nb).
-    // W resident in LDS (NH = 128) is stored transposed, [h][g]: a lane's B
-    // fragment (column h, 8 consecutive g) is then one 16-byte read per use.
-    if (C::WRES) {
+    // SPLIT stages W transposed, [h][g]: a lane's B fragment (column h, 8
+    // consecutive g) is then one 16-byte read.
+    if (C::SPLIT) {
         for (int q = tid; q < NH * NH; q += C::NT) {
             const int row = q / NH, col = q % NH;  // W[row][col] -> wl[col][row]
             const int p = row / nh, pc = col / nh;
@@ -1383,12 +1398,25 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         }
     }
     __syncthreads();
-    bf16x8 wf[C::WRES ? 1 : C::KB];  // W fragments in registers, or read from LDS per use
-    if (!C::WRES) {
+    bf16x8 wf[C::SPLIT ? 1 : C::KB];  // W fragments in registers (not SPLIT)
+    // SPLIT: a dW wave's two accumulators, or a dx wave's eight W fragments
+    // (fragment kb in keep[kb / 4], elements 4(kb % 4) ..)
+    f32x16 keep[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) keep[0][r] = keep[1][r] = 0.0f;
+    if (!C::SPLIT) {
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) wf[kb] = tr_frag(wl + (16 * kb) * C::WPITCH + 32 * nb, C::WPITCH, lane);
+    } else if (!dw_role) {
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+            const u32x4 f = *reinterpret_cast<const u32x4*>(wl + (32 * nb + (lane & 31)) * C::WPITCH + 16 * kb +
+                                                            8 * (lane >> 5));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) keep[kb >> 2][4 * (kb & 3) + e] = __uint_as_float(f[e]);
+        }
     }
-    __syncthreads();  // W's LDS becomes the pe scratch (unless W stays resident)
+    __syncthreads();  // W's LDS becomes the pe scratch
 
     f32x16 acc_w;
 #pragma unroll
@@ -1415,111 +1443,150 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         uint16_t* const lol = reinterpret_cast<uint16_t*>(rope_g + C::NBUF * rgt * pe);  // [NH][pe + 8]
 
         // ---- PS: the chunk's rotated pe operand, once.  A task is a row and
-        // 8 channels i .. i+7 of the first half with their partners i+h2 ..:
-        // both halves are read and written by the same thread.
+        // 4 channels i .. i+3 of the first half with their partners i+h2 ..:
+        // both halves are read and written by the same thread (4 channels,
+        // not 8: this phase sets the kernel's register peak)
         if (PS && chunk_pe) {
             const int L0 = nope - c_base;  // local first pe channel (the whole pe range is in this chunk)
-            const int vh = h2 >> 3;
+            const int vh = h2 >> 2;
             for (int task = tid; task < NH * vh; task += C::NT) {
-                const int row = task / vh, i = 8 * (task - row * vh);
+                const int row = task / vh, i = 4 * (task - row * vh);
                 uint16_t* const o1 = ol + row * C::PITCH + L0 + i;
                 uint16_t* const o2 = o1 + h2;
-                const u32x4 a = *reinterpret_cast<const u32x4*>(o1), b = *reinterpret_cast<const u32x4*>(o2);
+                const uint2 a = *reinterpret_cast<const uint2*>(o1), b = *reinterpret_cast<const uint2*>(o2);
                 int p = PAD ? row / nh : 0;
                 p = p < tp ? p : tp - 1;
                 const float* cr = csl + p * pe + i;
-                const f32x4 c0 = *reinterpret_cast<const f32x4*>(cr), c1 = *reinterpret_cast<const f32x4*>(cr + 4);
-                const f32x4 s0 = *reinterpret_cast<const f32x4*>(cr + h2), s1 = *reinterpret_cast<const f32x4*>(cr + h2 + 4);
-                float cs[8], sp[8], sm[8];
-                uint32_t aw[4], bw[4], h1[4], l1[4], hh2[4], ll2[4];
+                const f32x4 c4 = *reinterpret_cast<const f32x4*>(cr), s4 = *reinterpret_cast<const f32x4*>(cr + h2);
+                float cs[4], sp[4], sm[4];
+                uint32_t aw[2] = {a.x, a.y}, bw[2] = {b.x, b.y}, h1[2], l1[2], hh2[2], ll2[2];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    cs[e] = c0[e]; cs[4 + e] = c1[e];
-                    sp[e] = s0[e]; sp[4 + e] = s1[e];
-                    sm[e] = -s0[e]; sm[4 + e] = -s1[e];
-                    aw[e] = a[e]; bw[e] = b[e];
+                    cs[e] = c4[e];
+                    sp[e] = s4[e];
+                    sm[e] = -s4[e];
                 }
-                rotate_split8(aw, bw, cs, sp, h1, l1);   // first half: a C + b S
-                rotate_split8(bw, aw, cs, sm, hh2, ll2);  // second half: b C - a S
-                *reinterpret_cast<u32x4*>(o1) = u32x4{h1[0], h1[1], h1[2], h1[3]};
-                *reinterpret_cast<u32x4*>(o2) = u32x4{hh2[0], hh2[1], hh2[2], hh2[3]};
-                *reinterpret_cast<u32x4*>(lol + row * lpitch + i) = u32x4{l1[0], l1[1], l1[2], l1[3]};
-                *reinterpret_cast<u32x4*>(lol + row * lpitch + h2 + i) = u32x4{ll2[0], ll2[1], ll2[2], ll2[3]};
+                rotate_split<2>(aw, bw, cs, sp, h1, l1);   // first half: a C + b S
+                rotate_split<2>(bw, aw, cs, sm, hh2, ll2);  // second half: b C - a S
+                *reinterpret_cast<uint2*>(o1) = uint2{h1[0], h1[1]};
+                *reinterpret_cast<uint2*>(o2) = uint2{hh2[0], hh2[1]};
+                *reinterpret_cast<uint2*>(lol + row * lpitch + i) = uint2{l1[0], l1[1]};
+                *reinterpret_cast<uint2*>(lol + row * lpitch + h2 + i) = uint2{ll2[0], ll2[1]};
             }
             __syncthreads();
         }
 
-        // ---- weight gradient: tile (gb, hb), k-steps t = kset, kset + 2, ...
-#pragma unroll
-        for (int j = 0; j < C::KS / C::KSET; ++j) {
-            const int t = kset + C::KSET * j;
-            const int c = 16 * t + 8 * half;
-            const int cg = c_base + c;
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(dyl + (32 * gb + (lane & 31)) * C::PITCH + c);
-            const int h = 32 * hb + (lane & 31);
-            const u32x4 own = *reinterpret_cast<const u32x4*>(ol + h * C::PITCH + c);
-            const bool step_pe = chunk_pe && c_base + 16 * t + 16 > nope;  // wave-uniform
-            if (!step_pe) {
-                acc_w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(own), acc_w, 0, 0, 0);
-            } else if (PS) {  // hi formed in place of O, lo beside it
+        // the weight gradient's B operand of a pe k-step: the rotated O rows
+        // (h, channels c .. c+7), split into hi + lo; PS: hi formed in place
+        // of O, lo beside it
+        auto pe_operand = [&](int c, int cg, int h, const u32x4& own, u32x4& hi_out, u32x4& lo_out) {
+            if (PS) {
                 u32x4 lo = {0u, 0u, 0u, 0u};
                 if (cg >= nope) lo = *reinterpret_cast<const u32x4*>(lol + h * lpitch + (cg - nope));
-                acc_w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(own), acc_w, 0, 0, 0);
-                acc_w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(lo), acc_w, 0, 0, 0);
-            } else {
+                hi_out = own;
+                lo_out = lo;
+                return;
+            }
                 u32x4 hi = own, lo = {0u, 0u, 0u, 0u};
-                if (cg >= nope) {
-                    const bool first = cg < nope + h2;
-                    const int i0 = first ? cg - nope : cg - nope - h2;
-                    const float sgn = first ? 1.0f : -1.0f;
-                    const float* cr = csl + ph_off + i0;
-                    const float* sr = snl + ph_off + i0;
-                    const u32x4 par = *reinterpret_cast<const u32x4*>(ol + h * C::PITCH + (first ? c + h2 : c - h2));
-                    const f32x4 c0 = *reinterpret_cast<const f32x4*>(cr), c1 = *reinterpret_cast<const f32x4*>(cr + 4);
-                    const f32x4 s0 = *reinterpret_cast<const f32x4*>(sr), s1 = *reinterpret_cast<const f32x4*>(sr + 4);
-                    float cs[8], sn[8];
-                    uint32_t ow[4], pw[4], hw[4], lw[4];
+            if (cg >= nope) {
+                const bool first = cg < nope + h2;
+                const int i0 = first ? cg - nope : cg - nope - h2;
+                const float sgn = first ? 1.0f : -1.0f;
+                const float* cr = csl + ph_off + i0;
+                const float* sr = snl + ph_off + i0;
+                const u32x4 par = *reinterpret_cast<const u32x4*>(ol + h * C::PITCH + (first ? c + h2 : c - h2));
+                const f32x4 c0 = *reinterpret_cast<const f32x4*>(cr), c1 = *reinterpret_cast<const f32x4*>(cr + 4);
+                const f32x4 s0 = *reinterpret_cast<const f32x4*>(sr), s1 = *reinterpret_cast<const f32x4*>(sr + 4);
+                float cs[8], sn[8];
+                uint32_t ow[4], pw[4], hw[4], lw[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        cs[e] = c0[e]; cs[4 + e] = c1[e];
-                        sn[e] = sgn * s0[e]; sn[4 + e] = sgn * s1[e];
-                        ow[e] = own[e]; pw[e] = par[e];
-                    }
-                    rotate_split8(ow, pw, cs, sn, hw, lw);
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) { hi[jj] = hw[jj]; lo[jj] = lw[jj]; }
+                for (int e = 0; e < 4; ++e) {
+                    cs[e] = c0[e]; cs[4 + e] = c1[e];
+                    sn[e] = sgn * s0[e]; sn[4 + e] = sgn * s1[e];
+                    ow[e] = own[e]; pw[e] = par[e];
                 }
-                acc_w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(hi), acc_w, 0, 0, 0);
-                acc_w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(lo), acc_w, 0, 0, 0);
+                rotate_split8(ow, pw, cs, sn, hw, lw);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) { hi[jj] = hw[jj]; lo[jj] = lw[jj]; }
+            }
+            hi_out = hi;
+            lo_out = lo;
+        };
+
+        if (C::SPLIT && dw_role) {
+            // ---- weight gradient: tiles (gb, hb) and (gb + 1, hb), every k-step
+#pragma unroll
+            for (int t = 0; t < C::KS; ++t) {
+                const int c = 16 * t + 8 * half;
+                const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(dyl + (32 * gb + (lane & 31)) * C::PITCH + c);
+                const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(dyl + (32 * gb + 32 + (lane & 31)) * C::PITCH + c);
+                const int h = 32 * hb + (lane & 31);
+                const u32x4 own = *reinterpret_cast<const u32x4*>(ol + h * C::PITCH + c);
+                const bool step_pe = chunk_pe && c_base + 16 * t + 16 > nope;  // wave-uniform
+                // the branches only form operands: MFMAs under a branch gave
+                // each accumulator a second register copy at the join
+                u32x4 hi = own, lo = {0u, 0u, 0u, 0u};
+                if (step_pe) pe_operand(c, c_base + c, h, own, hi, lo);
+                keep[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, as_bf16x8(hi), keep[0], 0, 0, 0);
+                if (step_pe) keep[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, as_bf16x8(lo), keep[0], 0, 0, 0);
+                keep[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, as_bf16x8(hi), keep[1], 0, 0, 0);
+                if (step_pe) keep[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, as_bf16x8(lo), keep[1], 0, 0, 0);
+            }
+        } else if (!C::SPLIT) {
+            // ---- weight gradient: tile (gb, hb), k-steps t = kset, kset + KSET, ...
+#pragma unroll
+            for (int j = 0; j < C::KS / C::KSET; ++j) {
+                const int t = kset + C::KSET * j;
+                const int c = 16 * t + 8 * half;
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(dyl + (32 * gb + (lane & 31)) * C::PITCH + c);
+                const int h = 32 * hb + (lane & 31);
+                const u32x4 own = *reinterpret_cast<const u32x4*>(ol + h * C::PITCH + c);
+                const bool step_pe = chunk_pe && c_base + 16 * t + 16 > nope;  // wave-uniform
+                if (!step_pe) {
+                    acc_w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(own), acc_w, 0, 0, 0);
+                } else {
+                    u32x4 hi, lo;
+                    pe_operand(c, c_base + c, h, own, hi, lo);
+                    acc_w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(hi), acc_w, 0, 0, 0);
+                    acc_w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(lo), acc_w, 0, 0, 0);
+                }
             }
         }
 
-        // ---- input gradient: M-block mb (channels), N-block nb (heads)
+        // ---- input gradient: M-block m (channels), N-block nb (heads); bfrag(kb)
+        // gives the lane's W fragment of k-block kb
         const bool paired = chunk_pe && pe_pairs_in_blocks(nope, pe);
         const int L = nope - c_base;  // local index of the first pe channel (chunks with pe)
-        {
+        auto dx_block = [&](int m, auto&& bfrag) {
             f32x16 acc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-            const bool pb = paired && 32 * mb >= L;  // a paired pe block (wave-uniform)
-            const int q = mb - (L >> 5);
-            const int clo = pb ? L + 16 * q : 32 * mb, chi = pb ? L + h2 + 16 * q : 32 * mb + 16;
-            bf16x8 af[C::KB];
+            const bool pb = paired && 32 * m >= L;  // a paired pe block (wave-uniform)
+            const int q = m - (L >> 5);
+            const int clo = pb ? L + 16 * q : 32 * m, chi = pb ? L + h2 + 16 * q : 32 * m + 16;
+            if constexpr (C::SPLIT) {  // A fragments one k-block ahead (registers)
+                bf16x8 a = tr_frag2(dyl, clo, chi, C::PITCH, lane);
 #pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb)
-                af[kb] = tr_frag2(dyl + (16 * kb) * C::PITCH, clo, chi, C::PITCH, lane);
+                for (int kb = 0; kb < C::KB; ++kb) {
+                    const bf16x8 an = tr_frag2(dyl + (16 * (kb + 1 < C::KB ? kb + 1 : kb)) * C::PITCH, clo, chi,
+                                               C::PITCH, lane);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bfrag(kb), acc, 0, 0, 0);
+                    a = an;
+                }
+            } else {
+                bf16x8 af[C::KB];
 #pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb) {
-                const bf16x8 b = C::WRES ? *reinterpret_cast<const bf16x8*>(wl + (32 * nb + (lane & 31)) * C::WPITCH +
-                                                                            16 * kb + 8 * (lane >> 5))
-                                         : wf[C::WRES ? 0 : kb];
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], b, acc, 0, 0, 0);
+                for (int kb = 0; kb < C::KB; ++kb)
+                    af[kb] = tr_frag2(dyl + (16 * kb) * C::PITCH, clo, chi, C::PITCH, lane);
+#pragma unroll
+                for (int kb = 0; kb < C::KB; ++kb)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], bfrag(kb), acc, 0, 0, 0);
             }
             const int hrow = 32 * nb + (lane & 31);
             if (pb) rotate_paired_block(acc, dol, C::PITCH, hrow, L, h2, q, Q, csl + pr_off, snl + pr_off, -1.0f);
 #pragma unroll
             for (int a = 0; a < 4 && !pb; ++a) {
-                const int cl = 32 * mb + 8 * a + 4 * Q;
+                const int cl = 32 * m + 8 * a + 4 * Q;
                 const int cg = c_base + cl;
                 if (cg < nope) {
                     uint2 o;
@@ -1531,6 +1598,18 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
                     *reinterpret_cast<f32x4*>(pes + hrow * pes_pitch + (cg - nope)) = o;
                 }
             }
+        };
+        if (!C::SPLIT) {
+            dx_block(mb, [&](int kb) { return wf[C::SPLIT ? 0 : kb]; });
+        } else if (!dw_role) {
+            auto kept = [&](int kb) {
+                u32x4 f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) f[e] = __float_as_uint(keep[kb >> 2][4 * (kb & 3) + e]);
+                return as_bf16x8(f);
+            };
+            dx_block(mb, kept);
+            dx_block(mb + 1, kept);
         }
         __syncthreads();  // dY/O buffers free; dO and the pe scratch complete
         if (k + 1 < nchunks) {
@@ -1585,14 +1664,45 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         __syncthreads();  // dO buffers read; chunk k+1 and its cos/sin rows staged
     }
 
-    // ---- dW partial: the k-sets of each tile summed in k-set order (fixed)
+    // ---- dW partial: the k-sets of each tile summed in k-set order (fixed);
+    // SPLIT: each tile is one wave's (all k-steps)
     float* red = reinterpret_cast<float*>(smem);
-    if (kset != 0) {
+    if (!C::SPLIT && kset != 0) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) red[(((kset - 1) * C::NTILE + tile) * 16 + r) * 64 + lane] = acc_w[r];
     }
     __syncthreads();
-    if constexpr (PAD) {
+    if constexpr (C::SPLIT && PAD) {
+        // the [NH, NH] tile sums to LDS, then the partial's nh x nh corner
+        // (tp = 1 at 128 rows)
+        float* m = red;
+        static_assert(NH * (NH + 1) * 4 <= 3 * NH * C::PITCH * 2, "partial area");
+        if (dw_role) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    m[(32 * (gb + j) + 8 * (r >> 2) + 4 * half + (r & 3)) * (NH + 1) + 32 * hb + (lane & 31)] =
+                        keep[j][r];
+        }
+        __syncthreads();
+        float* part_out = partials + (int64_t)blockIdx.x * nh * nh;
+        for (int idx = tid; idx < nh * nh; idx += C::NT) {
+            const int g = idx / nh, h = idx - g * nh;
+            part_out[idx] = m[g * (NH + 1) + h];
+        }
+        return;
+    } else if constexpr (C::SPLIT) {
+        if (!dw_role) return;
+        float* part_out = partials + (int64_t)blockIdx.x * nh * nh;
+        const int h = 32 * hb + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                part_out[(32 * (gb + j) + 8 * (r >> 2) + 4 * half + (r & 3)) * nh + h] = keep[j][r];
+        return;
+    } else if constexpr (PAD) {
         // the full [NH, NH] sum goes to LDS (after the k-set area), then the
         // partial is the sum of the tp diagonal [nh, nh] blocks, p = 0, 1, ..
         // in order (tp = 1: the block itself)
