@@ -1184,13 +1184,13 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
 // of the shape only), one fp32 weight-gradient partial each, and every
 // (token, CH-channel) chunk of dY and O is staged in LDS once.  CH = 256 with
 // 16 waves (one workgroup per CU) where d allows, else CH = 128 with 8 waves.
-// With KSET = WAVES/4 waves per dW output tile:
+// At 64 head rows, with KSET = WAVES/4 waves per dW output tile:
 //   - dW:  wave w owns output tile w%4 (g-block tile/2, h-block tile%2) over
 //          the k-steps t = w/4 (mod KSET); at the end of the block the KSET
 //          waves of a tile are added in k-set order (fixed);
 //   - dx:  wave w owns M-block w%(CH/32) and N-block w/(CH/32) of the chunk's head mix
 //          dX[c, h] = sum_g dY[g, c] W[g, h] (A = dY^T by transposing LDS
-//          loads, B = W in registers, or read from LDS per use at nh = 128),
+//          loads, B = W in registers),
 //          rotates paired pe blocks by +phi in registers and writes the
 //          results to an LDS output chunk (other pe layouts: an fp32 scratch,
 //          rotated in the store phase); the store phase writes dO rows with
@@ -1198,8 +1198,9 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
 // The dx arithmetic (MFMA inputs, k order, rotation expression, tokens per
 // tile) is that of the token-part kernel, so dO is bitwise the same as
 // postmix_bwd_dx's.  64 head rows (nh <= 32: several tokens per chunk; up to
-// 64: padded), or 128 with pe rotated in registers (16 waves, one dW tile
-// each); d a multiple of 128, pe <= 128 (all pe channels in a token's last chunk).
+// 64: padded), or 128 with pe rotated in registers (16 waves split by
+// gradient, BwdCfg::SPLIT); d a multiple of 128, pe <= 128 (all pe channels
+// in a token's last chunk).
 // ---------------------------------------------------------------------------
 
 template <int NH, int CH, int WAVES>
