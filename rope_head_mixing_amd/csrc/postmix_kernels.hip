@@ -1258,7 +1258,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O, const uint16_t* __restrict__ W,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
     const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe,
-    uint16_t* __restrict__ dO, float* __restrict__ partials, int tokens_per_block, int ptok, int rgt) {
+    uint16_t* __restrict__ dO, float* __restrict__ partials, int64_t ngroups, int ptok, int rgt) {
     // PAD: nh < NH.  A chunk then holds ptok consecutive tokens (ptok*nh
     // consecutive rows of the [sq*nh, d] arrays; W staged block-diagonally,
     // one copy per token, exactly as in the token-part kernel), the other rows
@@ -1301,8 +1301,10 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     int ph = PAD ? (32 * hb + (lane & 31)) / nh : 0, pr = PAD ? (32 * nb + (lane & 31)) / nh : 0;
     const int ph_off = (ph < tp ? ph : tp - 1) * pe, pr_off = (pr < tp ? pr : tp - 1) * pe;
 
-    const int64_t s_begin = (int64_t)blockIdx.x * tokens_per_block;
-    int64_t s_end = s_begin + tokens_per_block;
+    // block b of B = gridDim.x holds the token groups (tp tokens each, one
+    // chunk's rows) [b*G/B, (b+1)*G/B) of the G = ngroups groups
+    const int64_t s_begin = (int64_t)blockIdx.x * ngroups / gridDim.x * tp;
+    int64_t s_end = ((int64_t)blockIdx.x + 1) * ngroups / gridDim.x * tp;
     if (s_end > sq) s_end = sq;
     const int nchunks = (int)((s_end - s_begin + tp - 1) / tp) * cpt;
 
@@ -2254,7 +2256,7 @@ static int bwd_fused_tokens_per_chunk(int nh, int nope, int pe) {
     return nh <= 32 ? mix_tokens_per_tile64(nh, pe, bwd_fused_chunk(nope + pe)) : 1;
 }
 
-// The fused backward uses blocks of half as many tokens as the weight
+// The fused backward aims at blocks of half as many tokens as the weight
 // gradient: sq*max(nh, 64)/65536 rounded up to a multiple of 4 (at least 4),
 // then to a multiple of the tokens per chunk (whole chunks, aligned with the
 // dx tiles).  Its one 16-wave workgroup per CU then works through four rounds
@@ -2269,9 +2271,25 @@ int bwd_fused_tokens_per_block(int64_t sq, int nh, int nope, int pe) {
     return (int)t;
 }
 
+// Blocks of the fused backward.  The count that blocks of
+// bwd_fused_tokens_per_block tokens give is kept unless it leaves the last
+// round of kFusedRound blocks (one workgroup on each of gfx950's 256 CUs)
+// less than three quarters full; then it is rounded to the nearest multiple
+// of kFusedRound and the token groups are spread evenly over the blocks
+// (nh = 96 at 1 GiB: 683 -> 768 blocks, 1000 -> 775 us).  A constant, not
+// the device's CU count: the partition, and with it the weight gradient's
+// summation order, depends on the shape only.
+static constexpr int64_t kFusedRound = 256;
 int64_t bwd_fused_num_blocks(int64_t sq, int nh, int nope, int pe) {
     const int t = bwd_fused_tokens_per_block(sq, nh, nope, pe);
-    return (sq + t - 1) / t;
+    const int tp = bwd_fused_tokens_per_chunk(nh, nope, pe);
+    const int64_t groups = (sq + tp - 1) / tp, per_block = t / tp;
+    int64_t b = (groups + per_block - 1) / per_block;
+    if (b > kFusedRound && b % kFusedRound < kFusedRound * 3 / 4) {
+        b = (b + kFusedRound / 2) / kFusedRound * kFusedRound;
+        if (b > groups) b = groups;
+    }
+    return b;
 }
 
 // Chunk width of the LDS-staged weight-gradient kernel, or 0 for the direct kernel.
@@ -2359,7 +2377,7 @@ bool bwd_fused_applies(int nh, int nope, int pe) {
 }
 
 template <int NH, int CH, int WAVES>
-static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int tpb, int64_t nb, int tp,
+static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int64_t ngroups, int64_t nb, int tp,
                                      hipStream_t stream) {
     using C = BwdCfg<NH, CH, WAVES>;
     const bool pad = a.nh != NH;
@@ -2385,20 +2403,20 @@ static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int tpb
     const size_t lds = C::lds_bytes(a.nope, a.pe, rgt, ps);
     if (lds > kMaxLds) return hipErrorInvalidValue;  // excluded by bwd_fused_applies
     hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), lds, stream, a.dY, a.O, mx.W, a.rcos, a.rsin,
-                       a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, mx.Out, a.partials, tpb, tp, rgt);
+                       a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, mx.Out, a.partials, ngroups, tp, rgt);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_fused(const MixArgs& mx, const DwArgs& a, hipStream_t stream) {
-    const int tpb = bwd_fused_tokens_per_block(a.sq, a.nh, a.nope, a.pe);
     const int64_t nb = bwd_fused_num_blocks(a.sq, a.nh, a.nope, a.pe);
     const int tp = bwd_fused_tokens_per_chunk(a.nh, a.nope, a.pe);
+    const int64_t ngroups = (a.sq + tp - 1) / tp;
     hipError_t err;
     if (a.nh > 64)
-        err = launch_bwd_fused_t<128, 128, 16>(mx, a, tpb, nb, 1, stream);
+        err = launch_bwd_fused_t<128, 128, 16>(mx, a, ngroups, nb, 1, stream);
     else
-        err = bwd_fused_chunk(a.nope + a.pe) == 256 ? launch_bwd_fused_t<64, 256, 16>(mx, a, tpb, nb, tp, stream)
-                                                    : launch_bwd_fused_t<64, 128, 8>(mx, a, tpb, nb, tp, stream);
+        err = bwd_fused_chunk(a.nope + a.pe) == 256 ? launch_bwd_fused_t<64, 256, 16>(mx, a, ngroups, nb, tp, stream)
+                                                    : launch_bwd_fused_t<64, 128, 8>(mx, a, ngroups, nb, tp, stream);
     if (err != hipSuccess) return err;
     const int64_t ne = (int64_t)a.nh * a.nh;
     hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((ne + 63) / 64)), dim3(1024), 0, stream,

@@ -190,6 +190,12 @@ def test_workspace_size_is_a_function_of_the_shape():
     assert L.postmix_bwd_dw_workspace_bytes(8192, 128, 448, 64) == 512 * 128 * 128 * 4
     # nh = 128 with pe = 80 (not fused): the weight-gradient kernels' 256 blocks
     assert L.postmix_bwd_dw_workspace_bytes(8192, 128, 432, 80) == 256 * 128 * 128 * 4
+    # single pass, last round of 256 blocks less than 3/4 full: the block count
+    # goes to the nearest multiple of 256 (547 blocks of 20 tokens -> 512;
+    # 834 of 12 -> 768); otherwise it stays (1000 blocks of 12 tokens)
+    assert L.postmix_bwd_dw_workspace_bytes(10923, 96, 448, 64) == 512 * 96 * 96 * 4
+    assert L.postmix_bwd_dw_workspace_bytes(10000, 64, 448, 64) == 768 * 64 * 64 * 4
+    assert L.postmix_bwd_dw_workspace_bytes(12000, 32, 448, 64) == 1000 * 32 * 32 * 4
     assert L.postmix_bwd_dw_workspace_bytes(0, 64, 448, 64) == 0
     assert L.postmix_bwd_dw_workspace_bytes(16, 0, 448, 64) == 0
     for args in [(64, 4, 48, 16), (8192, 3, 448, 64), (7, 5, 8, 16)]:

@@ -219,6 +219,10 @@ def test_tiled_and_general_kernels_agree(sq, nh, nope, pe):
     # cancel to 6e-5 of the sum of |terms|, below what an fp32 accumulation
     # can resolve to 1e-4 relative)
     (12, 1, 496, 16, 1),        # not fused (nh = 1, pe = 16: 64 tokens would exceed the cos/sin group)
+    # block counts rounded to a multiple of 256, token groups spread evenly
+    (2400, 8, 192, 64, 3),      # 300 blocks of one 8-token chunk -> 256 blocks of 1 or 2 chunks
+    (4800, 64, 192, 64, 11),    # 600 blocks of 8 tokens -> 512 blocks of 9 or 10
+    (1500, 96, 192, 64, 5),     # 375 blocks of 4 tokens -> 256 blocks of 5 or 6 (rows padded to 128)
 ])
 def test_fused_backward_matches_oracle_and_separate_calls(sq, nh, nope, pe, off):
     c = synthetic.case(sq, nh, nope, pe, seed=4000 + sq, pos_offset=off)
@@ -230,7 +234,7 @@ def test_fused_backward_matches_oracle_and_separate_calls(sq, nh, nope, pe, off)
     gu.check_dw(dW, oracle.bwd_dw(dv.dY, dv.O, dv.pos, c.theta, nope, pe), "fused dW")
     # dO is the same computation as postmix_bwd_dx, bit for bit
     np.testing.assert_array_equal(dO, gu.host_bits(dv.dx()))
-    # dW: same blocks, different order inside a block; each repeats bitwise
+    # dW: other token blocks, other order; each repeats bitwise
     dW_sep = dv.dw().cpu().numpy()
     assert np.linalg.norm(dW - dW_sep) <= 1e-5 * np.linalg.norm(dW_sep)
     for _ in range(3):
