@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void dw_partial_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
     const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe,
-    float* __restrict__ partials, int tokens_per_block) {
+    float* __restrict__ partials) {
     constexpr int NB = (NHP + 31) / 32;
     constexpr bool SPLIT_TOKENS = NB <= 2;
     constexpr int TG = SPLIT_TOKENS ? NB : 2;
@@ -357,9 +357,9 @@ __global__ __launch_bounds__(256) void dw_partial_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-    const int64_t s_begin = (int64_t)blockIdx.x * tokens_per_block;
-    int64_t s_end = s_begin + tokens_per_block;
-    if (s_end > sq) s_end = sq;
+    // block b of B = gridDim.x: tokens [b*sq/B, (b+1)*sq/B)
+    const int64_t s_begin = (int64_t)blockIdx.x * sq / gridDim.x;
+    const int64_t s_end = ((int64_t)blockIdx.x + 1) * sq / gridDim.x;
 
     for (int64_t s = s_begin + (SPLIT_TOKENS ? wave : 0); s < s_end; s += (SPLIT_TOKENS ? 4 : 1)) {
         int64_t prow = 0;
@@ -945,7 +945,7 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
     const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe,
-    float* __restrict__ partials, int tokens_per_block, int ptok) {
+    float* __restrict__ partials, int ptok) {
     // PAD: nh < NH.  A chunk then holds ptok consecutive tokens (ptok*nh
     // consecutive rows of the [sq*nh, d] arrays), the rest of its rows are
     // zero padding (not loaded), and the partial is the sum of the ptok
@@ -969,9 +969,9 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
     const int gb0 = C::SPLIT_K ? 0 : C::TG * (wave / (C::NB / C::TH));
     const int hb0 = C::SPLIT_K ? 0 : C::TH * (wave % (C::NB / C::TH));
 
-    const int64_t s_begin = (int64_t)blockIdx.x * tokens_per_block;
-    int64_t s_end = s_begin + tokens_per_block;
-    if (s_end > sq) s_end = sq;
+    // block b of B = gridDim.x: tokens [b*sq/B, (b+1)*sq/B)
+    const int64_t s_begin = (int64_t)blockIdx.x * sq / gridDim.x;
+    const int64_t s_end = ((int64_t)blockIdx.x + 1) * sq / gridDim.x;
     const int nchunks = (int)((s_end - s_begin + tp - 1) / tp) * cpt;
 
     f32x16 acc[C::TG][C::TH];
@@ -2019,18 +2019,18 @@ __global__ __launch_bounds__(512) void small_mix_kernel(
     }
 }
 
-// one weight-gradient partial per block of tokens_per_block tokens; 256 threads
+// one weight-gradient partial per block of tokens (block b of B = gridDim.x:
+// tokens [b*sq/B, (b+1)*sq/B)); 256 threads
 __global__ __launch_bounds__(256) void small_dw_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
-    const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe, int tokens_per_block,
+    const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe,
     float* __restrict__ partials) {
     constexpr int NN = SMALL_NH * SMALL_NH;
     __shared__ float red[NN][256];
     const int d = nope + pe, h2 = pe >> 1, nv = nope >> 3, pv = pe >> 3;
-    const int64_t s0 = (int64_t)blockIdx.x * tokens_per_block;
-    int64_t s1 = s0 + tokens_per_block;
-    if (s1 > sq) s1 = sq;
+    const int64_t s0 = (int64_t)blockIdx.x * sq / gridDim.x;
+    const int64_t s1 = ((int64_t)blockIdx.x + 1) * sq / gridDim.x;
     const int vpr = nv + pv;
     const int64_t n_items = (s1 - s0) * vpr;
     float acc[NN];
@@ -2241,9 +2241,23 @@ int dw_tokens_per_block(int64_t sq, int nh) {
     return (int)t;
 }
 
+// Blocks of the weight-gradient kernels: the count that blocks of
+// dw_tokens_per_block tokens give, unless that leaves the last round of
+// resident workgroups (two per CU up to 64 head rows, one at 128, on
+// gfx950's 256 CUs) less than three quarters full; then it is rounded to the
+// nearest multiple of a round.  The tokens are spread evenly over the blocks
+// (block b holds tokens [b*sq/B, (b+1)*sq/B)).  Constants, not the device's
+// CU count: the partition, and with it the summation order, depends on the
+// shape only.
 int64_t dw_num_blocks(int64_t sq, int nh) {
     const int t = dw_tokens_per_block(sq, nh);
-    return (sq + t - 1) / t;
+    const int64_t round = nh > 64 ? 256 : 512;
+    int64_t b = (sq + t - 1) / t;
+    if (b > round && b % round < round * 3 / 4) {
+        b = (b + round / 2) / round * round;
+        if (b > sq) b = sq;
+    }
+    return b;
 }
 
 // chunk width of the fused backward: 256 channels (16 waves) where d allows
@@ -2319,33 +2333,32 @@ static int dw_tile_heads(int nh, int pe) {
 }
 
 template <int NHC>
-static hipError_t launch_dw_chunk_t(const DwArgs& a, int tpb, int64_t nb, hipStream_t stream) {
+static hipError_t launch_dw_chunk_t(const DwArgs& a, int64_t nb, hipStream_t stream) {
     const bool pad = a.nh != NHC;
     const int tp = pad ? dw_tokens_per_chunk<NHC>(a.nh, a.pe) : 1;
     auto kern = pad ? dw_chunk_kernel<NHC, 128, true> : dw_chunk_kernel<NHC, 128, false>;
     hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(DwCfg<NHC, 128>::NT), 0, stream, a.dY, a.O, a.rcos,
-                       a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, a.partials, tpb, tp);
+                       a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, a.partials, tp);
     return hipGetLastError();
 }
 
 template <int NHP>
 static hipError_t launch_dw_t(const DwArgs& a, hipStream_t stream) {
-    const int tpb = dw_tokens_per_block(a.sq, a.nh);
     const int64_t nb = dw_num_blocks(a.sq, a.nh);
     const int ch = a.force_general ? 0 : dw_chunk_width(a.nh, a.nope, a.pe);
     if (ch == 128) {
         const int nhc = dw_tile_heads(a.nh, a.pe);
-        const hipError_t e = nhc == 32   ? launch_dw_chunk_t<32>(a, tpb, nb, stream)
-                             : nhc == 64 ? launch_dw_chunk_t<64>(a, tpb, nb, stream)
-                                         : launch_dw_chunk_t<128>(a, tpb, nb, stream);
+        const hipError_t e = nhc == 32   ? launch_dw_chunk_t<32>(a, nb, stream)
+                             : nhc == 64 ? launch_dw_chunk_t<64>(a, nb, stream)
+                                         : launch_dw_chunk_t<128>(a, nb, stream);
         if (e != hipSuccess) return e;
     } else if (!a.force_general && a.nh <= SMALL_NH) {
         hipLaunchKernelGGL(small_dw_kernel, dim3((unsigned)nb), dim3(256), 0, stream, a.dY, a.O, a.rcos,
-                           a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, tpb, a.partials);
+                           a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, a.partials);
     } else {
         hipLaunchKernelGGL((dw_partial_kernel<NHP>), dim3((unsigned)nb), dim3(256), 0, stream, a.dY,
                            a.O, a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe,
-                           a.partials, tpb);
+                           a.partials);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

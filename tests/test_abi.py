@@ -196,6 +196,9 @@ def test_workspace_size_is_a_function_of_the_shape():
     assert L.postmix_bwd_dw_workspace_bytes(10923, 96, 448, 64) == 512 * 96 * 96 * 4
     assert L.postmix_bwd_dw_workspace_bytes(10000, 64, 448, 64) == 768 * 64 * 64 * 4
     assert L.postmix_bwd_dw_workspace_bytes(12000, 32, 448, 64) == 1000 * 32 * 32 * 4
+    # the weight-gradient kernels round the same way above 64 heads (one
+    # workgroup per CU): 304 blocks of 36 tokens -> 256; not fused (pe = 80)
+    assert L.postmix_bwd_dw_workspace_bytes(10923, 96, 432, 80) == 256 * 96 * 96 * 4
     assert L.postmix_bwd_dw_workspace_bytes(0, 64, 448, 64) == 0
     assert L.postmix_bwd_dw_workspace_bytes(16, 0, 448, 64) == 0
     for args in [(64, 4, 48, 16), (8192, 3, 448, 64), (7, 5, 8, 16)]:
