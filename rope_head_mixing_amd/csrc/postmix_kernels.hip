@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "postmix_launch.h"
 
 namespace pm {
@@ -2109,6 +2111,24 @@ __global__ __launch_bounds__(256) void small_dw_kernel(
 
 static constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
+// A kernel attribute set once per device: hipFuncSetAttribute acts on the
+// current device, so bit d records device d (devices from 64 on set it on
+// every launch).  Idempotent: a race only repeats the call.
+struct AttrPerDevice {
+    std::atomic<uint64_t> done{0};
+    template <class Set>
+    hipError_t ensure(Set&& set) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+        if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+        e = set();
+        if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+        return e;
+    }
+};
+
 template <int NHP, int MPI, bool DX>
 static hipError_t launch_mix_t(const MixArgs& a, hipStream_t stream) {
     const int d = a.nope + a.pe;
@@ -2137,17 +2157,14 @@ static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
     const int64_t n_tiles = (a.sq + tp - 1) / tp * cpt;
     const size_t lds = C::lds_bytes(a.nope, a.pe, tp);
     auto kern = pad ? mix_part_kernel<NH, CP, WAVES, DX, NS, true> : mix_part_kernel<NH, CP, WAVES, DX, NS, false>;
-    static bool attr_done[2] = {false, false};  // idempotent; a race only repeats the call
-    if (!attr_done[pad]) {
+    static AttrPerDevice attr[2];
+    const hipError_t ae = attr[pad].ensure([&] {
         size_t lds_max = C::lds_bytes(8, CP) + (size_t)C::NT * 16;  // largest: pe = CP with the scratch
         if (lds_max > kMaxLds) lds_max = kMaxLds;  // shapes beyond it are not routed here
-        if (lds_max > 65536) {
-            hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
-            if (e != hipSuccess) return e;
-        }
-        attr_done[pad] = true;
-    }
+        if (lds_max <= 65536) return hipSuccess;
+        return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
+    });
+    if (ae != hipSuccess) return ae;
     hipLaunchKernelGGL(kern, dim3((unsigned)n_tiles), dim3(64 * WAVES), lds, stream, a.X, a.W, a.rcos,
                        a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, cpt, tp, n_tiles, a.Out);
     return hipGetLastError();
@@ -2404,15 +2421,13 @@ static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int64_t
     const bool ps = PS_OK && C::lds_bytes(a.nope, a.pe, rgt, true) <= kMaxLds;
     auto kern = pad ? (ps ? bwd_fused_kernel<NH, CH, WAVES, true, PS_OK> : bwd_fused_kernel<NH, CH, WAVES, true, false>)
                     : (ps ? bwd_fused_kernel<NH, CH, WAVES, false, PS_OK> : bwd_fused_kernel<NH, CH, WAVES, false, false>);
-    static bool attr_done[2][2] = {{false, false}, {false, false}};  // idempotent; a race only repeats the call
-    if (!attr_done[pad][ps]) {
+    static AttrPerDevice attr[2][2];
+    const hipError_t ae = attr[pad][ps].ensure([&] {
         size_t lds_max = C::lds_bytes(8, 128, C::RG_MAX, true);  // largest: pe = 128 with the scratch
         if (lds_max > kMaxLds) lds_max = kMaxLds;
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)lds_max);
-        if (e != hipSuccess) return e;
-        attr_done[pad][ps] = true;
-    }
+        return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
+    });
+    if (ae != hipSuccess) return ae;
     const size_t lds = C::lds_bytes(a.nope, a.pe, rgt, ps);
     if (lds > kMaxLds) return hipErrorInvalidValue;  // excluded by bwd_fused_applies
     hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), lds, stream, a.dY, a.O, mx.W, a.rcos, a.rsin,
