@@ -811,58 +811,131 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
         const bool paired = tile_pe && pe_pairs_in_blocks(nope, pe);
         const int L = nope - c_base;  // local index of the first pe channel (tiles with pe)
 
-        for (int b = wave / NS; b < C::MBP; b += C::MSTEP) {
-            f32x16 acc[C::NBW];
-#pragma unroll
-            for (int j = 0; j < C::NBW; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
-            const bool pb = paired && 32 * b >= L;  // a paired pe block (wave-uniform)
-            const int q = b - (L >> 5);
-            const int clo = pb ? L + 16 * q : 32 * b, chi = pb ? L + h2 + 16 * q : 32 * b + 16;
-            bf16x8 af[C::KB];
-#pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb)
-                af[kb] = tr_frag2(tile + (16 * kb) * C::PITCH, clo, chi, C::PITCH, lane);
-#pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb)
+        if constexpr (NS != 4) {
+            for (int b = wave / NS; b < C::MBP; b += C::MSTEP) {
+                f32x16 acc[C::NBW];
 #pragma unroll
                 for (int j = 0; j < C::NBW; ++j)
-                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], wf[kb][j], acc[j], 0, 0, 0);
-            // with an N split, other waves read this M-block's columns too: all
-            // reads are done before any wave overwrites them with results
-            if (NS > 1) __syncthreads();
-            if (pb) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+                const bool pb = paired && 32 * b >= L;  // a paired pe block (wave-uniform)
+                const int q = b - (L >> 5);
+                const int clo = pb ? L + 16 * q : 32 * b, chi = pb ? L + h2 + 16 * q : 32 * b + 16;
+                bf16x8 af[C::KB];
+#pragma unroll
+                for (int kb = 0; kb < C::KB; ++kb)
+                    af[kb] = tr_frag2(tile + (16 * kb) * C::PITCH, clo, chi, C::PITCH, lane);
+#pragma unroll
+                for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+                    for (int j = 0; j < C::NBW; ++j)
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], wf[kb][j], acc[j], 0, 0, 0);
+                // with an N split, other waves read this M-block's columns too: all
+                // reads are done before any wave overwrites them with results
+                if (NS > 1) __syncthreads();
+                if (pb) {
+#pragma unroll
+                    for (int j = 0; j < C::NBW; ++j) {
+                        const int g = 32 * (ng * C::NBW + j) + (lane & 31);
+                        int p = PAD ? g / nh : 0;  // the row's token within the tile
+                        p = p < tp ? p : tp - 1;   // (padding rows: any staged row)
+                        rotate_paired_block(acc[j], tile, C::PITCH, g, L, h2, q, Q, csl + p * pe, snl + p * pe,
+                                            DX ? -1.0f : 1.0f);
+                    }
+                    continue;
+                }
+                // D register r of lane half Q: channel 32b + 8(r/4) + 4Q + r%4, head 32nb + lane%32
 #pragma unroll
                 for (int j = 0; j < C::NBW; ++j) {
-                    const int g = 32 * (ng * C::NBW + j) + (lane & 31);
-                    int p = PAD ? g / nh : 0;  // the row's token within the tile
-                    p = p < tp ? p : tp - 1;   // (padding rows: any staged row)
-                    rotate_paired_block(acc[j], tile, C::PITCH, g, L, h2, q, Q, csl + p * pe, snl + p * pe,
-                                        DX ? -1.0f : 1.0f);
-                }
-                continue;
-            }
-            // D register r of lane half Q: channel 32b + 8(r/4) + 4Q + r%4, head 32nb + lane%32
+                    const int nb = ng * C::NBW + j;
+                    const int g = 32 * nb + (lane & 31);
 #pragma unroll
-            for (int j = 0; j < C::NBW; ++j) {
-                const int nb = ng * C::NBW + j;
-                const int g = 32 * nb + (lane & 31);
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const int cl = 32 * b + 8 * a + 4 * Q;  // 4 consecutive channels, all nope or all pe
-                    const int cg = c_base + cl;
-                    if (cg < nope) {
-                        uint2 o;
-                        o.x = pack_bf16(acc[j][4 * a], acc[j][4 * a + 1]);
-                        o.y = pack_bf16(acc[j][4 * a + 2], acc[j][4 * a + 3]);
-                        *reinterpret_cast<uint2*>(tile + g * C::PITCH + cl) = o;
-                    } else {
-                        f32x4 o = {acc[j][4 * a], acc[j][4 * a + 1], acc[j][4 * a + 2], acc[j][4 * a + 3]};
-                        *reinterpret_cast<f32x4*>(pes + g * pes_pitch + (cg - nope)) = o;
+                    for (int a = 0; a < 4; ++a) {
+                        const int cl = 32 * b + 8 * a + 4 * Q;  // 4 consecutive channels, all nope or all pe
+                        const int cg = c_base + cl;
+                        if (cg < nope) {
+                            uint2 o;
+                            o.x = pack_bf16(acc[j][4 * a], acc[j][4 * a + 1]);
+                            o.y = pack_bf16(acc[j][4 * a + 2], acc[j][4 * a + 3]);
+                            *reinterpret_cast<uint2*>(tile + g * C::PITCH + cl) = o;
+                        } else {
+                            f32x4 o = {acc[j][4 * a], acc[j][4 * a + 1], acc[j][4 * a + 2], acc[j][4 * a + 3]};
+                            *reinterpret_cast<f32x4*>(pes + g * pes_pitch + (cg - nope)) = o;
+                        }
                     }
                 }
             }
+        } else {
+            // one M-block b: its NBW accumulators (MFMA over the heads), then the
+            // rounded results written over the block's own tile columns (paired
+            // pe blocks rotated in registers first; other pe channels to the fp32
+            // scratch)
+            auto mix_block = [&](int b, f32x16* acc) {
+#pragma unroll
+                for (int j = 0; j < C::NBW; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+                const bool pb = paired && 32 * b >= L;  // a paired pe block (wave-uniform)
+                const int q = b - (L >> 5);
+                const int clo = pb ? L + 16 * q : 32 * b, chi = pb ? L + h2 + 16 * q : 32 * b + 16;
+                bf16x8 af[C::KB];
+#pragma unroll
+                for (int kb = 0; kb < C::KB; ++kb)
+                    af[kb] = tr_frag2(tile + (16 * kb) * C::PITCH, clo, chi, C::PITCH, lane);
+#pragma unroll
+                for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+                    for (int j = 0; j < C::NBW; ++j)
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], wf[kb][j], acc[j], 0, 0, 0);
+            };
+            auto write_block = [&](int b, const f32x16* acc) {
+                const bool pb = paired && 32 * b >= L;
+                const int q = b - (L >> 5);
+                if (pb) {
+#pragma unroll
+                    for (int j = 0; j < C::NBW; ++j) {
+                        const int g = 32 * (ng * C::NBW + j) + (lane & 31);
+                        int p = PAD ? g / nh : 0;  // the row's token within the tile
+                        p = p < tp ? p : tp - 1;   // (padding rows: any staged row)
+                        rotate_paired_block(acc[j], tile, C::PITCH, g, L, h2, q, Q, csl + p * pe, snl + p * pe,
+                                            DX ? -1.0f : 1.0f);
+                    }
+                    return;
+                }
+                // D register r of lane half Q: channel 32b + 8(r/4) + 4Q + r%4, head 32nb + lane%32
+#pragma unroll
+                for (int j = 0; j < C::NBW; ++j) {
+                    const int nb = ng * C::NBW + j;
+                    const int g = 32 * nb + (lane & 31);
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const int cl = 32 * b + 8 * a + 4 * Q;  // 4 consecutive channels, all nope or all pe
+                        const int cg = c_base + cl;
+                        if (cg < nope) {
+                            uint2 o;
+                            o.x = pack_bf16(acc[j][4 * a], acc[j][4 * a + 1]);
+                            o.y = pack_bf16(acc[j][4 * a + 2], acc[j][4 * a + 3]);
+                            *reinterpret_cast<uint2*>(tile + g * C::PITCH + cl) = o;
+                        } else {
+                            f32x4 o = {acc[j][4 * a], acc[j][4 * a + 1], acc[j][4 * a + 2], acc[j][4 * a + 3]};
+                            *reinterpret_cast<f32x4*>(pes + g * pes_pitch + (cg - nope)) = o;
+                        }
+                    }
+                }
+            };
+            // 128 rows: all of the wave's blocks are computed first, then one
+            // barrier, then every result is written.  Their accumulators fit
+            // the registers that the LDS-bound occupancy (two workgroups per
+            // CU) leaves: nh = 128 fwd 392 -> 384 us, nh = 112 507 -> 467 us.
+            // At 96 rows the registers cost a resident workgroup (nh = 80:
+            // 408 -> 551 us), so those keep a barrier per M-block.
+            constexpr int NMB = C::MBP / C::MSTEP;
+            f32x16 acc[NMB][C::NBW];
+#pragma unroll
+            for (int i = 0; i < NMB; ++i) mix_block(wave / NS + i * C::MSTEP, acc[i]);
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < NMB; ++i) write_block(wave / NS + i * C::MSTEP, acc[i]);
         }
         __syncthreads();
 
