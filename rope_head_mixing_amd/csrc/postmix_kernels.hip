@@ -811,7 +811,8 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
         const bool paired = tile_pe && pe_pairs_in_blocks(nope, pe);
         const int L = nope - c_base;  // local index of the first pe channel (tiles with pe)
 
-        if constexpr (NS != 4) {
+        // Padded 96-row tiles keep a barrier per M-block (see below).
+        if constexpr (NS == 1 || (NS == 3 && PAD)) {
             for (int b = wave / NS; b < C::MBP; b += C::MSTEP) {
                 f32x16 acc[C::NBW];
 #pragma unroll
@@ -923,19 +924,28 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
                     }
                 }
             };
-            // 128 rows: all of the wave's blocks are computed first, then one
-            // barrier, then every result is written.  Their accumulators fit
-            // the registers that the LDS-bound occupancy (two workgroups per
-            // CU) leaves: nh = 128 fwd 392 -> 384 us, nh = 112 507 -> 467 us.
-            // At 96 rows the registers cost a resident workgroup (nh = 80:
-            // 408 -> 551 us), so those keep a barrier per M-block.
+            // With an N split, other waves read this wave's M-blocks too, so a
+            // block's results wait for a barrier.  The wave's M-blocks go in
+            // groups of MG: a group is computed, then one barrier, then its
+            // results are written.  128 rows take all four blocks at once, 96
+            // rows two: their accumulators fit the registers that the
+            // LDS-bound occupancy leaves (two workgroups per CU at 128 rows,
+            // three at 96).  Against a barrier per block: nh = 128 fwd 388 ->
+            // 375 us, nh = 112 507 -> 462 us, nh = 96 391 -> 372 us.  Padded
+            // 96-row tiles measured slower grouped (nh = 80: 401 -> 504 us
+            // with two blocks, 551 us with four) and keep a barrier per block.
             constexpr int NMB = C::MBP / C::MSTEP;
-            f32x16 acc[NMB][C::NBW];
+            constexpr int MG = NS == 4 ? NMB : 2;
+            static_assert(NMB % MG == 0, "M-block groups");
 #pragma unroll
-            for (int i = 0; i < NMB; ++i) mix_block(wave / NS + i * C::MSTEP, acc[i]);
-            __syncthreads();
+            for (int g0 = 0; g0 < NMB; g0 += MG) {
+                f32x16 acc[MG][C::NBW];
 #pragma unroll
-            for (int i = 0; i < NMB; ++i) write_block(wave / NS + i * C::MSTEP, acc[i]);
+                for (int i = 0; i < MG; ++i) mix_block(wave / NS + (g0 + i) * C::MSTEP, acc[i]);
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < MG; ++i) write_block(wave / NS + (g0 + i) * C::MSTEP, acc[i]);
+            }
         }
         __syncthreads();
 
