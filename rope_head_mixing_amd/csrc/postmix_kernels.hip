@@ -759,20 +759,25 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
         const int n = nh * nh;
         const int nvec = ((uintptr_t)W & 15u) == 0 ? n / 8 : 0;
         const int bd = nh * (C::WPITCH + 1);  // one block-diagonal step: nh rows and nh columns
-        for (int q = tid; q < nvec; q += C::NT) {
+        // a work item is one vector of W for one diagonal copy p (tp copies),
+        // then one leftover element for one copy: with few heads the copies,
+        // not the elements, give the threads their work
+        for (int it = tid; it < tp * nvec; it += C::NT) {
+            const int p = it / nvec, q = it - p * nvec;
             const u32x4 x = reinterpret_cast<const u32x4*>(W)[q];
             int row = (8 * q) / nh, col = 8 * q - row * nh;
+            uint16_t* const blk = wl + p * bd;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint16_t w = (uint16_t)(x[e >> 1] >> (16 * (e & 1)));
-                for (int p = 0; p < tp; ++p) wl[p * bd + row * C::WPITCH + col] = w;
+                blk[row * C::WPITCH + col] = (uint16_t)(x[e >> 1] >> (16 * (e & 1)));
                 if (++col == nh) { col = 0; ++row; }
             }
         }
-        for (int idx = 8 * nvec + tid; idx < n; idx += C::NT) {
+        const int rem = n - 8 * nvec;
+        for (int it = tid; it < tp * rem; it += C::NT) {
+            const int p = it / rem, idx = 8 * nvec + (it - p * rem);
             const int row = idx / nh;
-            const uint16_t w = W[idx];
-            for (int p = 0; p < tp; ++p) wl[p * bd + row * C::WPITCH + (idx - row * nh)] = w;
+            wl[p * bd + row * C::WPITCH + (idx - row * nh)] = W[idx];
         }
     }
     __syncthreads();
