@@ -2394,8 +2394,11 @@ int bwd_fused_tokens_per_block(int64_t sq, int nh, int nope, int pe) {
 // bwd_fused_tokens_per_block tokens give is kept unless it leaves the last
 // round of kFusedRound blocks (one workgroup on each of gfx950's 256 CUs)
 // less than three quarters full; then it is rounded to the nearest multiple
-// of kFusedRound and the token groups are spread evenly over the blocks
-// (nh = 96 at 1 GiB: 683 -> 768 blocks, 1000 -> 775 us).  A constant, not
+// of kFusedRound (at most one block per token group) and the groups are
+// spread evenly over the blocks (nh = 96 at 1 GiB: 547 -> 512 blocks, 1000
+// -> 776 us).  Blocks of one group stay one group each: rounding nh = 5 at
+// sq = 8192 down from 683 to 512 blocks of one or two groups measured
+// 43.6 -> 47.5 us.  A constant, not
 // the device's CU count: the partition, and with it the weight gradient's
 // summation order, depends on the shape only.
 static constexpr int64_t kFusedRound = 256;
