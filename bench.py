@@ -40,6 +40,13 @@ KERNELS_NH64 = {
     "bwd_dx": "mix_part_kernel<64, 256, 8, true, 1, false>",
     "bwd_dw": "dw_chunk_kernel<64, 128, false> + dw_reduce_kernel",
 }
+# the same at nh=128, d=512 (head-count sweep workload)
+KERNELS_NH128 = {
+    "fwd": "mix_part_kernel<128, 256, 8, false, 4, false>",
+    "bwd": "bwd_fused_kernel<128, 128, 16, false, true> + dw_reduce_kernel",
+    "bwd_dx": "mix_part_kernel<128, 256, 8, true, 4, false>",
+    "bwd_dw": "dw_chunk_kernel<128, 128, false> + dw_reduce_kernel",
+}
 STEP_OPS = ("fwd", "bwd")          # the timed step
 EXTRA_OPS = ("bwd_dx", "bwd_dw")   # the separate backward entry points, timed after
 # The pages' own figures for this workload (another GPU; context only).
@@ -103,10 +110,13 @@ def cpu_baseline(case, O, W, dY, pos, target_s: float):
     }
 
 
-def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix, timed=20):
+def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix, timed=20,
+                       kernels=None, traffic_file=True):
     """Turn rocprofv3 outputs (kernel-trace --stats, --pmc FETCH_SIZE, --pmc
-    WRITE_SIZE runs of this script) into profiles/<out_prefix>_*.md and the
-    per-launch HBM traffic file read by the benchmark.
+    WRITE_SIZE runs of this script) into profiles/<out_prefix>.md and (for
+    the production workload, traffic_file=True) the per-launch HBM traffic
+    file read by the benchmark.  `kernels` maps each op to its kernels
+    (default: the production shape's).
 
     The counters are calibrated on the plain 1 GiB device copy that the
     benchmark runs (its known traffic: 1 GiB read, 1 GiB written)."""
@@ -147,7 +157,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix
                   (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
                  for r in csv.DictReader(open(one(os.path.join(trace_dir, "**", "*kernel_trace.csv")))))
     names = [x[1] for x in seq]
-    pat = [k.strip() for op in STEP_OPS for k in KERNELS_NH64[op].split("+")]
+    kernels = KERNELS_NH64 if kernels is None else kernels
+    pat = [k.strip() for op in STEP_OPS for k in kernels[op].split("+")]
     occ = [i for i in range(len(seq) - len(pat) + 1) if names[i:i + len(pat)] == pat]
     runs, cur = [], []
     for i in occ:
@@ -177,7 +188,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix
         wb = write.get((name, grid), 0.0)
         traffic[short(name)] = {"fetch_bytes": fb * f_scale, "write_bytes": wb * w_scale,
                                 "hbm_bytes_per_launch": fb * f_scale + wb * w_scale}
-    ops = {op: [k.strip() for k in names.split("+")] for op, names in KERNELS_NH64.items()}
+    ops = {op: [k.strip() for k in names.split("+")] for op, names in kernels.items()}
     doc = {"kernel_source_sha": kernel_source_sha(), "fetch_scale": f_scale, "write_scale": w_scale,
            "kernels": {}}
     for op, names in ops.items():
@@ -187,9 +198,10 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix
                 "kernels": present,
                 "hbm_bytes_per_launch": sum(traffic[n]["hbm_bytes_per_launch"] for n in present)}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
-        json.dump(doc, f, indent=1)
-        f.write("\n")
+    if traffic_file:
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(doc, f, indent=1)
+            f.write("\n")
     lines = [f"# {out_prefix}: rocprofv3 kernel trace and HBM counters", "",
              "Commands (from the repository root on one MI355X):", "", "```", command_note.strip(),
              "```", "", f"Kernel source sha256[:16]: `{doc['kernel_source_sha']}`", "",
@@ -211,14 +223,17 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(path)
-    print(TRAFFIC_FILE)
+    if traffic_file:
+        print(TRAFFIC_FILE)
 
 
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
-        # bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR NAME COMMAND_NOTE_FILE
+        # bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR NAME COMMAND_NOTE_FILE [nh128]
         trace_dir, fetch_dir, write_dir, name, note_file = sys.argv[2:7]
-        summarize_profiles(trace_dir, fetch_dir, write_dir, open(note_file).read(), name)
+        nh128 = len(sys.argv) > 7 and sys.argv[7] == "nh128"
+        summarize_profiles(trace_dir, fetch_dir, write_dir, open(note_file).read(), name,
+                           kernels=KERNELS_NH128 if nh128 else None, traffic_file=not nh128)
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,7 +353,7 @@ def main():
     del dst
 
     dominant = max(STEP_OPS, key=lambda op: per_op_ms[op])
-    kernel_key = KERNELS_NH64[dominant] if case.nh == 64 else dominant
+    kernel_key = {64: KERNELS_NH64, 128: KERNELS_NH128}.get(case.nh, {}).get(dominant, dominant)
     achieved = alg[dominant] / (per_op_ms[dominant] * 1e-3) / 1e9
     roofline = {
         "bound": "hbm",
