@@ -114,8 +114,9 @@ size_t postmix_bwd_dw_workspace_bytes(int64_t sq, int32_t nh, int32_t nope,
  * Backward, weight gradient.  dW[g,h] = sum over tokens s and channels c of
  * dY[s,g,c] * inv_rope(O)[s,h,c] (PR #1772 description part 一: the weight
  * gradient contracts the full channel axis and cannot be split).
- * Deterministic: fixed-size token blocks (a function of the shape only) each
- * produce an fp32 partial; the partials are summed in a fixed pairwise tree.
+ * Deterministic: token blocks of equal size up to one token (a function of
+ * the shape only) each produce an fp32 partial; the partials are summed in a
+ * fixed pairwise tree.
  * No atomics; repeated calls give bitwise-identical dW (the atomic-free
  * principle of PaddleFleet PR #1776, "deterministic TileLang backend for
  * absorbed-MQA sparse backward").  The rotated pe operand is split into a
@@ -143,10 +144,10 @@ int postmix_bwd_dw(const pm_bf16 *dY, const pm_bf16 *O, const float *rope_cos,
  * once and feeds both the head-mix gradient and the weight-gradient partials.  That is one full read of dY
  * fewer than the two separate calls.  Other shapes (or
  * postmix_set_general_kernels(1)) run the two separate computations.
- * dO is bitwise the same as postmix_bwd_dx's; dW is deterministic (fixed
- * token blocks, half the size of postmix_bwd_dw's, and the same fixed-order
- * reduction), but it sums in a different order than postmix_bwd_dw, so the
- * two may differ in the last bits.
+ * dO is bitwise the same as postmix_bwd_dx's; dW is deterministic (token
+ * blocks fixed by the shape, about half the size of postmix_bwd_dw's, and the
+ * same fixed-order reduction), but it sums in a different order than
+ * postmix_bwd_dw, so the two may differ in the last bits.
  *   dY, O [sq, nh, nope+pe] bf16, read;  W [nh, nh] bf16, read
  *   dO    [sq, nh, nope+pe] bf16, written;  dW [nh, nh] fp32, written
  *   workspace as postmix_bwd_dw (postmix_bwd_dw_workspace_bytes bytes).

@@ -342,8 +342,9 @@ int postmix_bwd(const pm_bf16* dY, const pm_bf16* O, const pm_bf16* W, const flo
     a.partials = (float*)workspace;
     a.force_general = mx.force_general;
     hipError_t e;
-    // the fused kernel reads W with 16-byte loads only when nh fills its 64 or
-    // 128 head rows exactly; padded and packed head counts read it element-wise
+    // with nh = 64 or 128 and a W that is not 16-byte aligned, postmix_bwd_dx
+    // runs the general kernel (the tiled one reads W with 16-byte loads), so
+    // the fused pass, whose dO is the tiled kernel's, is not used there
     const bool w_ok = ((uintptr_t)W & 15u) == 0 || (nh != 64 && nh != 128);
     if (!mx.force_general && w_ok && pm::bwd_fused_applies(nh, nope, pe)) {
         e = pm::launch_bwd_fused(mx, a, (hipStream_t)stream);

@@ -200,7 +200,7 @@ def test_tiled_and_general_kernels_agree(sq, nh, nope, pe):
     (13, 64, 480, 32, 7),       # fused path, pe = 32 (one paired pe block)
     (9, 64, 416, 96, 11),       # fused path, pe = 96 (three paired pe blocks)
     (11, 64, 496, 16, 5),       # fused path, pe = 16 (fp32 scratch)
-    (13, 128, 448, 64, 5),      # fused path, nh = 128 (W fragments read from LDS)
+    (13, 128, 448, 64, 5),      # fused path, nh = 128 (waves split by gradient)
     (9, 128, 192, 64, 3),       # fused path, nh = 128, d = 256
     (7, 128, 384, 128, 11),     # fused path, nh = 128, pe = 128
     (5, 128, 432, 80, 2),       # not fused (nh = 128 with pe = 80): separate kernels
