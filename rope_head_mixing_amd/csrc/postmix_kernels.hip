@@ -1540,16 +1540,22 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         // both halves are read and written by the same thread (4 channels,
         // not 8: this phase sets the kernel's register peak)
         if (PS && chunk_pe) {
+            // 128 rows: one token per chunk, so every row takes the chunk's
+            // cos/sin row.  vh (tasks per row) is a power of two (pe = 32 or
+            // 64; checked at launch): a shift and a mask split the task index.
+            // A division there made the compiler keep a 64-bit value across
+            // the chunk loop, spilled, and its reload waited for the chunk
+            // prefetch (nh = 96: 65 us of 760).
+            static_assert(!PS || C::SPLIT, "the pe pass is compiled at 128 rows only");
             const int L0 = nope - c_base;  // local first pe channel (the whole pe range is in this chunk)
             const int vh = h2 >> 2;
-            for (int task = tid; task < NH * vh; task += C::NT) {
-                const int row = task / vh, i = 4 * (task - row * vh);
+            const int lvh = __builtin_ctz((unsigned)vh);
+            for (int task = tid; task < (NH << lvh); task += C::NT) {
+                const int row = task >> lvh, i = 4 * (task & (vh - 1));
                 uint16_t* const o1 = ol + row * C::PITCH + L0 + i;
                 uint16_t* const o2 = o1 + h2;
                 const uint2 a = *reinterpret_cast<const uint2*>(o1), b = *reinterpret_cast<const uint2*>(o2);
-                int p = PAD ? row / nh : 0;
-                p = p < tp ? p : tp - 1;
-                const float* cr = csl + p * pe + i;
+                const float* cr = csl + i;
                 const f32x4 c4 = *reinterpret_cast<const f32x4*>(cr), s4 = *reinterpret_cast<const f32x4*>(cr + h2);
                 float cs[4], sp[4], sm[4];
                 uint32_t aw[2] = {a.x, a.y}, bw[2] = {b.x, b.y}, h1[2], l1[2], hh2[2], ll2[2];
@@ -2509,7 +2515,8 @@ static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int64_t
     // backward from 732 to 712 us.  At NH = 64 its registers pushed spill
     // reloads into the chunk loop (535 -> 730 us), so it is not compiled there.
     constexpr bool PS_OK = NH == 128;
-    const bool ps = PS_OK && C::lds_bytes(a.nope, a.pe, rgt, true) <= kMaxLds;
+    const int vh = a.pe / 8;  // its tasks per row: a power of two
+    const bool ps = PS_OK && a.pe > 0 && (vh & (vh - 1)) == 0 && C::lds_bytes(a.nope, a.pe, rgt, true) <= kMaxLds;
     auto kern = pad ? (ps ? bwd_fused_kernel<NH, CH, WAVES, true, PS_OK> : bwd_fused_kernel<NH, CH, WAVES, true, false>)
                     : (ps ? bwd_fused_kernel<NH, CH, WAVES, false, PS_OK> : bwd_fused_kernel<NH, CH, WAVES, false, false>);
     static AttrPerDevice attr[2][2];
