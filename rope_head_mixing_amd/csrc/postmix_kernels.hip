@@ -816,7 +816,10 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
         const bool paired = tile_pe && pe_pairs_in_blocks(nope, pe);
         const int L = nope - c_base;  // local index of the first pe channel (tiles with pe)
 
-        // Padded 96-row tiles keep a barrier per M-block (see below).
+        // One M-block at a time (64 rows; padded 96-row tiles, with a barrier
+        // per block, see below).  This loop is kept as written rather than
+        // through mix_block/write_block of the grouped path: routed through
+        // them, the 64-row dx measured 2% slower (351 -> 358 us).
         if constexpr (NS == 1 || (NS == 3 && PAD)) {
             for (int b = wave / NS; b < C::MBP; b += C::MSTEP) {
                 f32x16 acc[C::NBW];
