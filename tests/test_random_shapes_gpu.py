@@ -4,7 +4,9 @@ fp64 oracle.
 The hand-picked cases of test_parity_gpu.py aim at one route each; this sweep
 draws head counts from 2 to 128 (padded rows, several tokens per tile, 96- and
 128-row tiles), channel splits with and without d a multiple of 128 (tiled and
-general kernels), pe from 0 to 256 and short ragged token counts.  Each shape
+general kernels), pe from 0 to 256 and short ragged token counts, and eight
+more with 1100 to 4000 tokens, where the token blocks are rounded to whole
+rounds and spread evenly.  Each shape
 runs the forward, dx, dW and the single-call backward, each checked against
 the oracle, and the single-call dO must equal postmix_bwd_dx's bit for bit.
 
@@ -60,3 +62,24 @@ def test_random_shape(sq, nh, nope, pe, off):
     dO, dW = dv.bwd()
     np.testing.assert_array_equal(gu.host_bits(dO), dO_dx)
     gu.check_dw(dW.cpu().numpy(), ref_dW, f"{c.name} bwd dW")
+
+
+def _large_shapes(n: int, seed: int = 20261203):
+    """Token counts large enough that the token blocks are rounded to whole
+    rounds and spread evenly (more than 256 blocks of the fused backward, and
+    of the weight gradient above 64 heads); d = 128 or 256 keeps the oracle
+    at seconds."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        nh = int(rng.integers(2, 129))
+        d = int(rng.choice([128, 256]))
+        pe = int(rng.choice([0, 32, 64]))
+        sq = int(rng.integers(1100, 1700)) if nh > 32 else int(rng.integers(2100, 4000))
+        out.append((sq, nh, d - pe, pe, int(rng.integers(0, 30000))))
+    return out
+
+
+@pytest.mark.parametrize("sq,nh,nope,pe,off", _large_shapes(8))
+def test_random_shape_many_blocks(sq, nh, nope, pe, off):
+    test_random_shape(sq, nh, nope, pe, off)
