@@ -40,6 +40,13 @@ KERNELS_NH64 = {
     "bwd_dx": "mix_part_kernel<64, 256, 8, true, 1, false>",
     "bwd_dw": "dw_chunk_kernel<64, 128, false> + dw_reduce_kernel",
 }
+# the same at nh=3, d=512 (head-count sweep workload: 21 tokens per 64-row tile)
+KERNELS_NH3 = {
+    "fwd": "mix_part_kernel<64, 256, 8, false, 1, true>",
+    "bwd": "bwd_fused_kernel<64, 256, 16, true, false> + dw_reduce_kernel",
+    "bwd_dx": "mix_part_kernel<64, 256, 8, true, 1, true>",
+    "bwd_dw": "dw_chunk_kernel<64, 128, true> + dw_reduce_kernel",
+}
 # the same at nh=128, d=512 (head-count sweep workload)
 KERNELS_NH128 = {
     "fwd": "mix_part_kernel<128, 256, 8, false, 4, false>",
@@ -47,6 +54,8 @@ KERNELS_NH128 = {
     "bwd_dx": "mix_part_kernel<128, 256, 8, true, 4, false>",
     "bwd_dw": "dw_chunk_kernel<128, 128, false> + dw_reduce_kernel",
 }
+KERNELS_BY_WORKLOAD = {"prod": KERNELS_NH64, "fwd_1k": KERNELS_NH64, "sweep_nh3": KERNELS_NH3,
+                       "sweep_nh128": KERNELS_NH128}
 STEP_OPS = ("fwd", "bwd")          # the timed step
 EXTRA_OPS = ("bwd_dx", "bwd_dw")   # the separate backward entry points, timed after
 # The pages' own figures for this workload (another GPU; context only).
@@ -229,11 +238,11 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix
 
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
-        # bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR NAME COMMAND_NOTE_FILE [nh128]
+        # bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR NAME COMMAND_NOTE_FILE [WORKLOAD]
         trace_dir, fetch_dir, write_dir, name, note_file = sys.argv[2:7]
-        nh128 = len(sys.argv) > 7 and sys.argv[7] == "nh128"
+        workload = sys.argv[7] if len(sys.argv) > 7 else "prod"
         summarize_profiles(trace_dir, fetch_dir, write_dir, open(note_file).read(), name,
-                           kernels=KERNELS_NH128 if nh128 else None, traffic_file=not nh128)
+                           kernels=KERNELS_BY_WORKLOAD[workload], traffic_file=workload == "prod")
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,7 +362,7 @@ def main():
     del dst
 
     dominant = max(STEP_OPS, key=lambda op: per_op_ms[op])
-    kernel_key = {64: KERNELS_NH64, 128: KERNELS_NH128}.get(case.nh, {}).get(dominant, dominant)
+    kernel_key = KERNELS_BY_WORKLOAD.get(args.workload, {}).get(dominant, dominant)
     achieved = alg[dominant] / (per_op_ms[dominant] * 1e-3) / 1e9
     roofline = {
         "bound": "hbm",

@@ -327,7 +327,7 @@ def test_benchmark_kernel_names_exist_in_the_library():
     if shutil.which("nm") is None:
         pytest.skip("nm not available")
     out = subprocess.run(["nm", "-C", pm.LIB_PATH], capture_output=True, text=True, check=True).stdout
-    for table in (bench.KERNELS_NH64, bench.KERNELS_NH128):
+    for table in (bench.KERNELS_NH64, bench.KERNELS_NH3, bench.KERNELS_NH128):
         for op, names in table.items():
             for name in (n.strip() for n in names.split("+")):
                 assert f"pm::{name}(" in out, f"{op}: kernel {name!r} not in {pm.LIB_PATH}"
