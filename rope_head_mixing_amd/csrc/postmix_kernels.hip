@@ -2403,11 +2403,12 @@ int bwd_fused_tokens_per_block(int64_t sq, int nh, int nope, int pe) {
 // bwd_fused_tokens_per_block tokens give is kept unless it leaves the last
 // round of kFusedRound blocks (one workgroup on each of gfx950's 256 CUs)
 // less than three quarters full; then it is rounded to the nearest multiple
-// of kFusedRound (at most one block per token group) and the groups are
-// spread evenly over the blocks (nh = 96 at 1 GiB: 547 -> 512 blocks, 1000
-// -> 776 us).  Blocks of one group stay one group each: rounding nh = 5 at
-// sq = 8192 down from 683 to 512 blocks of one or two groups measured
-// 43.6 -> 47.5 us.  A constant, not
+// of kFusedRound and the token groups are spread evenly over the blocks
+// (nh = 96 at 1 GiB: 547 -> 512 blocks, 1000 -> 776 us).  With blocks of one
+// group the nearest multiple can exceed the groups: below two rounds the
+// count is then one round (nh = 3 at sq = 8192: 391 -> 256 blocks of one or
+// two groups, 30.6 -> 27.6 us), else one block per group (nh = 5: 683 ->
+// 512 blocks measured 43.6 -> 47.5 us).  A constant, not
 // the device's CU count: the partition, and with it the weight gradient's
 // summation order, depends on the shape only.
 static constexpr int64_t kFusedRound = 256;
@@ -2418,7 +2419,10 @@ int64_t bwd_fused_num_blocks(int64_t sq, int nh, int nope, int pe) {
     int64_t b = (groups + per_block - 1) / per_block;
     if (b > kFusedRound && b % kFusedRound < kFusedRound * 3 / 4) {
         b = (b + kFusedRound / 2) / kFusedRound * kFusedRound;
-        if (b > groups) b = groups;
+        // more blocks than token groups: with fewer than two rounds of
+        // groups, one round of blocks of one or two groups; otherwise one
+        // group per block
+        if (b > groups) b = groups < 2 * kFusedRound ? kFusedRound : groups;
     }
     return b;
 }
