@@ -120,15 +120,16 @@ def cpu_baseline(case, O, W, dY, pos, target_s: float):
 
 
 def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix, timed=20,
-                       kernels=None, traffic_file=True):
+                       kernels=None, traffic_file=True, copy_bytes=1 << 30):
     """Turn rocprofv3 outputs (kernel-trace --stats, --pmc FETCH_SIZE, --pmc
     WRITE_SIZE runs of this script) into profiles/<out_prefix>.md and (for
     the production workload, traffic_file=True) the per-launch HBM traffic
     file read by the benchmark.  `kernels` maps each op to its kernels
-    (default: the production shape's).
+    (default: the production shape's); `copy_bytes` is the size of the
+    benchmark's plain device copy of O for the workload (1 GiB in production).
 
-    The counters are calibrated on the plain 1 GiB device copy that the
-    benchmark runs (its known traffic: 1 GiB read, 1 GiB written)."""
+    The counters are calibrated on the plain device copy of O that the
+    benchmark runs (its known traffic: copy_bytes read, copy_bytes written)."""
     import collections
     import csv
     import glob
@@ -150,9 +151,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix
 
     fetch, write = counters(fetch_dir, "FETCH_SIZE"), counters(write_dir, "WRITE_SIZE")
     gib = float(1 << 30)
-    # the 1 GiB copy: the copy kernel launch whose written bytes are largest
+    # the copy of O: the copy kernel launch whose written bytes are largest
     copy_key = max((k for k in write if "copy" in k[0].lower()), key=lambda k: write[k])
-    f_scale, w_scale = gib / fetch[copy_key], gib / write[copy_key]
+    f_scale, w_scale = copy_bytes / fetch[copy_key], copy_bytes / write[copy_key]
 
     def short(name):
         return name.split("(")[0].replace("void ", "").replace("pm::", "")
@@ -222,8 +223,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix
              "| kernel | calls | avg us | timed avg us | min us | max us |", "|---|---|---|---|---|---|"]
     lines += [f"| `{n}` | {c} | {a:.1f} | {ta:.1f} | {mn:.1f} | {mx:.1f} |" for n, c, a, ta, mn, mx in rows]
     lines += ["", "## HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)", "",
-              f"Calibration on the benchmark's plain 1 GiB device copy (`{short(copy_key[0])}`): "
-              f"FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f} gives 1 GiB each.", "",
+              f"Calibration on the benchmark's plain device copy of O, {copy_bytes / gib:.4f} GiB "
+              f"(`{short(copy_key[0])}`): FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f} "
+              f"gives that read and written.", "",
               "| kernel | fetched GiB | written GiB | total GiB |", "|---|---|---|---|"]
     for n, t in sorted(traffic.items()):
         lines.append(f"| `{n}` | {t['fetch_bytes'] / gib:.4f} | {t['write_bytes'] / gib:.4f} | "
@@ -241,8 +243,11 @@ def main():
         # bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR NAME COMMAND_NOTE_FILE [WORKLOAD]
         trace_dir, fetch_dir, write_dir, name, note_file = sys.argv[2:7]
         workload = sys.argv[7] if len(sys.argv) > 7 else "prod"
+        from rope_head_mixing_amd import synthetic
+        c = synthetic.CASES[workload]
         summarize_profiles(trace_dir, fetch_dir, write_dir, open(note_file).read(), name,
-                           kernels=KERNELS_BY_WORKLOAD[workload], traffic_file=workload == "prod")
+                           kernels=KERNELS_BY_WORKLOAD[workload], traffic_file=workload == "prod",
+                           copy_bytes=c.sq * c.nh * c.d * 2)
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
