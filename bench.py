@@ -238,7 +238,70 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, command_note, out_prefix
         print(TRAFFIC_FILE)
 
 
+SQ_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+               "SQ_INSTS_LDS", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE")
+
+
+def summarize_counters(pmc_dir, command_note, out_prefix, kernels=None, n_cu=256, n_simd=4, n_xcd=8):
+    """Per-launch averages of the SQ_COUNTERS (one rocprofv3 --pmc run of this
+    script) for the workload's kernels, with the rates derived from them, into
+    profiles/<out_prefix>.md.  rocprofv3 sums each counter over its hardware
+    instances, so the kernel's active cycles are GRBM_GUI_ACTIVE / XCDs; then
+    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles * CUs * SIMDs), and LDS
+    active and LDS bank-conflict cycles are per CU cycle."""
+    import collections
+    import csv
+    import glob
+    kernels = KERNELS_NH64 if kernels is None else kernels
+    names = {k.strip() for v in kernels.values() for k in v.split("+")}
+    hits = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not hits:
+        raise SystemExit(f"no counter file under {pmc_dir}")
+    # per dispatch: counter -> value (summed over the instances rocprofv3 reports)
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    kname = {}
+    for r in csv.DictReader(open(hits[0])):
+        short = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("pm::", "")
+        if short not in names:
+            continue
+        per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+        kname[r["Dispatch_Id"]] = short
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for did, cv in per.items():
+        for c, v in cv.items():
+            agg[kname[did]][c].append(v)
+    lines = [f"# {out_prefix}: rocprofv3 SQ counters", "", "Command (from the repository root on one MI355X):",
+             "", "```", command_note.strip(), "```", "",
+             f"Kernel source sha256[:16]: `{kernel_source_sha()}`", "",
+             "Per-launch averages over the run's launches of each kernel (counters summed over their "
+             "hardware instances).  Kernel cycles = GRBM_GUI_ACTIVE / 8 XCDs.  MFMA busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 256 CUs x 4 SIMDs); LDS active and LDS bank "
+             "conflict = SQ_LDS_IDX_ACTIVE and SQ_LDS_BANK_CONFLICT / (cycles x 256 CUs); "
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16 counts units of 512 FLOPs.  Short kernels (the reduce) "
+             "include the profiler's per-dispatch overhead in their cycles.",
+             "", "| kernel | launches | " + " | ".join(SQ_COUNTERS) + " | MFMA busy | LDS active | LDS bank conflict |",
+             "|---" * (len(SQ_COUNTERS) + 5) + "|"]
+    for n in sorted(agg):
+        a = {c: sum(v) / len(v) for c, v in agg[n].items()}
+        gui = (a.get("GRBM_GUI_ACTIVE", 0.0) / n_xcd) or float("nan")
+        mfma = a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * n_cu * n_simd)
+        lds = a.get("SQ_LDS_IDX_ACTIVE", 0.0) / (gui * n_cu)
+        conf = a.get("SQ_LDS_BANK_CONFLICT", 0.0) / (gui * n_cu)
+        cells = " | ".join(f"{a.get(c, float('nan')):.4g}" for c in SQ_COUNTERS)
+        lines.append(f"| `{n}` | {len(next(iter(agg[n].values())))} | {cells} | {100 * mfma:.1f}% | "
+                     f"{100 * lds:.1f}% | {100 * conf:.1f}% |")
+    path = os.path.join(ROOT, "profiles", f"{out_prefix}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
+        # bench.py --summarize-counters PMC_DIR NAME COMMAND_NOTE_FILE
+        pmc_dir, name, note_file = sys.argv[2:5]
+        summarize_counters(pmc_dir, open(note_file).read(), name)
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
         # bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR NAME COMMAND_NOTE_FILE [WORKLOAD]
         trace_dir, fetch_dir, write_dir, name, note_file = sys.argv[2:7]
