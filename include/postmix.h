@@ -36,7 +36,7 @@
  *    (a hipStream_t; NULL = the null stream) and the call returns at once.
  *  - Outputs are overwritten, never accumulated.  Inputs are not modified.
  *    In-place operation is not supported: an output range that overlaps an
- *    input range is rejected.
+ *    input range is rejected (postmix_kv_index_remap alone allows out == idx).
  *  - Limits: 1 <= nh <= 128; nope >= 0 with nope % 8 == 0; pe >= 0 with
  *    pe % 16 == 0; nope + pe > 0; sq >= 0.  sq == 0 is a successful no-op.
  *  - Activation, table and workspace pointers must be 16-byte aligned; W must
@@ -46,7 +46,8 @@
  *  - Return 0 on success, else a negative PM_ERR_* code; a thread-local
  *    message naming the offending argument is available from
  *    postmix_last_error().  Arguments are validated before any HIP call.
- *  - Calls are reentrant.  Concurrent bwd_dw calls need distinct workspaces.
+ *  - Calls are reentrant.  Concurrent postmix_bwd_dw / postmix_bwd calls need
+ *    distinct workspaces.
  */
 #ifndef POSTMIX_H
 #define POSTMIX_H
