@@ -266,6 +266,22 @@ def test_identity_mix_keeps_nope_columns_bitwise():
     gu.check_bf16(Y, ref, "W=I Y")
 
 
+@pytest.mark.parametrize("nh", [20, 64, 128])
+def test_channel_axis_splits_bitwise(nh):
+    """The channel axis is a pure N dimension (PR #1772 body item 1; the pages
+    test their split-N GEMM for bitwise equality): the first 256 (nope)
+    channels of Y and of dO computed over the full width, 448 + 64, equal bit
+    for bit the same channels computed on their own, 256 + 0."""
+    c = synthetic.case(19, nh, 448, 64, seed=880 + nh, pos_offset=321)
+    dv = Dev(c)
+    Y, dO = gu.host_bits(dv.fwd()), gu.host_bits(dv.dx())
+    s = synthetic.case(19, nh, 256, 0, seed=880 + nh, pos_offset=321)
+    ds = Dev(s, O=np.ascontiguousarray(dv.O[..., :256]), W=dv.W,
+             dY=np.ascontiguousarray(dv.dY[..., :256]), positions=dv.pos)
+    np.testing.assert_array_equal(gu.host_bits(ds.fwd()), Y[..., :256])
+    np.testing.assert_array_equal(gu.host_bits(ds.dx()), dO[..., :256])
+
+
 def test_zero_positions_equal_the_unrotated_mix_bitwise():
     c = synthetic.case(23, 64, 448, 64, seed=333)
     dv = Dev(c, positions=np.zeros(23, np.int32))
