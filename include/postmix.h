@@ -38,7 +38,9 @@
  *    In-place operation is not supported: an output range that overlaps an
  *    input range is rejected (postmix_kv_index_remap alone allows out == idx).
  *  - Limits: 1 <= nh <= 128; nope >= 0 with nope % 8 == 0; pe >= 0 with
- *    pe % 16 == 0; nope + pe > 0; sq >= 0.  sq == 0 is a successful no-op.
+ *    pe % 16 == 0; nope + pe > 0; sq >= 0; sq * nh * (nope + pe) <= 2^40
+ *    elements, so any tensor that fits in device memory.  sq == 0 is a
+ *    successful no-op.
  *  - Activation, table and workspace pointers must be 16-byte aligned; W must
  *    be 2-byte aligned (for nh of 32, 64 or 128 the tiled kernels read W in
  *    16-byte vectors and are used only when W is 16-byte aligned; other head

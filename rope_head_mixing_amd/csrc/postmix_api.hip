@@ -71,7 +71,7 @@ int check_shape(int64_t sq, int32_t nh, int32_t nope, int32_t pe) {
     if (pe < 0 || pe % 16 != 0)
         return fail(PM_ERR_SHAPE, "pe must be >= 0 and a multiple of 16 (got %d)", pe);
     if (nope + pe <= 0) return fail(PM_ERR_SHAPE, "nope + pe must be > 0");
-    // element offsets stay well inside int64 and the grid inside 2^31 items
+    // element offsets stay well inside int64 (data-sized grids are split over x and y)
     if (sq > ((int64_t)1 << 40) / ((int64_t)nh * (nope + pe)))
         return fail(PM_ERR_SHAPE, "sq=%lld too large for nh=%d, d=%d", (long long)sq, nh, nope + pe);
     return PM_OK;

@@ -93,6 +93,33 @@ __device__ __forceinline__ int64_t table_row(const int32_t* positions, int64_t s
     return p >= table_rows ? table_rows - 1 : p;
 }
 
+// Data-sized launches.  One dimension of a dispatch holds fewer than 2^32
+// work-items, so a grid of more than 2^21 workgroups (2^31 work-items at 1024
+// threads) takes rows of 2^21 in x and the rows in y: workgroup
+// b = y * 2^21 + x.  The fixed row width keeps gridDim out of the index (on
+// gfx950 reading it costs a dispatch-packet load and a division).  The last
+// row can run past n: each such kernel checks its index.
+constexpr int kGridXLog2 = 21;
+constexpr int64_t kMaxGridY = 65535;
+static bool data_grid(int64_t n_blocks, dim3* g) {
+    const int64_t gx = (int64_t)1 << kGridXLog2;
+    if (n_blocks <= gx) {
+        *g = dim3((unsigned)n_blocks);
+        return true;
+    }
+    const int64_t gy = (n_blocks + gx - 1) / gx;
+    if (gy > kMaxGridY) return false;
+    *g = dim3((unsigned)gx, (unsigned)gy);
+    return true;
+}
+
+// workgroup index; ROWS = false for a grid of one row, where it is blockIdx.x
+template <bool ROWS = true>
+__device__ __forceinline__ int64_t linear_block() {
+    if constexpr (ROWS) return ((int64_t)blockIdx.y << kGridXLog2) + blockIdx.x;
+    return blockIdx.x;
+}
+
 // ---------------------------------------------------------------------------
 // channel groups
 //
@@ -711,7 +738,7 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
 
-    int64_t t = blockIdx.x;
+    int64_t t = linear_block();
     u32x4 v[C::VPT];
     // thread tid < tp*pe/4 carries quad tid%(pe/4) of token tid/(pe/4)'s cos
     // (first pe/8 quads) or sin row
@@ -1864,8 +1891,9 @@ __device__ __forceinline__ int32_t remap_one(int32_t v, uint32_t off, int32_t pa
 // batch of element (or vector) i, with `per_batch` elements per batch: one
 // scalar division per workgroup when a batch spans at least a workgroup
 // (then a workgroup holds at most one batch boundary), else per element
+template <bool ROWS>
 __device__ __forceinline__ int64_t batch_of(int64_t i, int64_t per_batch) {
-    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x;
+    const int64_t i0 = linear_block<ROWS>() * blockDim.x;
     if (per_batch >= (int64_t)blockDim.x) {
         const int64_t b0 = i0 / per_batch;
         return b0 + (i >= (b0 + 1) * per_batch ? 1 : 0);
@@ -1873,13 +1901,14 @@ __device__ __forceinline__ int64_t batch_of(int64_t i, int64_t per_batch) {
     return i / per_batch;
 }
 
+template <bool ROWS>
 __global__ __launch_bounds__(256) void kv_remap_vec_kernel(const int32_t* __restrict__ idx,
                                                            int64_t n_vec, int64_t vec_per_batch,
                                                            int64_t seqlen_kv, int32_t pad,
                                                            int32_t* __restrict__ out) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t i = linear_block<ROWS>() * 256 + threadIdx.x;
     if (i >= n_vec) return;
-    const uint32_t off = (uint32_t)(batch_of(i, vec_per_batch) * seqlen_kv);
+    const uint32_t off = (uint32_t)(batch_of<ROWS>(i, vec_per_batch) * seqlen_kv);
     const i32x4 v = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(idx) + i);
     i32x4 o;
 #pragma unroll
@@ -1887,13 +1916,14 @@ __global__ __launch_bounds__(256) void kv_remap_vec_kernel(const int32_t* __rest
     __builtin_nontemporal_store(o, reinterpret_cast<i32x4*>(out) + i);
 }
 
+template <bool ROWS>
 __global__ __launch_bounds__(256) void kv_remap_scalar_kernel(const int32_t* __restrict__ idx,
                                                               int64_t n, int64_t per_batch,
                                                               int64_t seqlen_kv, int32_t pad,
                                                               int32_t* __restrict__ out) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t i = linear_block<ROWS>() * 256 + threadIdx.x;
     if (i >= n) return;
-    out[i] = remap_one(idx[i], (uint32_t)(batch_of(i, per_batch) * seqlen_kv), pad);
+    out[i] = remap_one(idx[i], (uint32_t)(batch_of<ROWS>(i, per_batch) * seqlen_kv), pad);
 }
 
 hipError_t launch_kv_remap(const int32_t* idx, int64_t rows, int64_t sq, int64_t topk,
@@ -1901,13 +1931,16 @@ hipError_t launch_kv_remap(const int32_t* idx, int64_t rows, int64_t sq, int64_t
     const int64_t n = rows * topk;
     if (n == 0) return hipSuccess;
     const bool vec = topk % 4 == 0 && ((uintptr_t)idx & 15u) == 0 && ((uintptr_t)out & 15u) == 0;
+    dim3 grid;
     if (vec) {
         const int64_t n_vec = n / 4;
-        hipLaunchKernelGGL(kv_remap_vec_kernel, dim3((unsigned)((n_vec + 255) / 256)), dim3(256), 0, stream,
-                           idx, n_vec, (topk / 4) * sq, seqlen_kv, pad, out);
+        if (!data_grid((n_vec + 255) / 256, &grid)) return hipErrorInvalidConfiguration;
+        auto kern = grid.y > 1 ? kv_remap_vec_kernel<true> : kv_remap_vec_kernel<false>;
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, idx, n_vec, (topk / 4) * sq, seqlen_kv, pad, out);
     } else {
-        hipLaunchKernelGGL(kv_remap_scalar_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                           idx, n, topk * sq, seqlen_kv, pad, out);
+        if (!data_grid((n + 255) / 256, &grid)) return hipErrorInvalidConfiguration;
+        auto kern = grid.y > 1 ? kv_remap_scalar_kernel<true> : kv_remap_scalar_kernel<false>;
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, idx, n, topk * sq, seqlen_kv, pad, out);
     }
     return hipGetLastError();
 }
@@ -1928,13 +1961,23 @@ hipError_t launch_kv_remap(const int32_t* idx, int64_t rows, int64_t sq, int64_t
 // non-temporal loads and stores.
 // ---------------------------------------------------------------------------
 
+template <bool ROWS>
 __global__ __launch_bounds__(512) void rope_apply_kernel(
     const uint16_t* __restrict__ X, const float* __restrict__ rcos, const float* __restrict__ rsin,
-    int64_t table_rows, const int32_t* __restrict__ positions, int nh, int nope, int pe, int rows_per_wg,
-    int groups_per_token, int direction, uint16_t* __restrict__ Out) {
+    int64_t table_rows, const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe,
+    int rows_per_wg, int groups_per_token, int direction, uint16_t* __restrict__ Out) {
     const int d = nope + pe, h2 = pe >> 1, nv = nope >> 3, pv = pe >> 3;
-    const int64_t s = blockIdx.x / (unsigned)groups_per_token;      // token
-    const int h0 = (int)(blockIdx.x - s * groups_per_token) * rows_per_wg;
+    int64_t s;  // token
+    int h0;     // first head row
+    if (!ROWS || blockIdx.y == 0) {  // 32-bit division in the first row
+        s = blockIdx.x / (unsigned)groups_per_token;
+        h0 = (int)(blockIdx.x - s * groups_per_token) * rows_per_wg;
+    } else {
+        const int64_t b = linear_block();
+        s = b / groups_per_token;
+        if (s >= sq) return;
+        h0 = (int)(b - s * groups_per_token) * rows_per_wg;
+    }
     const int n_copy = rows_per_wg * nv, n_all = rows_per_wg * (nv + pv);
     const float sg = (float)direction;  // +1: turn by +phi, -1: by -phi
     for (int t = threadIdx.x; t < n_all; t += blockDim.x) {
@@ -1986,12 +2029,13 @@ hipError_t launch_rope_apply(const uint16_t* X, const float* rcos, const float* 
     int rows_per_wg = vpr >= 512 ? 1 : 512 / vpr;
     if (rows_per_wg > nh) rows_per_wg = nh;
     const int groups = (nh + rows_per_wg - 1) / rows_per_wg;
-    const int64_t grid = sq * groups;
-    if (grid > 0xffffffffll) return hipErrorInvalidValue;
     int threads = (rows_per_wg * vpr + 63) / 64 * 64;
     if (threads > 512) threads = 512;
-    hipLaunchKernelGGL(rope_apply_kernel, dim3((unsigned)grid), dim3(threads), 0, stream, X, rcos, rsin,
-                       table_rows, positions, nh, nope, pe, rows_per_wg, groups, direction, Out);
+    dim3 grid;
+    if (!data_grid(sq * groups, &grid)) return hipErrorInvalidConfiguration;
+    auto kern = grid.y > 1 ? rope_apply_kernel<true> : rope_apply_kernel<false>;
+    hipLaunchKernelGGL(kern, grid, dim3(threads), 0, stream, X, rcos, rsin,
+                       table_rows, positions, sq, nh, nope, pe, rows_per_wg, groups, direction, Out);
     return hipGetLastError();
 }
 
@@ -2027,7 +2071,7 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4& v, float* f) {
     }
 }
 
-template <bool DX>
+template <bool DX, bool ROWS>
 __global__ __launch_bounds__(512) void small_mix_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
@@ -2040,7 +2084,7 @@ __global__ __launch_bounds__(512) void small_mix_kernel(
 #pragma unroll
         for (int i = 0; i < SMALL_NH; ++i)
             m[o][i] = (o < nh && i < nh) ? bf16_to_f32(DX ? W[i * nh + o] : W[o * nh + i]) : 0.0f;
-    const int64_t s0 = (int64_t)blockIdx.x * tokens_per_wg;
+    const int64_t s0 = linear_block<ROWS>() * tokens_per_wg;
     const int n_copy = tokens_per_wg * nv, n_all = tokens_per_wg * (nv + pv);
     for (int t = threadIdx.x; t < n_all; t += blockDim.x) {
         const bool is_pe = t >= n_copy;
@@ -2262,7 +2306,9 @@ static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
         return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
     });
     if (ae != hipSuccess) return ae;
-    hipLaunchKernelGGL(kern, dim3((unsigned)n_tiles), dim3(64 * WAVES), lds, stream, a.X, a.W, a.rcos,
+    dim3 grid;
+    if (!data_grid(n_tiles, &grid)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), lds, stream, a.X, a.W, a.rcos,
                        a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, cpt, tp, n_tiles, a.Out);
     return hipGetLastError();
 }
@@ -2325,10 +2371,12 @@ static hipError_t launch_mix_dx(const MixArgs& a, hipStream_t stream) {
     if (!a.force_general && a.nh <= SMALL_NH) {
         const int vpr = (a.nope + a.pe) / 8;
         const int tok = vpr >= 512 ? 1 : 512 / vpr;
-        const int64_t grid = (a.sq + tok - 1) / tok;
         int threads = (tok * vpr + 63) / 64 * 64;
         if (threads > 512) threads = 512;
-        hipLaunchKernelGGL(small_mix_kernel<DX>, dim3((unsigned)grid), dim3(threads), 0, stream, a.X, a.W,
+        dim3 grid;
+        if (!data_grid((a.sq + tok - 1) / tok, &grid)) return hipErrorInvalidConfiguration;
+        auto kern = grid.y > 1 ? small_mix_kernel<DX, true> : small_mix_kernel<DX, false>;
+        hipLaunchKernelGGL(kern, grid, dim3(threads), 0, stream, a.X, a.W,
                            a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, tok, a.Out);
         return hipGetLastError();
     }
