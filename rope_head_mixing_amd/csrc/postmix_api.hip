@@ -70,9 +70,13 @@ int check_shape(int64_t sq, int32_t nh, int32_t nope, int32_t pe) {
         return fail(PM_ERR_SHAPE, "nope must be >= 0 and a multiple of 8 (got %d)", nope);
     if (pe < 0 || pe % 16 != 0)
         return fail(PM_ERR_SHAPE, "pe must be >= 0 and a multiple of 16 (got %d)", pe);
-    if (nope + pe <= 0) return fail(PM_ERR_SHAPE, "nope + pe must be > 0");
+    const int64_t d = (int64_t)nope + pe;
+    if (d <= 0) return fail(PM_ERR_SHAPE, "nope + pe must be > 0");
+    // offsets within a token (head * d + channel, head < 128) fit 31 bits
+    if (d > ((int64_t)1 << 24))
+        return fail(PM_ERR_SHAPE, "nope + pe must be at most 2^24 (got %lld)", (long long)d);
     // element offsets stay well inside int64 (data-sized grids are split over x and y)
-    if (sq > ((int64_t)1 << 40) / ((int64_t)nh * (nope + pe)))
+    if (sq > ((int64_t)1 << 40) / ((int64_t)nh * d))
         return fail(PM_ERR_SHAPE, "sq=%lld too large for nh=%d, d=%d", (long long)sq, nh, nope + pe);
     return PM_OK;
 }

@@ -101,6 +101,8 @@ def dw(**kw):
     (dict(pe=8), pm.PM_ERR_SHAPE, "pe"),
     (dict(pe=-16), pm.PM_ERR_SHAPE, "pe"),
     (dict(nope=0, pe=0), pm.PM_ERR_SHAPE, "nope + pe"),
+    (dict(nope=(1 << 24) - 48, pe=64), pm.PM_ERR_SHAPE, "2^24"),
+    (dict(nope=2 ** 31 - 8, pe=16), pm.PM_ERR_SHAPE, "2^24"),  # int32 sum would wrap
     (dict(sq=-1), pm.PM_ERR_SHAPE, "sq"),
     (dict(rows=0), pm.PM_ERR_SHAPE, "table_rows"),
     (dict(W=0), pm.PM_ERR_NULL, "W"),
@@ -138,6 +140,13 @@ def test_pe_zero_does_not_need_tables():
     """With pe == 0 the tables may be NULL; the call gets past validation
     (then fails at the device check on a host without a gfx950)."""
     rc, msg = fwd(pe=0, nope=512, cos=0, sin=0, pos=0, rows=0)
+    assert rc not in (pm.PM_ERR_NULL, pm.PM_ERR_SHAPE, pm.PM_ERR_ALIGN, pm.PM_ERR_OVERLAP), msg
+
+
+def test_widest_rows_pass_the_shape_check():
+    """nope + pe = 2^24 is the widest accepted row (then the call fails at
+    the device check on a host without a gfx950)."""
+    rc, msg = fwd(sq=1, nh=1, nope=(1 << 24) - 64, pe=64)
     assert rc not in (pm.PM_ERR_NULL, pm.PM_ERR_SHAPE, pm.PM_ERR_ALIGN, pm.PM_ERR_OVERLAP), msg
 
 
