@@ -6,6 +6,8 @@ cases are small shapes that reach a second row on their routes:
 
 - the forward head mix in the token-part kernel at nh = 32, 64 + 64 channels
   (one tile per token): 2^21 + 4099 tokens, 17 GB per tensor;
+- the small-head mix (nh <= 4, d not a multiple of 128) at one head of 16 pe
+  channels, 256 tokens per workgroup: 2^29 + 5000 tokens, 17 GB;
 - the full-width rotation (the unfused route's materialised inv_rope,
   PaddleFleet PR #1772, PR body item 1) at one head of 16 pe channels, where a
   workgroup covers one token;
@@ -65,6 +67,38 @@ def test_forward_mix_over_two_grid_rows():
     gu.check_bf16(gu.host_bits(_sub(Y, picks)), ref, "Y at sampled tokens")
 
     for lo, hi in [(0, 4096), (ROW - 2048, ROW + 2048), (sq - 4200, sq)]:
+        part = pm.postmix_fwd(O[lo:hi].contiguous(), W, cos, sin, pos[lo:hi].contiguous(), nope, pe)
+        np.testing.assert_array_equal(gu.host_bits(part), gu.host_bits(Y[lo:hi].contiguous()),
+                                      err_msg=f"tokens [{lo}, {hi})")
+
+
+def test_small_head_mix_over_two_grid_rows():
+    import torch
+    pm = P()
+    tok = 256  # tokens per workgroup at 16 channels
+    sq, nh, nope, pe, theta = ROW * tok + 5000, 1, 0, 16, 10000.0
+    print(f"\n[case] postmix_fwd (small-head mix) sq={sq} nh={nh} nope={nope} pe={pe}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(95)
+    O = torch.empty(sq, nh, nope + pe, device="cuda", dtype=torch.bfloat16)
+    for lo in range(0, sq, 1 << 27):  # in slices: no full-size fp32 temporary
+        hi = min(sq, lo + (1 << 27))
+        O[lo:hi] = torch.randn(hi - lo, nh, nope + pe, device="cuda", generator=g).to(torch.bfloat16)
+    W = torch.tensor([[1.25]], device="cuda").to(torch.bfloat16)
+    pos = (torch.arange(sq, device="cuda", dtype=torch.int64) % 65536).to(torch.int32)
+    cos, sin = pm.postmix_rope_table(theta, pe, 65536)
+    Y = pm.postmix_fwd(O, W, cos, sin, pos, nope, pe)
+    torch.cuda.synchronize()
+
+    seam = ROW * tok
+    rng = np.random.default_rng(9)
+    picks = np.unique(np.concatenate([
+        np.arange(64), np.arange(seam - 600, seam + 600), np.arange(sq - 5000, sq),
+        rng.integers(0, sq, 2048)]))
+    ref = oracle.fwd(gu.host_bits(_sub(O, picks)), gu.host_bits(W), _sub(pos, picks).cpu().numpy(),
+                     theta, nope, pe)
+    gu.check_bf16(gu.host_bits(_sub(Y, picks)), ref, "Y at sampled tokens")
+
+    for lo, hi in [(0, 4096), (seam - 2048, seam + 2048), (sq - 5000, sq)]:
         part = pm.postmix_fwd(O[lo:hi].contiguous(), W, cos, sin, pos[lo:hi].contiguous(), nope, pe)
         np.testing.assert_array_equal(gu.host_bits(part), gu.host_bits(Y[lo:hi].contiguous()),
                                       err_msg=f"tokens [{lo}, {hi})")
