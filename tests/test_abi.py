@@ -150,6 +150,14 @@ def test_widest_rows_pass_the_shape_check():
     assert rc not in (pm.PM_ERR_NULL, pm.PM_ERR_SHAPE, pm.PM_ERR_ALIGN, pm.PM_ERR_OVERLAP), msg
 
 
+def test_rope_apply_shares_the_shape_limits():
+    L = pm.lib()
+    rc = L.postmix_rope_apply(A, C, D, 32768, E, 1, 1, (1 << 24) - 48, 64, -1, F, None)
+    assert rc == pm.PM_ERR_SHAPE and "2^24" in L.postmix_last_error().decode()
+    rc = L.postmix_rope_apply(A, C, D, 32768, E, 1, 0, 448, 64, -1, F, None)
+    assert rc == pm.PM_ERR_SHAPE and "nh" in L.postmix_last_error().decode()
+
+
 def test_empty_sq_is_a_noop_before_any_pointer_check():
     rc, _ = fwd(sq=0, O=0, Y=0, W=0)
     assert rc == pm.PM_OK
@@ -171,6 +179,7 @@ def test_empty_sq_is_a_noop_before_any_pointer_check():
     (dict(dW=A + 64), pm.PM_ERR_OVERLAP, "dW"),
     (dict(ws=B), pm.PM_ERR_OVERLAP, "workspace"),
     (dict(nh=200), pm.PM_ERR_SHAPE, "nh"),
+    (dict(nope=(1 << 24) - 48, pe=64), pm.PM_ERR_SHAPE, "2^24"),
     (dict(pos=0), pm.PM_ERR_NULL, "positions"),
 ])
 def test_dw_argument_errors(kw, code, word):
@@ -285,6 +294,7 @@ def bwd(**kw):
     (dict(dW=F + 64), pm.PM_ERR_OVERLAP, "dW"),
     (dict(ws=0x200000000), pm.PM_ERR_OVERLAP, "workspace"),
     (dict(nope=20), pm.PM_ERR_SHAPE, "nope"),
+    (dict(nope=(1 << 24) - 48, pe=64), pm.PM_ERR_SHAPE, "2^24"),
     (dict(sin=0), pm.PM_ERR_NULL, "rope_sin"),
 ])
 def test_fused_backward_argument_errors(kw, code, word):
