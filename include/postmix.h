@@ -150,8 +150,8 @@ int postmix_bwd_dw(const pm_bf16 *dY, const pm_bf16 *O, const float *rope_cos,
  * not a multiple of 256), or 64 < nh <= 128 with pe and nope multiples of
  * 32): each (token, channel chunk) of dY and O is read from HBM
  * once and feeds both the head-mix gradient and the weight-gradient partials.  That is one full read of dY
- * fewer than the two separate calls.  Other shapes (or
- * postmix_set_general_kernels(1)) run the two separate computations.
+ * fewer than the two separate calls.  Other shapes run the two separate
+ * computations.
  * dO is bitwise the same as postmix_bwd_dx's; dW is deterministic (token
  * blocks fixed by the shape, about half the size of postmix_bwd_dw's, and the
  * same fixed-order reduction), but it sums in a different order than
@@ -214,23 +214,6 @@ const char *postmix_status_string(int status);
 
 /* Message for the last failing call on this thread ("" if none). */
 const char *postmix_last_error(void);
-
-/*
- * Kernel choice (process-wide).  By default shapes whose channels split into
- * 128- or 256-channel parts that hold the whole pe range run the tiled kernels
- * (postmix_fwd / postmix_bwd_dx: one workgroup per tile of 32, 64, 96 or 128
- * head rows; postmix_bwd_dw: LDS-staged chunks); every other shape runs the
- * general kernels.  Head counts below the tile height are padded with zero
- * rows, and for nh <= 32 a tile holds several consecutive tokens with W
- * applied block-diagonally.  The products between different tokens are then
- * exact zeros for finite inputs; a non-finite value in one token makes the
- * other tokens of its tile NaN (0 * Inf), which the general kernels avoid.
- * enable != 0 routes every shape through the general kernels, which is how
- * the two are tested against each other.  Y and dO agree up to fp32
- * summation order; dW of either choice is bitwise repeatable, but the two
- * choices sum in different orders.  Returns the previous setting.
- */
-int postmix_set_general_kernels(int enable);
 
 #ifdef __cplusplus
 }

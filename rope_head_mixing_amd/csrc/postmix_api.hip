@@ -11,6 +11,7 @@
 
 #include "../../include/postmix.h"
 #include "postmix_launch.h"
+#include "postmix_testing.h"
 
 namespace {
 
@@ -34,7 +35,9 @@ int ok() {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 std::atomic<int> g_dev_cus[kMaxDevices];
-std::atomic<int> g_force_general{0};
+// test hook (postmix_testing.h): per calling thread, so it never changes
+// another thread's results
+thread_local int g_force_general = 0;
 
 int check_device(int* n_cu) {
     int dev = 0;
@@ -165,7 +168,7 @@ int mix_common(const char* xname, const pm_bf16* X, const pm_bf16* W, const floa
     a.Out = Out;
     a.n_cu = n_cu;
     a.waves_per_cu = 16;
-    a.force_general = g_force_general.load(std::memory_order_relaxed) != 0;
+    a.force_general = g_force_general != 0;
     hipError_t e = pm::launch_mix(a, dx, (hipStream_t)stream);
     if (e != hipSuccess) return fail(PM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -267,7 +270,7 @@ int postmix_bwd_dw(const pm_bf16* dY, const pm_bf16* O, const float* rope_cos,
     a.pe = pe;
     a.dW = dW;
     a.partials = (float*)workspace;
-    a.force_general = g_force_general.load(std::memory_order_relaxed) != 0;
+    a.force_general = g_force_general != 0;
     hipError_t e = pm::launch_dw(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(PM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -330,7 +333,7 @@ int postmix_bwd(const pm_bf16* dY, const pm_bf16* O, const pm_bf16* W, const flo
     mx.Out = dO;
     mx.n_cu = n_cu;
     mx.waves_per_cu = 16;
-    mx.force_general = g_force_general.load(std::memory_order_relaxed) != 0;
+    mx.force_general = g_force_general != 0;
     pm::DwArgs a;
     a.dY = dY;
     a.O = O;
@@ -464,8 +467,10 @@ const char* postmix_status_string(int status) {
 
 const char* postmix_last_error(void) { return g_last_error; }
 
-int postmix_set_general_kernels(int enable) {
-    return g_force_general.exchange(enable ? 1 : 0, std::memory_order_relaxed);
+int pm_testing_set_general_kernels(int enable) {
+    const int prev = g_force_general;
+    g_force_general = enable ? 1 : 0;
+    return prev;
 }
 
 }  // extern "C"

@@ -14,7 +14,6 @@ Entry points keep the C names:
     postmix_rope_table(theta, pe, table_rows, device=None)
     postmix_kv_index_remap(idx, sq, seqlen_kv, pad_value=-1, out=None)
     postmix_rope_apply(X, rope_cos, rope_sin, positions, nope, pe, direction, out=None)
-    postmix_set_general_kernels(enable)
 The unfused comparison route (unfused_fwd, unfused_bwd) is composed of these
 entry points only.
 Tensors: O/Y/dY/dO bfloat16 [sq, nh, nope+pe]; W bfloat16 [nh, nh] (W[g,h], g =
@@ -79,8 +78,9 @@ def lib():
     L.postmix_status_string.restype = ctypes.c_char_p
     L.postmix_last_error.argtypes = []
     L.postmix_last_error.restype = ctypes.c_char_p
-    L.postmix_set_general_kernels.argtypes = [ctypes.c_int]
-    L.postmix_set_general_kernels.restype = ctypes.c_int
+    # test hook (csrc/postmix_testing.h), not part of the public interface
+    L.pm_testing_set_general_kernels.argtypes = [ctypes.c_int]
+    L.pm_testing_set_general_kernels.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -101,65 +101,130 @@ def _stream_handle(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _need(t, name, dtype, ndim=None):
+def _fmt_shape(shape):
+    return "[" + ", ".join("*" if s is None else str(s) for s in shape) + "]"
+
+
+class _Spec:
+    """One tensor argument: its name, dtype and expected shape (None = any size)."""
+
+    def __init__(self, t, name, dtype, shape):
+        self.t, self.name, self.dtype, self.shape = t, name, dtype, shape
+
+
+def _validate(*specs):
+    """Check every tensor argument, in two passes: first what needs no device
+    (type, dtype, shape, contiguity) for all of them, then that all live on
+    one GPU device.  The C ABI sees only pointers and sizes, so a tensor that
+    is smaller than the sizes say would be read or written past its end; these
+    checks are what prevents that.  Returns the common device."""
     torch = _torch()
-    if not isinstance(t, torch.Tensor):
-        raise ValueError(f"{name} must be a torch.Tensor")
-    if t.dtype != dtype:
-        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be on a GPU device")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if ndim is not None and t.dim() != ndim:
-        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
-    return t
+    for s in specs:
+        t = s.t
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{s.name} must be a torch.Tensor")
+        if t.dtype != s.dtype:
+            raise ValueError(f"{s.name} must be {s.dtype}, got {t.dtype}")
+        if s.shape is not None and (t.dim() != len(s.shape) or any(
+                want is not None and got != want for got, want in zip(t.shape, s.shape))):
+            raise ValueError(f"{s.name} must have shape {_fmt_shape(s.shape)}, got {list(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{s.name} must be contiguous")
+    device = None
+    for s in specs:
+        if not s.t.is_cuda:
+            raise ValueError(f"{s.name} must be on a GPU device, got {s.t.device}")
+        if device is None:
+            device = s.t.device
+        elif s.t.device != device:
+            raise ValueError(f"{s.name} is on {s.t.device}, but {specs[0].name} is on {device}: "
+                             "all tensors must be on one device")
+    return device
 
 
-def _rope_ptrs(rope_cos, rope_sin, positions, pe, sq):
+def _rope_specs(rope_cos, rope_sin, positions, pe, sq):
+    """Specs of the table arguments (none when pe == 0: they are not read)."""
     torch = _torch()
     if pe == 0:
+        return []
+    rows = rope_cos.shape[0] if isinstance(rope_cos, torch.Tensor) and rope_cos.dim() == 2 else None
+    return [_Spec(rope_cos, "rope_cos", torch.float32, (rows, pe // 2)),
+            _Spec(rope_sin, "rope_sin", torch.float32, (rows, pe // 2)),
+            _Spec(positions, "positions", torch.int32, (sq,))]
+
+
+def _rope_ptrs(rope_cos, rope_sin, positions, pe):
+    if pe == 0:
         return None, None, 0, None
-    _need(rope_cos, "rope_cos", torch.float32, 2)
-    _need(rope_sin, "rope_sin", torch.float32, 2)
-    _need(positions, "positions", torch.int32, 1)
-    if rope_cos.shape != rope_sin.shape or rope_cos.shape[1] != pe // 2:
-        raise ValueError(f"rope_cos/rope_sin must both be [rows, {pe // 2}]")
-    if positions.shape[0] != sq:
-        raise ValueError(f"positions must have {sq} entries")
     return rope_cos.data_ptr(), rope_sin.data_ptr(), rope_cos.shape[0], positions.data_ptr()
 
 
-def _act_shape(X, name, nope, pe):
-    sq, nh, d = X.shape
-    if d != nope + pe:
-        raise ValueError(f"{name} last dim {d} != nope + pe = {nope + pe}")
-    return sq, nh, d
+def _act_dims(X, name, nope, pe):
+    """(sq, nh) of an activation [sq, nh, nope + pe]; raises on a wrong rank or width."""
+    torch = _torch()
+    if not isinstance(X, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if X.dim() != 3 or X.shape[2] != nope + pe:
+        raise ValueError(f"{name} must have shape [sq, nh, {nope + pe}] (nope + pe = {nope} + {pe}), "
+                         f"got {list(X.shape)}")
+    return X.shape[0], X.shape[1]
+
+
+class _on_device:
+    """Make `device` current for a call (the library launches on the current
+    device's stream and checks that device), restoring the previous one."""
+
+    def __init__(self, device):
+        self.device = device
+        self.prev = None
+
+    def __enter__(self):
+        torch = _torch()
+        cur = torch.cuda.current_device()
+        if self.device.index is not None and self.device.index != cur:
+            self.prev = cur
+            torch.cuda.set_device(self.device)
+        return self
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            _torch().cuda.set_device(self.prev)
+        return False
 
 
 def postmix_fwd(O, W, rope_cos, rope_sin, positions, nope: int, pe: int, out=None):
     """Y = inv_rope(W . O) per token (== W . inv_rope(O)), bf16 out."""
     torch = _torch()
-    _need(O, "O", torch.bfloat16, 3)
-    sq, nh, d = _act_shape(O, "O", nope, pe)
-    _need(W, "W", torch.bfloat16, 2)
-    c, s, rows, p = _rope_ptrs(rope_cos, rope_sin, positions, pe, sq)
-    Y = torch.empty_like(O) if out is None else _need(out, "out", torch.bfloat16, 3)
-    _check(lib().postmix_fwd(O.data_ptr(), W.data_ptr(), c, s, rows, p, sq, nh, nope, pe,
-                             Y.data_ptr(), _stream_handle(O.device)))
+    sq, nh = _act_dims(O, "O", nope, pe)
+    d = nope + pe
+    specs = [_Spec(O, "O", torch.bfloat16, (sq, nh, d)), _Spec(W, "W", torch.bfloat16, (nh, nh)),
+             *_rope_specs(rope_cos, rope_sin, positions, pe, sq)]
+    if out is not None:
+        specs.append(_Spec(out, "out", torch.bfloat16, (sq, nh, d)))
+    dev = _validate(*specs)
+    c, s, rows, p = _rope_ptrs(rope_cos, rope_sin, positions, pe)
+    Y = torch.empty_like(O) if out is None else out
+    with _on_device(dev):
+        _check(lib().postmix_fwd(O.data_ptr(), W.data_ptr(), c, s, rows, p, sq, nh, nope, pe,
+                                 Y.data_ptr(), _stream_handle(dev)))
     return Y
 
 
 def postmix_bwd_dx(dY, W, rope_cos, rope_sin, positions, nope: int, pe: int, out=None):
     """dO = rope(W^T . dY) per token, bf16 out."""
     torch = _torch()
-    _need(dY, "dY", torch.bfloat16, 3)
-    sq, nh, d = _act_shape(dY, "dY", nope, pe)
-    _need(W, "W", torch.bfloat16, 2)
-    c, s, rows, p = _rope_ptrs(rope_cos, rope_sin, positions, pe, sq)
-    dO = torch.empty_like(dY) if out is None else _need(out, "out", torch.bfloat16, 3)
-    _check(lib().postmix_bwd_dx(dY.data_ptr(), W.data_ptr(), c, s, rows, p, sq, nh, nope, pe,
-                                dO.data_ptr(), _stream_handle(dY.device)))
+    sq, nh = _act_dims(dY, "dY", nope, pe)
+    d = nope + pe
+    specs = [_Spec(dY, "dY", torch.bfloat16, (sq, nh, d)), _Spec(W, "W", torch.bfloat16, (nh, nh)),
+             *_rope_specs(rope_cos, rope_sin, positions, pe, sq)]
+    if out is not None:
+        specs.append(_Spec(out, "out", torch.bfloat16, (sq, nh, d)))
+    dev = _validate(*specs)
+    c, s, rows, p = _rope_ptrs(rope_cos, rope_sin, positions, pe)
+    dO = torch.empty_like(dY) if out is None else out
+    with _on_device(dev):
+        _check(lib().postmix_bwd_dx(dY.data_ptr(), W.data_ptr(), c, s, rows, p, sq, nh, nope, pe,
+                                    dO.data_ptr(), _stream_handle(dev)))
     return dO
 
 
@@ -167,25 +232,34 @@ def postmix_bwd_dw_workspace_bytes(sq: int, nh: int, nope: int, pe: int) -> int:
     return int(lib().postmix_bwd_dw_workspace_bytes(sq, nh, nope, pe))
 
 
+def _workspace_spec(workspace):
+    """A caller's workspace (any dtype; its size in bytes is passed on and checked by the library)."""
+    return [] if workspace is None else [_Spec(workspace, "workspace",
+                                               getattr(workspace, "dtype", None), None)]
+
+
 def postmix_bwd_dw(dY, O, rope_cos, rope_sin, positions, nope: int, pe: int, out=None,
                    workspace=None):
     """dW[g,h] = sum_{s,c} dY[s,g,c] * inv_rope(O)[s,h,c], fp32, deterministic."""
     torch = _torch()
-    _need(dY, "dY", torch.bfloat16, 3)
-    _need(O, "O", torch.bfloat16, 3)
-    sq, nh, d = _act_shape(dY, "dY", nope, pe)
-    if tuple(O.shape) != tuple(dY.shape):
-        raise ValueError("O and dY must have the same shape")
-    c, s, rows, p = _rope_ptrs(rope_cos, rope_sin, positions, pe, sq)
-    dW = (torch.empty((nh, nh), dtype=torch.float32, device=dY.device) if out is None
-          else _need(out, "out", torch.float32, 2))
+    sq, nh = _act_dims(dY, "dY", nope, pe)
+    d = nope + pe
+    specs = [_Spec(dY, "dY", torch.bfloat16, (sq, nh, d)), _Spec(O, "O", torch.bfloat16, (sq, nh, d)),
+             *_rope_specs(rope_cos, rope_sin, positions, pe, sq)]
+    if out is not None:
+        specs.append(_Spec(out, "out", torch.float32, (nh, nh)))
+    specs += _workspace_spec(workspace)
+    dev = _validate(*specs)
+    c, s, rows, p = _rope_ptrs(rope_cos, rope_sin, positions, pe)
+    dW = torch.empty((nh, nh), dtype=torch.float32, device=dev) if out is None else out
     need = postmix_bwd_dw_workspace_bytes(sq, nh, nope, pe)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dY.device)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib().postmix_bwd_dw(dY.data_ptr(), O.data_ptr(), c, s, rows, p, sq, nh, nope, pe,
-                                dW.data_ptr(), workspace.data_ptr(), ws_bytes,
-                                _stream_handle(dY.device)))
+    with _on_device(dev):
+        _check(lib().postmix_bwd_dw(dY.data_ptr(), O.data_ptr(), c, s, rows, p, sq, nh, nope, pe,
+                                    dW.data_ptr(), workspace.data_ptr(), ws_bytes,
+                                    _stream_handle(dev)))
     return dW
 
 
@@ -193,23 +267,28 @@ def postmix_bwd(dY, O, W, rope_cos, rope_sin, positions, nope: int, pe: int, out
                 out_dW=None, workspace=None):
     """Both gradients in one call: (dO, dW) as postmix_bwd_dx and postmix_bwd_dw."""
     torch = _torch()
-    _need(dY, "dY", torch.bfloat16, 3)
-    _need(O, "O", torch.bfloat16, 3)
-    _need(W, "W", torch.bfloat16, 2)
-    sq, nh, d = _act_shape(dY, "dY", nope, pe)
-    if tuple(O.shape) != tuple(dY.shape):
-        raise ValueError("O and dY must have the same shape")
-    c, s, rows, p = _rope_ptrs(rope_cos, rope_sin, positions, pe, sq)
-    dO = torch.empty_like(dY) if out_dO is None else _need(out_dO, "out_dO", torch.bfloat16, 3)
-    dW = (torch.empty((nh, nh), dtype=torch.float32, device=dY.device) if out_dW is None
-          else _need(out_dW, "out_dW", torch.float32, 2))
+    sq, nh = _act_dims(dY, "dY", nope, pe)
+    d = nope + pe
+    specs = [_Spec(dY, "dY", torch.bfloat16, (sq, nh, d)), _Spec(O, "O", torch.bfloat16, (sq, nh, d)),
+             _Spec(W, "W", torch.bfloat16, (nh, nh)),
+             *_rope_specs(rope_cos, rope_sin, positions, pe, sq)]
+    if out_dO is not None:
+        specs.append(_Spec(out_dO, "out_dO", torch.bfloat16, (sq, nh, d)))
+    if out_dW is not None:
+        specs.append(_Spec(out_dW, "out_dW", torch.float32, (nh, nh)))
+    specs += _workspace_spec(workspace)
+    dev = _validate(*specs)
+    c, s, rows, p = _rope_ptrs(rope_cos, rope_sin, positions, pe)
+    dO = torch.empty_like(dY) if out_dO is None else out_dO
+    dW = torch.empty((nh, nh), dtype=torch.float32, device=dev) if out_dW is None else out_dW
     need = postmix_bwd_dw_workspace_bytes(sq, nh, nope, pe)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dY.device)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib().postmix_bwd(dY.data_ptr(), O.data_ptr(), W.data_ptr(), c, s, rows, p, sq, nh,
-                             nope, pe, dO.data_ptr(), dW.data_ptr(), workspace.data_ptr(),
-                             ws_bytes, _stream_handle(dY.device)))
+    with _on_device(dev):
+        _check(lib().postmix_bwd(dY.data_ptr(), O.data_ptr(), W.data_ptr(), c, s, rows, p, sq, nh,
+                                 nope, pe, dO.data_ptr(), dW.data_ptr(), workspace.data_ptr(),
+                                 ws_bytes, _stream_handle(dev)))
     return dO, dW
 
 
@@ -217,12 +296,18 @@ def postmix_rope_apply(X, rope_cos, rope_sin, positions, nope: int, pe: int, dir
                        out=None):
     """Out = inv_rope(X) (direction -1) or rope(X) (+1), materialised in bf16."""
     torch = _torch()
-    _need(X, "X", torch.bfloat16, 3)
-    sq, nh, d = _act_shape(X, "X", nope, pe)
-    c, s, rows, p = _rope_ptrs(rope_cos, rope_sin, positions, pe, sq)
-    Out = torch.empty_like(X) if out is None else _need(out, "out", torch.bfloat16, 3)
-    _check(lib().postmix_rope_apply(X.data_ptr(), c, s, rows, p, sq, nh, nope, pe, int(direction),
-                                    Out.data_ptr(), _stream_handle(X.device)))
+    sq, nh = _act_dims(X, "X", nope, pe)
+    d = nope + pe
+    specs = [_Spec(X, "X", torch.bfloat16, (sq, nh, d)),
+             *_rope_specs(rope_cos, rope_sin, positions, pe, sq)]
+    if out is not None:
+        specs.append(_Spec(out, "out", torch.bfloat16, (sq, nh, d)))
+    dev = _validate(*specs)
+    c, s, rows, p = _rope_ptrs(rope_cos, rope_sin, positions, pe)
+    Out = torch.empty_like(X) if out is None else out
+    with _on_device(dev):
+        _check(lib().postmix_rope_apply(X.data_ptr(), c, s, rows, p, sq, nh, nope, pe,
+                                        int(direction), Out.data_ptr(), _stream_handle(dev)))
     return Out
 
 
@@ -245,25 +330,37 @@ def unfused_bwd(dY, O, W, rope_cos, rope_sin, positions, nope: int, pe: int, wor
 def postmix_kv_index_remap(idx, sq: int, seqlen_kv: int, pad_value: int = -1, out=None):
     """Per-batch-local KV column indices -> flat-global: idx [b*sq, topk] int32."""
     torch = _torch()
-    _need(idx, "idx", torch.int32, 2)
+    if not isinstance(idx, torch.Tensor) or idx.dim() != 2:
+        raise ValueError("idx must be a 2-dimensional torch.Tensor [rows, topk]")
     rows, topk = idx.shape
-    out = torch.empty_like(idx) if out is None else _need(out, "out", torch.int32, 2)
-    _check(lib().postmix_kv_index_remap(idx.data_ptr(), rows, sq, topk, seqlen_kv, pad_value,
-                                        out.data_ptr(), _stream_handle(idx.device)))
+    specs = [_Spec(idx, "idx", torch.int32, (rows, topk))]
+    if out is not None:
+        specs.append(_Spec(out, "out", torch.int32, (rows, topk)))
+    dev = _validate(*specs)
+    out = torch.empty_like(idx) if out is None else out
+    with _on_device(dev):
+        _check(lib().postmix_kv_index_remap(idx.data_ptr(), rows, sq, topk, seqlen_kv, pad_value,
+                                            out.data_ptr(), _stream_handle(dev)))
     return out
 
 
-def postmix_set_general_kernels(enable: bool) -> bool:
-    """Route fwd/dx through the general kernel for every shape; returns the previous setting."""
-    return bool(lib().postmix_set_general_kernels(1 if enable else 0))
+def testing_set_general_kernels(enable: bool) -> bool:
+    """Test hook: this thread's later calls run the general kernels for every
+    shape; returns the thread's previous setting."""
+    return bool(lib().pm_testing_set_general_kernels(1 if enable else 0))
 
 
 def postmix_rope_table(theta: float, pe: int, table_rows: int, device=None):
     """(cos, sin) fp32 [table_rows, pe/2] built on the GPU from an fp64 angle."""
     torch = _torch()
     device = torch.device("cuda") if device is None else torch.device(device)
+    if device.type != "cuda":
+        raise ValueError(f"device must be a GPU device, got {device}")
+    if device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
     cos = torch.empty((table_rows, pe // 2), dtype=torch.float32, device=device)
     sin = torch.empty_like(cos)
-    _check(lib().postmix_rope_table(float(theta), pe, table_rows, cos.data_ptr(), sin.data_ptr(),
-                                    _stream_handle(device)))
+    with _on_device(device):
+        _check(lib().postmix_rope_table(float(theta), pe, table_rows, cos.data_ptr(), sin.data_ptr(),
+                                        _stream_handle(device)))
     return cos, sin

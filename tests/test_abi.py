@@ -260,6 +260,59 @@ def test_binding_rejects_wrong_dtypes_by_name():
         pm.postmix_bwd_dw(O, O, None, None, None, 48, 16)
 
 
+def test_binding_checks_shapes_before_any_launch():
+    """The C ABI sees pointers and sizes only, so the binding checks every
+    tensor's shape against the sizes it passes (a short W or output would
+    otherwise be read or written past its end on the device).  All of these
+    are CPU tensors: the shape checks come before the device check, so each
+    case raises before any launch."""
+    import re as _re
+    torch = pytest.importorskip("torch")
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    O = torch.zeros((3, 4, 64), dtype=bf)
+    W = torch.zeros((4, 4), dtype=bf)
+    cos, sin = torch.zeros((8, 8), dtype=f32), torch.zeros((8, 8), dtype=f32)
+    pos = torch.zeros((3,), dtype=i32)
+    idx = torch.zeros((6, 16), dtype=i32)
+    cases = [
+        (lambda: pm.postmix_fwd(O, torch.zeros((4, 5), dtype=bf), cos, sin, pos, 48, 16), "W must have shape [4, 4]"),
+        (lambda: pm.postmix_fwd(O, torch.zeros((3, 3), dtype=bf), cos, sin, pos, 48, 16), "W must have shape [4, 4]"),
+        (lambda: pm.postmix_fwd(O, W, cos, sin, pos, 48, 16, out=torch.zeros((2, 4, 64), dtype=bf)),
+         "out must have shape [3, 4, 64]"),
+        (lambda: pm.postmix_fwd(O, W, cos, sin, pos, 40, 16), "O must have shape [sq, nh, 56]"),
+        (lambda: pm.postmix_fwd(O, W, cos, torch.zeros((8, 4), dtype=f32), pos, 48, 16), "rope_sin must have shape [8, 8]"),
+        (lambda: pm.postmix_fwd(O, W, cos, torch.zeros((7, 8), dtype=f32), pos, 48, 16), "rope_sin must have shape [8, 8]"),
+        (lambda: pm.postmix_fwd(O, W, cos, sin, torch.zeros((2,), dtype=i32), 48, 16), "positions must have shape [3]"),
+        (lambda: pm.postmix_bwd_dx(O, W, cos, sin, pos, 48, 16, out=torch.zeros((3, 4, 48), dtype=bf)),
+         "out must have shape [3, 4, 64]"),
+        (lambda: pm.postmix_bwd_dx(O, torch.zeros((16,), dtype=bf), cos, sin, pos, 48, 16), "W must have shape [4, 4]"),
+        (lambda: pm.postmix_bwd_dw(O, torch.zeros((3, 2, 64), dtype=bf), cos, sin, pos, 48, 16),
+         "O must have shape [3, 4, 64]"),
+        (lambda: pm.postmix_bwd_dw(O, O, cos, sin, pos, 48, 16, out=torch.zeros((4, 3), dtype=f32)),
+         "out must have shape [4, 4]"),
+        (lambda: pm.postmix_bwd(O, O, torch.zeros((2, 2), dtype=bf), cos, sin, pos, 48, 16), "W must have shape [4, 4]"),
+        (lambda: pm.postmix_bwd(O, O, W, cos, sin, pos, 48, 16, out_dO=torch.zeros((3, 4, 63), dtype=bf)),
+         "out_dO must have shape [3, 4, 64]"),
+        (lambda: pm.postmix_bwd(O, O, W, cos, sin, pos, 48, 16, out_dW=torch.zeros((5, 5), dtype=f32)),
+         "out_dW must have shape [4, 4]"),
+        (lambda: pm.postmix_bwd(O, O, W, cos, sin, pos, 48, 16, workspace=[0] * 4), "workspace must be a torch.Tensor"),
+        (lambda: pm.postmix_rope_apply(O, cos, sin, pos, 48, 16, -1, out=torch.zeros((4, 4, 64), dtype=bf)),
+         "out must have shape [3, 4, 64]"),
+        (lambda: pm.postmix_kv_index_remap(idx, 3, 100, out=torch.zeros((6, 15), dtype=i32)),
+         "out must have shape [6, 16]"),
+        (lambda: pm.postmix_kv_index_remap(torch.zeros((96,), dtype=i32), 3, 100), "idx must be a 2-dimensional"),
+    ]
+    for fn, msg in cases:
+        with pytest.raises(ValueError, match=_re.escape(msg)):
+            fn()
+    # well-formed CPU tensors pass the shape checks and stop at the device check
+    with pytest.raises(ValueError, match="must be on a GPU device"):
+        pm.postmix_fwd(O, W, cos, sin, pos, 48, 16)
+    with pytest.raises(ValueError, match="must be on a GPU device"):
+        pm.postmix_bwd(O, O, W, cos, sin, pos, 48, 16, out_dO=torch.zeros_like(O),
+                       out_dW=torch.zeros((4, 4), dtype=f32))
+
+
 def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(pm, "_lib", None)
     monkeypatch.setattr(pm, "LIB_PATH", str(tmp_path / "missing.so"))

@@ -117,9 +117,9 @@ def test_02_tiny_workload():
 def kernel_policy(request):
     """Run a test with the default (tiled where the shape allows) kernels, and
     again with every shape forced onto the general kernels."""
-    prev = P().postmix_set_general_kernels(request.param == "general")
+    prev = P().testing_set_general_kernels(request.param == "general")
     yield request.param
-    P().postmix_set_general_kernels(prev)
+    P().testing_set_general_kernels(prev)
 
 
 @pytest.mark.parametrize("sq,nh,nope,pe,off", [
@@ -174,13 +174,13 @@ def test_tiled_and_general_kernels_agree(sq, nh, nope, pe):
     fp32 evaluation order of the rotation (one bf16 ulp at most)."""
     c = synthetic.case(sq, nh, nope, pe, seed=777, pos_offset=16384)
     dv = Dev(c)
-    prev = P().postmix_set_general_kernels(False)
+    prev = P().testing_set_general_kernels(False)
     try:
         Y1, dO1, dW1 = gu.host_bits(dv.fwd()), gu.host_bits(dv.dx()), dv.dw().cpu().numpy()
-        P().postmix_set_general_kernels(True)
+        P().testing_set_general_kernels(True)
         Y2, dO2, dW2 = gu.host_bits(dv.fwd()), gu.host_bits(dv.dx()), dv.dw().cpu().numpy()
     finally:
-        P().postmix_set_general_kernels(prev)
+        P().testing_set_general_kernels(prev)
     np.testing.assert_array_equal(Y1[..., :nope], Y2[..., :nope])
     np.testing.assert_array_equal(dO1[..., :nope], dO2[..., :nope])
     for a, b in [(Y1, Y2), (dO1, dO2)]:
