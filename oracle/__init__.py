@@ -91,6 +91,7 @@ def _bind(lib):
         "oracle_bwd_dx_f64": ([_P, _P, _P, _F64, _I64, _I32, _I32, _I32, _P, _I32], _I32),
         "oracle_bwd_dw_bf16": ([_P, _P, _P, _F64, _I64, _I32, _I32, _I32, _P, _I32], _I32),
         "oracle_bwd_dw_f64": ([_P, _P, _P, _F64, _I64, _I32, _I32, _I32, _P, _I32], _I32),
+        "oracle_bwd_dw_abs_bf16": ([_P, _P, _P, _F64, _I64, _I32, _I32, _I32, _P, _I32], _I32),
         "oracle_rotate_f64": ([_P, _P, _P, _F64, _I64, _I32, _I32, _I32, _I32], _I32),
         "oracle_fwd_at_bf16": ([_P, _P, _P, _F64, _I64, _I32, _I32, _I32, _P, _I64, _P], _I32),
         "oracle_bwd_dx_at_bf16": ([_P, _P, _P, _F64, _I64, _I32, _I32, _I32, _P, _I64, _P], _I32),
@@ -189,6 +190,21 @@ def bwd_dw(dY, O, positions, theta, nope, pe, nthreads=None) -> np.ndarray:
     nt = default_threads() if nthreads is None else nthreads
     _check_rc(fn(_ptr(dY), _ptr(O), _ptr(p), float(theta), sq, nh, nope, pe, _ptr(dW), nt), "bwd_dw")
     return dW
+
+
+def bwd_dw_abs(dY, O, positions, theta, nope, pe, nthreads=None) -> np.ndarray:
+    """A[g,h] = sum_{s,c} |dY[s,g,c] * inv_rope(O)[s,h,c]| (the magnitude of the
+    terms of each dW entry, i.e. its conditioning); bf16 inputs; fp64 [nh, nh]."""
+    dY, O, kind = _same_kind(dY, O, "dY", "O")
+    assert kind == "bf16"
+    sq, nh, d = dY.shape
+    assert O.shape == dY.shape and d == nope + pe
+    p = _positions(positions, sq)
+    A = np.empty((nh, nh), np.float64)
+    nt = default_threads() if nthreads is None else nthreads
+    _check_rc(_load().oracle_bwd_dw_abs_bf16(_ptr(dY), _ptr(O), _ptr(p), float(theta), sq, nh, nope, pe,
+                                             _ptr(A), nt), "bwd_dw_abs")
+    return A
 
 
 def rotate(X, positions, theta, nope, pe, direction) -> np.ndarray:

@@ -192,6 +192,7 @@ typedef struct {
     int64_t sq;
     int32_t nh, nope, pe;
     double *out;     /* fwd/dx: [sq, nh, d]; dW: [nthreads, nh, nh]      */
+    int abs_terms;   /* dW only: sum |dY * X| instead of dY * X          */
 } problem;
 
 static int shape_ok(int64_t sq, int32_t nh, int32_t nope, int32_t pe)
@@ -244,7 +245,7 @@ int oracle_fwd_bf16(const uint16_t *O, const uint16_t *W,
                     int32_t nh, int32_t nope, int32_t pe, double *Y,
                     int32_t nthreads)
 {
-    problem p = {O, 1, NULL, 0, W, 1, positions, theta, sq, nh, nope, pe, Y};
+    problem p = {O, 1, NULL, 0, W, 1, positions, theta, sq, nh, nope, pe, Y, 0};
     return run_fwd(&p, nthreads);
 }
 
@@ -252,7 +253,7 @@ int oracle_fwd_f64(const double *O, const double *W, const int32_t *positions,
                    double theta, int64_t sq, int32_t nh, int32_t nope,
                    int32_t pe, double *Y, int32_t nthreads)
 {
-    problem p = {O, 0, NULL, 0, W, 0, positions, theta, sq, nh, nope, pe, Y};
+    problem p = {O, 0, NULL, 0, W, 0, positions, theta, sq, nh, nope, pe, Y, 0};
     return run_fwd(&p, nthreads);
 }
 
@@ -303,7 +304,7 @@ int oracle_bwd_dx_bf16(const uint16_t *dY, const uint16_t *W,
                        int32_t nh, int32_t nope, int32_t pe, double *dO,
                        int32_t nthreads)
 {
-    problem p = {dY, 1, NULL, 0, W, 1, positions, theta, sq, nh, nope, pe, dO};
+    problem p = {dY, 1, NULL, 0, W, 1, positions, theta, sq, nh, nope, pe, dO, 0};
     return run_dx(&p, nthreads);
 }
 
@@ -312,7 +313,7 @@ int oracle_bwd_dx_f64(const double *dY, const double *W,
                       int32_t nh, int32_t nope, int32_t pe, double *dO,
                       int32_t nthreads)
 {
-    problem p = {dY, 0, NULL, 0, W, 0, positions, theta, sq, nh, nope, pe, dO};
+    problem p = {dY, 0, NULL, 0, W, 0, positions, theta, sq, nh, nope, pe, dO, 0};
     return run_dx(&p, nthreads);
 }
 
@@ -343,7 +344,10 @@ static void dw_rows(void *vctx, int64_t lo, int64_t hi, int tid)
         for (int32_t g = 0; g < nh; ++g)
             for (int32_t h = 0; h < nh; ++h) {
                 double t = 0.0;
-                for (int32_t c = 0; c < d; ++c) t += dy[g * d + c] * x[h * d + c];
+                if (p->abs_terms)
+                    for (int32_t c = 0; c < d; ++c) t += fabs(dy[g * d + c] * x[h * d + c]);
+                else
+                    for (int32_t c = 0; c < d; ++c) t += dy[g * d + c] * x[h * d + c];
                 acc[g * nh + h] += t;
             }
     }
@@ -374,7 +378,7 @@ int oracle_bwd_dw_bf16(const uint16_t *dY, const uint16_t *O,
                        int32_t nh, int32_t nope, int32_t pe, double *dW,
                        int32_t nthreads)
 {
-    problem p = {dY, 1, O, 1, NULL, 0, positions, theta, sq, nh, nope, pe, NULL};
+    problem p = {dY, 1, O, 1, NULL, 0, positions, theta, sq, nh, nope, pe, NULL, 0};
     return run_dw(&p, dW, nthreads);
 }
 
@@ -383,8 +387,25 @@ int oracle_bwd_dw_f64(const double *dY, const double *O,
                       int32_t nh, int32_t nope, int32_t pe, double *dW,
                       int32_t nthreads)
 {
-    problem p = {dY, 0, O, 0, NULL, 0, positions, theta, sq, nh, nope, pe, NULL};
+    problem p = {dY, 0, O, 0, NULL, 0, positions, theta, sq, nh, nope, pe, NULL, 0};
     return run_dw(&p, dW, nthreads);
+}
+
+/* The magnitude of the terms of each weight-gradient entry,
+ *   A[g,h] = sum_s sum_c |dY[s,g,c] * inv_rope(O)[s,h,c]|,
+ * the same loops with each product's absolute value.  A[g,h] / |dW[g,h]| is
+ * the condition number of the sum: an entry that cancels to far below A[g,h]
+ * cannot be computed in fp32 to a small relative error in any order, and
+ * u * A[g,h] (u = 2^-24) is the size of one rounding at the largest magnitude
+ * a partial sum of its terms can reach.  The parity tests use it to bound
+ * such entries. */
+int oracle_bwd_dw_abs_bf16(const uint16_t *dY, const uint16_t *O,
+                           const int32_t *positions, double theta, int64_t sq,
+                           int32_t nh, int32_t nope, int32_t pe, double *A,
+                           int32_t nthreads)
+{
+    problem p = {dY, 1, O, 1, NULL, 0, positions, theta, sq, nh, nope, pe, NULL, 1};
+    return run_dw(&p, A, nthreads);
 }
 
 /* ------------------------------------------------------------------ */

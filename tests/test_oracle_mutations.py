@@ -36,6 +36,8 @@ MUTANTS = [
      "rotate_head(o + h * d, x + h * d, p->nope, p->pe, cs, sn, +1);", 1),
     ("dw_transposed_output", "acc[g * nh + h] += t;", "acc[h * nh + g] += t;", 0),
     ("dw_wrong_head", "t += dy[g * d + c] * x[h * d + c];", "t += dy[g * d + c] * x[g * d + c];", 0),
+    ("dw_abs_dropped", "t += fabs(dy[g * d + c] * x[h * d + c]);", "t += dy[g * d + c] * x[h * d + c];", 0),
+    ("dw_abs_one_factor", "t += fabs(dy[g * d + c] * x[h * d + c]);", "t += fabs(dy[g * d + c]) * x[h * d + c];", 0),
     ("dw_dropped_slab", "for (int32_t k = 0; k < nthreads; ++k) t += slabs[(int64_t)k * nh * nh + i];",
      "for (int32_t k = 0; k + 1 < nthreads; ++k) t += slabs[(int64_t)k * nh * nh + i];", 0),
     ("rows_skip_first_of_chunk", "tasks[t].lo = n * t / nthreads;",

@@ -14,7 +14,11 @@ the oracle is pinned by:
     for pe channels, the rotation partner);
   * the adjoint identities <dY, Y> = <dO, O> = <dW, W> (Y is linear in O and W);
   * central finite differences for dO and dW (exact up to rounding: linear loss);
-  * the one-by-one evaluators agree with the full ones.
+  * the one-by-one evaluators agree with the full ones;
+  * the magnitude sums of the weight-gradient terms (each dW entry's
+    conditioning, used by the GPU tests' dW bound) against brute force with
+    the expm rotations, and against dW itself when every term is
+    non-negative.
 """
 from decimal import Decimal, localcontext
 
@@ -206,6 +210,39 @@ def test_backward_brute_force_with_rotation_matrices(nh, nope, pe):
         np.testing.assert_allclose(dO[s], (W.T @ dY[s]) @ Rp.T, rtol=0, atol=1e-11)
         dW_ref += dY[s] @ (O[s] @ Rm.T).T
     np.testing.assert_allclose(dW, dW_ref, rtol=0, atol=1e-10)
+
+
+@pytest.mark.parametrize("nh,nope,pe", [(4, 48, 16), (3, 6, 4), (1, 8, 8)])
+def test_dw_term_magnitudes_brute_force(nh, nope, pe):
+    """A[g,h] = sum_{s,c} |dY[s,g,c] X[s,h,c]| with X = O rotated by the
+    expm matrices (numpy only), and A >= |dW| entry by entry."""
+    sq, d = 5, nope + pe
+    to_bits = synthetic.f32_to_bf16_bits
+    O = to_bits(rand((sq, nh, d), 41).astype(np.float32))
+    dY = to_bits(rand((sq, nh, d), 42).astype(np.float32))
+    pos = np.array([0, 3, 99, 4000, 31000], np.int32)
+    A = oracle.bwd_dw_abs(dY, O, pos, THETA, nope, pe)
+    Of, dYf = synthetic.bf16_bits_to_f32(O).astype(np.float64), synthetic.bf16_bits_to_f32(dY).astype(np.float64)
+    inv = textbook_inv_freq(THETA, pe)
+    A_ref = np.zeros((nh, nh))
+    for s in range(sq):
+        X = Of[s] @ rotation_matrix_expm(pos[s] * inv, nope, pe, -1).T
+        A_ref += np.abs(dYf[s]) @ np.abs(X).T
+    np.testing.assert_allclose(A, A_ref, rtol=1e-12, atol=1e-12)
+    dW = oracle.bwd_dw(dY, O, pos, THETA, nope, pe)
+    assert np.all(A >= np.abs(dW) * (1 - 1e-12))
+
+
+def test_dw_term_magnitudes_equal_dw_for_nonnegative_terms():
+    """With zero positions (X = O) and non-negative dY and O, every term is
+    non-negative, so A equals dW itself."""
+    sq, nh, nope, pe = 6, 3, 16, 16
+    to_bits = synthetic.f32_to_bf16_bits
+    O = to_bits(np.abs(rand((sq, nh, nope + pe), 43)).astype(np.float32))
+    dY = to_bits(np.abs(rand((sq, nh, nope + pe), 44)).astype(np.float32))
+    pos = np.zeros(sq, np.int32)
+    np.testing.assert_array_equal(oracle.bwd_dw_abs(dY, O, pos, THETA, nope, pe),
+                                  oracle.bwd_dw(dY, O, pos, THETA, nope, pe))
 
 
 # --------------------------------------------------------------------------
