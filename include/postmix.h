@@ -125,11 +125,13 @@ size_t postmix_bwd_dw_workspace_bytes(int64_t sq, int32_t nh, int32_t nope,
  * absorbed-MQA sparse backward").  The rotated pe operand is split into a
  * bf16 high part and a bf16 low correction (the compensated product of
  * tilelang-ascend PR #1640), both accumulated in fp32.
- * Accuracy: each element of a block's partial is one fp32 chain of n =
- * (tokens in the block) * (nope + pe) / 16 k-steps, whose norm-wise relative
- * error grows like 2^-24 * sqrt(n).  The production shape (n = 2^10) is far
- * inside the 1e-4 bar; a single token of 2^24 channels (n = 2^20, the
- * widest row) measured 1.05e-4.
+ * Accuracy: each element of a partial is one fp32 chain of k-steps (16
+ * channels of one token each), whose norm-wise relative error grows like
+ * 2^-24 * sqrt(length).  No chain is longer than 2^14 k-steps: blocks whose
+ * tokens would exceed that are made smaller, and a token wider than 2^18
+ * channels is split into channel spans with a partial each (one token of
+ * 2^24 channels, a single 2^20-step chain, had measured 1.05e-4 relative;
+ * the production blocks take 2^10 steps and are partitioned as before).
  *   dY, O     [sq, nh, nope+pe] bf16, read
  *   dW        [nh, nh] fp32, written
  *   workspace device scratch of workspace_bytes >= postmix_bwd_dw_workspace_bytes;

@@ -203,9 +203,9 @@ size_t postmix_bwd_dw_workspace_bytes(int64_t sq, int32_t nh, int32_t nope, int3
     const int rc = check_shape(sq, nh, nope, pe);
     memcpy(g_last_error, saved, sizeof saved);  // a size query leaves the message alone
     if (rc || sq == 0) return 0;
-    int64_t blocks = pm::dw_num_blocks(sq, nh);
+    int64_t blocks = pm::dw_plan(sq, nh, nope, pe).partials();
     if (pm::bwd_fused_applies(nh, nope, pe)) {  // postmix_bwd's single pass has its own blocks
-        const int64_t fb = pm::bwd_fused_num_blocks(sq, nh, nope, pe);
+        const int64_t fb = pm::bwd_fused_plan(sq, nh, nope, pe).partials();
         if (fb > blocks) blocks = fb;
     }
     const size_t bytes = (size_t)blocks * nh * nh * sizeof(float);

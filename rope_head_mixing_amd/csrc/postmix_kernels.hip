@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256) void dw_partial_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
     const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe,
-    float* __restrict__ partials) {
+    float* __restrict__ partials, int spans) {
     constexpr int NB = (NHP + 31) / 32;
     constexpr bool SPLIT_TOKENS = NB <= 2;
     constexpr int TG = SPLIT_TOKENS ? NB : 2;
@@ -386,9 +386,14 @@ __global__ __launch_bounds__(256) void dw_partial_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-    // block b of B = gridDim.x: tokens [b*sq/B, (b+1)*sq/B)
-    const int64_t s_begin = (int64_t)blockIdx.x * sq / gridDim.x;
-    const int64_t s_end = ((int64_t)blockIdx.x + 1) * sq / gridDim.x;
+    // token block tb of B = gridDim.x / spans: tokens [tb*sq/B, (tb+1)*sq/B);
+    // k-step span y: [y*ksteps/spans, (y+1)*ksteps/spans) (spans > 1 only
+    // for very wide rows, to bound the accumulation chain)
+    const int64_t nbt = gridDim.x / spans, tb = blockIdx.x / spans;
+    const int y = (int)(blockIdx.x - tb * spans);
+    const int64_t s_begin = tb * sq / nbt;
+    const int64_t s_end = (tb + 1) * sq / nbt;
+    const int t_begin = (int)((int64_t)y * ksteps / spans), t_end = (int)((int64_t)(y + 1) * ksteps / spans);
 
     for (int64_t s = s_begin + (SPLIT_TOKENS ? wave : 0); s < s_end; s += (SPLIT_TOKENS ? 4 : 1)) {
         int64_t prow = 0;
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(256) void dw_partial_kernel(
         const uint16_t* dys = dY + s * nh * (int64_t)d;
         const uint16_t* os = O + s * nh * (int64_t)d;
 
-        for (int t = 0; t < ksteps; ++t) {
+        for (int t = t_begin; t < t_end; ++t) {
             const int grp = 2 * t + half;
             const int c = 8 * grp;
             const bool gvalid = grp < ngroups;
@@ -1065,12 +1070,16 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
     const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe,
-    float* __restrict__ partials, int ptok) {
+    float* __restrict__ partials, int ptok, int spans) {
     // PAD: nh < NH.  A chunk then holds ptok consecutive tokens (ptok*nh
     // consecutive rows of the [sq*nh, d] arrays), the rest of its rows are
     // zero padding (not loaded), and the partial is the sum of the ptok
     // diagonal [nh, nh] blocks of the chunk products; otherwise nh == NH and
     // ptok == 1.
+    // spans: workgroup b covers token block b / spans and channel span
+    // b % spans (its share of each token's 128-channel parts); one partial
+    // per workgroup.  spans > 1 only where a token block's accumulation
+    // chain would otherwise be too long (very wide rows).
     using C = DwCfg<NH, CH>;
     const int tp = PAD ? ptok : 1;
     // cos and sin rows of the chunk's tokens: [tp][pe/2] each
@@ -1089,10 +1098,14 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
     const int gb0 = C::SPLIT_K ? 0 : C::TG * (wave / (C::NB / C::TH));
     const int hb0 = C::SPLIT_K ? 0 : C::TH * (wave % (C::NB / C::TH));
 
-    // block b of B = gridDim.x: tokens [b*sq/B, (b+1)*sq/B)
-    const int64_t s_begin = (int64_t)blockIdx.x * sq / gridDim.x;
-    const int64_t s_end = ((int64_t)blockIdx.x + 1) * sq / gridDim.x;
-    const int nchunks = (int)((s_end - s_begin + tp - 1) / tp) * cpt;
+    // token block tb of B = gridDim.x / spans: tokens [tb*sq/B, (tb+1)*sq/B);
+    // channel span y: parts [y*cpt/spans, (y+1)*cpt/spans)
+    const int64_t nbt = gridDim.x / spans, tb = blockIdx.x / spans;
+    const int y = (int)(blockIdx.x - tb * spans);
+    const int64_t s_begin = tb * sq / nbt;
+    const int64_t s_end = (tb + 1) * sq / nbt;
+    const int p0 = (int)((int64_t)y * cpt / spans), cps = (int)((int64_t)(y + 1) * cpt / spans) - p0;
+    const int nchunks = (int)((s_end - s_begin + tp - 1) / tp) * cps;
 
     f32x16 acc[C::TG][C::TH];
 #pragma unroll
@@ -1105,8 +1118,8 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
     u32x4 v[C::VPT];
     f32x4 cv = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
     auto load_chunk = [&](int k) {
-        const int64_t s = s_begin + (int64_t)(k / cpt) * tp;  // first token of the chunk
-        const int part = k % cpt;
+        const int64_t s = s_begin + (int64_t)(k / cps) * tp;  // first token of the chunk
+        const int part = p0 + k % cps;
         const int ntok = (int)(s_end - s < tp ? s_end - s : tp);
         const int rows_valid = PAD ? ntok * nh : NH;
         const int64_t rowbase = s * nh * (int64_t)d + part * CH;
@@ -1131,7 +1144,7 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
 
     if (nchunks > 0) load_chunk(0);
     for (int k = 0; k < nchunks; ++k) {
-        const int part = k % cpt;
+        const int part = p0 + k % cps;
         __syncthreads();  // every wave is done with the previous chunk
 #pragma unroll
         for (int j = 0; j < C::VPT; ++j) {
@@ -1378,7 +1391,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O, const uint16_t* __restrict__ W,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
     const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe,
-    uint16_t* __restrict__ dO, float* __restrict__ partials, int64_t ngroups, int ptok, int rgt) {
+    uint16_t* __restrict__ dO, float* __restrict__ partials, int64_t ngroups, int ptok, int rgt, int spans) {
     // PAD: nh < NH.  A chunk then holds ptok consecutive tokens (ptok*nh
     // consecutive rows of the [sq*nh, d] arrays; W staged block-diagonally,
     // one copy per token, exactly as in the token-part kernel), the other rows
@@ -1421,12 +1434,19 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     int ph = PAD ? (32 * hb + (lane & 31)) / nh : 0, pr = PAD ? (32 * nb + (lane & 31)) / nh : 0;
     const int ph_off = (ph < tp ? ph : tp - 1) * pe, pr_off = (pr < tp ? pr : tp - 1) * pe;
 
-    // block b of B = gridDim.x holds the token groups (tp tokens each, one
-    // chunk's rows) [b*G/B, (b+1)*G/B) of the G = ngroups groups
-    const int64_t s_begin = (int64_t)blockIdx.x * ngroups / gridDim.x * tp;
-    int64_t s_end = ((int64_t)blockIdx.x + 1) * ngroups / gridDim.x * tp;
+    // token block tb of B = gridDim.x / spans holds the token groups (tp
+    // tokens each, one chunk's rows) [tb*G/B, (tb+1)*G/B) of the G = ngroups
+    // groups; channel span y = b % spans takes the CH-channel parts
+    // [y*cpt/spans, (y+1)*cpt/spans) of each (spans > 1 only for very wide
+    // rows, to bound the weight gradient's accumulation chain).  One partial
+    // per workgroup.
+    const int64_t nbt = gridDim.x / spans, tb = blockIdx.x / spans;
+    const int y = (int)(blockIdx.x - tb * spans);
+    const int64_t s_begin = tb * ngroups / nbt * tp;
+    int64_t s_end = (tb + 1) * ngroups / nbt * tp;
     if (s_end > sq) s_end = sq;
-    const int nchunks = (int)((s_end - s_begin + tp - 1) / tp) * cpt;
+    const int p0 = (int)((int64_t)y * cpt / spans), cps = (int)((int64_t)(y + 1) * cpt / spans) - p0;
+    const int nchunks = (int)((s_end - s_begin + tp - 1) / tp) * cps;
 
     u32x4 v[C::VPT];
     // cos and sin rows of tokens s0 .. s0+rgt-1 (within the block) -> LDS
@@ -1453,7 +1473,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     // head rows of chunk k backed by tokens < s_end
     auto chunk_rows = [&](int k) -> int {
         if (!PAD) return NH;
-        const int64_t left = s_end - (s_begin + (int64_t)(k / cpt) * tp);
+        const int64_t left = s_end - (s_begin + (int64_t)(k / cps) * tp);
         return (int)(left < tp ? left : tp) * nh;
     };
     // The loads are unconditional: padding rows re-read the chunk's last row
@@ -1462,8 +1482,8 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     // for every load in flight (scratch and global loads share one counter),
     // which serialises the prefetch.  In-chunk offsets fit 32 bits (d <= 2^24).
     auto load_chunk = [&](int k) {
-        const int64_t s = s_begin + (int64_t)(k / cpt) * tp;  // first token of the chunk
-        const int part = k % cpt;
+        const int64_t s = s_begin + (int64_t)(k / cps) * tp;  // first token of the chunk
+        const int part = p0 + k % cps;
         const int rows = chunk_rows(k);
         const int64_t rowbase = s * nh * (int64_t)d + part * CH;
         const uint16_t* const dyb = dY + rowbase;
@@ -1555,12 +1575,12 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     }
     __syncthreads();
     for (int k = 0; k < nchunks; ++k) {
-        const int64_t s = s_begin + (int64_t)(k / cpt) * tp;  // first token of the chunk
-        const int part = k % cpt;
+        const int64_t s = s_begin + (int64_t)(k / cps) * tp;  // first token of the chunk
+        const int part = p0 + k % cps;
         const int c_base = part * CH;
         const bool chunk_pe = pe > 0 && c_base + CH > nope;
         // cos/sin rows of the chunk's first token; a row r of the chunk uses those of token r / nh
-        const int tok = (k / cpt) * tp;  // the chunk's first token within the block
+        const int tok = (k / cps) * tp;  // the chunk's first token within the block
         const float* csl = rope_g + ((C::NBUF == 2 ? (tok / rgt) & 1 : 0) * rgt + tok % rgt) * pe;
         const float* snl = csl + (pe >> 1);
         uint16_t* const lol = reinterpret_cast<uint16_t*>(rope_g + C::NBUF * rgt * pe);  // [NH][pe + 8]
@@ -1746,8 +1766,8 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             // the group before this chunk's), ahead of the chunk prefetch, so
             // waiting for the table rows waits for nothing else in flight
             // but chunk k+1, which the staging needs anyway
-            const int tok1 = ((k + 1) / cpt) * tp;
-            if (pe > 0 && (k + 1) % cpt == 0 && tok1 % rgt == 0) load_rope_group(s_begin + tok1, (tok1 / rgt) & 1);
+            const int tok1 = ((k + 1) / cps) * tp;
+            if (pe > 0 && (k + 1) % cps == 0 && tok1 % rgt == 0) load_rope_group(s_begin + tok1, (tok1 / rgt) & 1);
             stage_chunk(k + 1);
             if (k + 2 < nchunks) load_chunk(k + 2);  // in flight during two compute phases
         }
@@ -2168,20 +2188,26 @@ __global__ __launch_bounds__(256) void small_dw_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
     const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe,
-    float* __restrict__ partials) {
+    float* __restrict__ partials, int spans) {
     constexpr int NN = SMALL_NH * SMALL_NH;
     __shared__ float red[NN][256];
     const int d = nope + pe, h2 = pe >> 1, nv = nope >> 3, pv = pe >> 3;
-    const int64_t s0 = (int64_t)blockIdx.x * sq / gridDim.x;
-    const int64_t s1 = ((int64_t)blockIdx.x + 1) * sq / gridDim.x;
-    const int vpr = nv + pv;
+    // token block tb of B = gridDim.x / spans, vector span y of each token's
+    // d/8 vectors (spans > 1 only for very wide rows)
+    const int64_t nbt = gridDim.x / spans, tb = blockIdx.x / spans;
+    const int y = (int)(blockIdx.x - tb * spans);
+    const int64_t s0 = tb * sq / nbt;
+    const int64_t s1 = (tb + 1) * sq / nbt;
+    const int v_all = nv + pv;
+    const int v0 = (int)((int64_t)y * v_all / spans);
+    const int vpr = (int)((int64_t)(y + 1) * v_all / spans) - v0;
     const int64_t n_items = (s1 - s0) * vpr;
     float acc[NN];
 #pragma unroll
     for (int k = 0; k < NN; ++k) acc[k] = 0.0f;
     for (int64_t it = threadIdx.x; it < n_items; it += 256) {
         const int64_t r = it / vpr;
-        const int v = (int)(it - r * vpr);
+        const int v = v0 + (int)(it - r * vpr);
         const int64_t s = s0 + r;
         const bool is_pe = v >= nv;
         const int c = 8 * v;  // nope vectors first, then pe vectors, in channel order
@@ -2422,6 +2448,38 @@ int64_t dw_num_blocks(int64_t sq, int nh) {
     return b;
 }
 
+// Each weight-gradient partial accumulates its products in fp32 chains, one
+// add per MFMA k-step (16 channels of one token); the error of such a chain
+// grows with its length (like 2^-24 * sqrt(length) for random data: one
+// token of 2^24 channels at 128 heads, a chain of 2^20, measured 1.05e-4
+// relative).  No chain is allowed more than kMaxChain k-steps.  A token (or a
+// group of tokens sharing a chunk) adds at most ceil(d/16) k-steps to a
+// chain; blocks whose units would exceed the cap are made smaller, and a
+// single unit that exceeds it is split into channel spans, each with its own
+// partial.  Shapes within the cap (every shape of fewer than 2^14 channels
+// per unit-block product, e.g. the production blocks of 16 or 32 tokens of
+// 512 channels: 512 or 1024 k-steps) keep the plain partition and its bits.
+static constexpr int64_t kMaxChain = (int64_t)1 << 14;
+
+static DwPlan chain_capped(int64_t units, int64_t nb0, int d) {
+    DwPlan p{nb0, 1};
+    if (units <= 0 || nb0 <= 0) return p;
+    const int64_t per_unit = ((int64_t)d + 15) / 16;
+    if ((units + nb0 - 1) / nb0 * per_unit <= kMaxChain) return p;
+    if (per_unit <= kMaxChain) {
+        const int64_t u = kMaxChain / per_unit;  // units per block; even spreading keeps <= u
+        p.blocks = (units + u - 1) / u;
+        return p;
+    }
+    p.blocks = units;
+    p.spans = (int)((per_unit + kMaxChain - 1) / kMaxChain);  // <= d/128: whole 128-channel parts
+    return p;
+}
+
+DwPlan dw_plan(int64_t sq, int nh, int nope, int pe) {
+    return chain_capped(sq, dw_num_blocks(sq, nh), nope + pe);
+}
+
 // chunk width of the fused backward: 256 channels (16 waves) where d allows
 static int bwd_fused_chunk(int d) { return d % 256 == 0 ? 256 : 128; }
 
@@ -2460,7 +2518,7 @@ int bwd_fused_tokens_per_block(int64_t sq, int nh, int nope, int pe) {
 // the device's CU count: the partition, and with it the weight gradient's
 // summation order, depends on the shape only.
 static constexpr int64_t kFusedRound = 256;
-int64_t bwd_fused_num_blocks(int64_t sq, int nh, int nope, int pe) {
+static int64_t bwd_fused_num_blocks(int64_t sq, int nh, int nope, int pe) {
     const int t = bwd_fused_tokens_per_block(sq, nh, nope, pe);
     const int tp = bwd_fused_tokens_per_chunk(nh, nope, pe);
     const int64_t groups = (sq + tp - 1) / tp, per_block = t / tp;
@@ -2473,6 +2531,12 @@ int64_t bwd_fused_num_blocks(int64_t sq, int nh, int nope, int pe) {
         if (b > groups) b = groups < 2 * kFusedRound ? kFusedRound : groups;
     }
     return b;
+}
+
+// The fused backward's plan: units are token groups (one chunk's tokens).
+DwPlan bwd_fused_plan(int64_t sq, int nh, int nope, int pe) {
+    const int tp = bwd_fused_tokens_per_chunk(nh, nope, pe);
+    return chain_capped((sq + tp - 1) / tp, bwd_fused_num_blocks(sq, nh, nope, pe), nope + pe);
 }
 
 // Chunk width of the LDS-staged weight-gradient kernel, or 0 for the direct kernel.
@@ -2502,38 +2566,41 @@ static int dw_tile_heads(int nh, int pe) {
 }
 
 template <int NHC>
-static hipError_t launch_dw_chunk_t(const DwArgs& a, int64_t nb, hipStream_t stream) {
+static hipError_t launch_dw_chunk_t(const DwArgs& a, const DwPlan& pl, hipStream_t stream) {
     const bool pad = a.nh != NHC;
     const int tp = pad ? dw_tokens_per_chunk<NHC>(a.nh, a.pe) : 1;
     auto kern = pad ? dw_chunk_kernel<NHC, 128, true> : dw_chunk_kernel<NHC, 128, false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(DwCfg<NHC, 128>::NT), 0, stream, a.dY, a.O, a.rcos,
-                       a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, a.partials, tp);
+    hipLaunchKernelGGL(kern, dim3((unsigned)pl.partials()), dim3(DwCfg<NHC, 128>::NT), 0, stream, a.dY, a.O,
+                       a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, a.partials, tp,
+                       pl.spans);
     return hipGetLastError();
 }
 
 template <int NHP>
 static hipError_t launch_dw_t(const DwArgs& a, hipStream_t stream) {
-    const int64_t nb = dw_num_blocks(a.sq, a.nh);
+    const DwPlan pl = dw_plan(a.sq, a.nh, a.nope, a.pe);
+    if (pl.partials() > INT32_MAX) return hipErrorInvalidValue;
     const int ch = a.force_general ? 0 : dw_chunk_width(a.nh, a.nope, a.pe);
     if (ch == 128) {
         const int nhc = dw_tile_heads(a.nh, a.pe);
-        const hipError_t e = nhc == 32   ? launch_dw_chunk_t<32>(a, nb, stream)
-                             : nhc == 64 ? launch_dw_chunk_t<64>(a, nb, stream)
-                                         : launch_dw_chunk_t<128>(a, nb, stream);
+        const hipError_t e = nhc == 32   ? launch_dw_chunk_t<32>(a, pl, stream)
+                             : nhc == 64 ? launch_dw_chunk_t<64>(a, pl, stream)
+                                         : launch_dw_chunk_t<128>(a, pl, stream);
         if (e != hipSuccess) return e;
     } else if (!a.force_general && a.nh <= SMALL_NH) {
-        hipLaunchKernelGGL(small_dw_kernel, dim3((unsigned)nb), dim3(256), 0, stream, a.dY, a.O, a.rcos,
-                           a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, a.partials);
+        hipLaunchKernelGGL(small_dw_kernel, dim3((unsigned)pl.partials()), dim3(256), 0, stream, a.dY, a.O,
+                           a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, a.partials,
+                           pl.spans);
     } else {
-        hipLaunchKernelGGL((dw_partial_kernel<NHP>), dim3((unsigned)nb), dim3(256), 0, stream, a.dY,
-                           a.O, a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe,
-                           a.partials);
+        hipLaunchKernelGGL((dw_partial_kernel<NHP>), dim3((unsigned)pl.partials()), dim3(256), 0, stream,
+                           a.dY, a.O, a.rcos, a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe,
+                           a.partials, pl.spans);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t ne = (int64_t)a.nh * a.nh;
     hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((ne + 63) / 64)), dim3(1024), 0, stream,
-                       a.partials, nb, ne, a.dW);
+                       a.partials, pl.partials(), ne, a.dW);
     return hipGetLastError();
 }
 
@@ -2559,8 +2626,8 @@ bool bwd_fused_applies(int nh, int nope, int pe) {
 }
 
 template <int NH, int CH, int WAVES>
-static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int64_t ngroups, int64_t nb, int tp,
-                                     hipStream_t stream) {
+static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int64_t ngroups, const DwPlan& pl,
+                                     int tp, hipStream_t stream) {
     using C = BwdCfg<NH, CH, WAVES>;
     const bool pad = a.nh != NH;
     const int rgt = C::rope_group(tp);
@@ -2583,25 +2650,27 @@ static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int64_t
     if (ae != hipSuccess) return ae;
     const size_t lds = C::lds_bytes(a.nope, a.pe, rgt, ps);
     if (lds > kMaxLds) return hipErrorInvalidValue;  // excluded by bwd_fused_applies
-    hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), lds, stream, a.dY, a.O, mx.W, a.rcos, a.rsin,
-                       a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, mx.Out, a.partials, ngroups, tp, rgt);
+    hipLaunchKernelGGL(kern, dim3((unsigned)pl.partials()), dim3(C::NT), lds, stream, a.dY, a.O, mx.W, a.rcos,
+                       a.rsin, a.table_rows, a.positions, a.sq, a.nh, a.nope, a.pe, mx.Out, a.partials, ngroups, tp,
+                       rgt, pl.spans);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_fused(const MixArgs& mx, const DwArgs& a, hipStream_t stream) {
-    const int64_t nb = bwd_fused_num_blocks(a.sq, a.nh, a.nope, a.pe);
+    const DwPlan pl = bwd_fused_plan(a.sq, a.nh, a.nope, a.pe);
+    if (pl.partials() > INT32_MAX) return hipErrorInvalidValue;
     const int tp = bwd_fused_tokens_per_chunk(a.nh, a.nope, a.pe);
     const int64_t ngroups = (a.sq + tp - 1) / tp;
     hipError_t err;
     if (a.nh > 64)
-        err = launch_bwd_fused_t<128, 128, 16>(mx, a, ngroups, nb, 1, stream);
+        err = launch_bwd_fused_t<128, 128, 16>(mx, a, ngroups, pl, 1, stream);
     else
-        err = bwd_fused_chunk(a.nope + a.pe) == 256 ? launch_bwd_fused_t<64, 256, 16>(mx, a, ngroups, nb, tp, stream)
-                                                    : launch_bwd_fused_t<64, 128, 8>(mx, a, ngroups, nb, tp, stream);
+        err = bwd_fused_chunk(a.nope + a.pe) == 256 ? launch_bwd_fused_t<64, 256, 16>(mx, a, ngroups, pl, tp, stream)
+                                                    : launch_bwd_fused_t<64, 128, 8>(mx, a, ngroups, pl, tp, stream);
     if (err != hipSuccess) return err;
     const int64_t ne = (int64_t)a.nh * a.nh;
     hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((ne + 63) / 64)), dim3(1024), 0, stream,
-                       a.partials, nb, ne, a.dW);
+                       a.partials, pl.partials(), ne, a.dW);
     return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ struct DwArgs {
     int64_t sq;
     int nh, nope, pe;
     float* dW;
-    float* partials;        // [blocks, nh, nh] fp32 workspace (dw_num_blocks or bwd_fused_num_blocks)
+    float* partials;        // [partials, nh, nh] fp32 workspace (dw_plan or bwd_fused_plan)
     bool force_general;     // use the direct-load kernel for every shape
 };
 
@@ -47,12 +47,20 @@ hipError_t launch_rope_apply(const uint16_t* X, const float* rcos, const float* 
 hipError_t launch_rope_table(double theta, int pe, int64_t rows, float* cos_out, float* sin_out,
                              int n_cu, hipStream_t stream);
 
-// Token blocking of the weight gradient: a function of the shape only, so the
-// summation order (and therefore every bit of dW) does not depend on the GPU.
+// Partition of the weight gradient into partials: token blocks, each split
+// into `spans` channel spans (1 unless the accumulation chain of a block would
+// be too long).  A function of the shape only, so the summation order (and
+// therefore every bit of dW) does not depend on the GPU.
+struct DwPlan {
+    int64_t blocks;
+    int spans;
+    int64_t partials() const { return blocks * spans; }
+};
 int dw_tokens_per_block(int64_t sq, int nh);
 int64_t dw_num_blocks(int64_t sq, int nh);
+DwPlan dw_plan(int64_t sq, int nh, int nope, int pe);         // postmix_bwd_dw
+DwPlan bwd_fused_plan(int64_t sq, int nh, int nope, int pe);  // postmix_bwd's single pass
 int bwd_fused_tokens_per_block(int64_t sq, int nh, int nope, int pe);
-int64_t bwd_fused_num_blocks(int64_t sq, int nh, int nope, int pe);
 int dw_chunk_width(int nh, int nope, int pe);
 
 // Fused backward: dx (into mx.Out) and the dW partials from one pass over dY

@@ -9,10 +9,17 @@ from rope_head_mixing_amd import synthetic
 # Tolerances (stated once, used by every parity test):
 #   bf16 outputs Y and dO: |gpu - ref| <= 1e-2 * |ref| + 1e-3, element-wise,
 #       against the unrounded fp64 oracle value;
-#   fp32 dW: ||gpu - ref||_F / ||ref||_F <= 1e-4, and every element within
-#       1e-4 * max|ref|.
+#   fp32 dW: ||gpu - ref||_F <= 1e-4 * ||ref||_F + u * ||A||_F, and every
+#       element |gpu - ref| <= 1e-4 * max|ref| + u * A[g,h], where
+#       A[g,h] = sum |dY[s,g,c] * inv_rope(O)[s,h,c]| (oracle.bwd_dw_abs) and
+#       u = 2^-24.  The u * A term is one fp32 rounding at the largest
+#       magnitude a partial sum of the entry's terms can reach: it admits
+#       entries that cancel to far below their terms (a single head's sum can
+#       cancel to 6e-5 of them), and is negligible beside 1e-4 * max|ref| for
+#       entries that do not.  Without A the bound is the relative one alone.
 Y_RTOL, Y_ATOL = 1e-2, 1e-3
 DW_REL = 1e-4
+U32 = 2.0 ** -24
 
 
 def has_gfx950() -> bool:
@@ -60,13 +67,45 @@ def check_bf16(gpu_bits: np.ndarray, ref: np.ndarray, label: str) -> float:
     return worst
 
 
-def check_dw(gpu: np.ndarray, ref: np.ndarray, label: str) -> float:
+def check_dw(gpu: np.ndarray, ref: np.ndarray, label: str, mag: np.ndarray | None = None) -> float:
+    """Norm-wise and element-wise dW bound (above); returns ||gpu - ref||_F / ||ref||_F."""
     gpu = np.asarray(gpu, np.float64)
-    num = float(np.linalg.norm(gpu - ref))
+    assert gpu.shape == ref.shape, (label, gpu.shape, ref.shape)
+    err = np.abs(gpu - ref)
+    num = float(np.linalg.norm(err))
     den = float(np.linalg.norm(ref))
     rel = num / den if den > 0 else num
-    assert rel <= DW_REL, f"{label}: ||dW - ref||_F / ||ref||_F = {rel:.3e} > {DW_REL}"
+    cond = 0.0 if mag is None else U32 * float(np.linalg.norm(mag))
+    assert num <= DW_REL * den + cond, (f"{label}: ||dW - ref||_F = {num:.3e} > 1e-4 * {den:.3e}"
+                                         f" + u * ||A||_F = {DW_REL * den + cond:.3e}")
     scale = float(np.abs(ref).max()) if ref.size else 0.0
-    worst = float(np.abs(gpu - ref).max()) if ref.size else 0.0
-    assert worst <= DW_REL * max(scale, 1e-30), f"{label}: max |dW - ref| = {worst:.3e}"
+    bound = DW_REL * max(scale, 1e-30) + (0.0 if mag is None else U32 * np.asarray(mag, np.float64))
+    bad = err > bound
+    if np.any(bad):
+        i = np.unravel_index(int(np.argmax(err - bound)), err.shape)
+        raise AssertionError(f"{label}: {int(bad.sum())} dW entries out of bound; worst at {i}: "
+                             f"gpu={gpu[i]!r} ref={ref[i]!r} bound={np.broadcast_to(bound, err.shape)[i]:.3e}")
     return rel
+
+
+def dw_refs(dY, O, pos, theta, nope, pe):
+    """(dW, A): the oracle's weight gradient and its terms' magnitude sums."""
+    import oracle
+    return (oracle.bwd_dw(dY, O, pos, theta, nope, pe),
+            oracle.bwd_dw_abs(dY, O, pos, theta, nope, pe))
+
+
+def check_bf16_streamed(gpu_bits: np.ndarray, ref_fn, label: str, chunk: int = 512,
+                        progress_every: int = 8) -> float:
+    """Element-wise bf16 bound over a whole [sq, nh, d] output, the fp64
+    reference computed `chunk` tokens at a time by ref_fn(s0, s1) (so no fp64
+    copy of the whole tensor is held).  Returns the worst |err| / bound."""
+    sq = gpu_bits.shape[0]
+    worst = 0.0
+    n_chunks = (sq + chunk - 1) // chunk
+    for j, s0 in enumerate(range(0, sq, chunk)):
+        s1 = min(sq, s0 + chunk)
+        worst = max(worst, check_bf16(gpu_bits[s0:s1], ref_fn(s0, s1), f"{label} tokens {s0}..{s1 - 1}"))
+        if progress_every and (j + 1) % progress_every == 0:
+            print(f"    {label}: {j + 1}/{n_chunks} chunks, worst err/bound {worst:.3f}", flush=True)
+    return worst

@@ -217,6 +217,18 @@ def test_workspace_size_is_a_function_of_the_shape():
     # the weight-gradient kernels round the same way above 64 heads (one
     # workgroup per CU): 304 blocks of 36 tokens -> 256; not fused (pe = 80)
     assert L.postmix_bwd_dw_workspace_bytes(10923, 96, 432, 80) == 256 * 96 * 96 * 4
+    # accumulation chains capped at 2^14 k-steps of 16 channels: one token of
+    # 2^24 channels (2^20 k-steps) is split into 64 channel spans, each with
+    # its own partial; two such tokens make 2 x 64
+    assert L.postmix_bwd_dw_workspace_bytes(1, 128, (1 << 24) - 64, 64) == 64 * 128 * 128 * 4
+    assert L.postmix_bwd_dw_workspace_bytes(2, 128, (1 << 24) - 64, 64) == 128 * 128 * 128 * 4
+    assert L.postmix_bwd_dw_workspace_bytes(1, 128, (1 << 24) - 72, 64) == 64 * 128 * 128 * 4
+    # 2^20 channels: 2^16 k-steps per token -> 4 spans per token
+    assert L.postmix_bwd_dw_workspace_bytes(8, 64, (1 << 20) - 64, 64) == 32 * 64 * 64 * 4
+    # 4096 channels (256 k-steps per token): the weight-gradient blocks of 256
+    # tokens (65536 k-steps) and the single pass's blocks of 128 both become
+    # blocks of 64 tokens (16384 k-steps): 2048 partials
+    assert L.postmix_bwd_dw_workspace_bytes(131072, 64, 4032, 64) == 2048 * 64 * 64 * 4
     assert L.postmix_bwd_dw_workspace_bytes(0, 64, 448, 64) == 0
     assert L.postmix_bwd_dw_workspace_bytes(16, 0, 448, 64) == 0
     for args in [(64, 4, 48, 16), (8192, 3, 448, 64), (7, 5, 8, 16)]:

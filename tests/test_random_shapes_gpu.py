@@ -2,17 +2,16 @@
 fp64 oracle.
 
 The hand-picked cases of test_parity_gpu.py aim at one route each; this sweep
-draws head counts from 2 to 128 (padded rows, several tokens per tile, 96- and
+draws head counts from 1 to 128 (padded rows, several tokens per tile, 96- and
 128-row tiles), channel splits with and without d a multiple of 128 (tiled and
 general kernels), pe from 0 to 256 and short ragged token counts, and eight
 more with 1100 to 4000 tokens, where the token blocks are rounded to whole
 rounds and spread evenly.  Each shape
 runs the forward, dx, dW and the single-call backward, each checked against
 the oracle, and the single-call dO must equal postmix_bwd_dx's bit for bit.
-
-nh = 1 is left to its own cases: a single dW entry can cancel to far below
-the sum of its terms' magnitudes, where no fp32 accumulation meets a relative
-tolerance (see the near-cancelled case in test_parity_gpu.py).
+Head counts start at one: a single dW entry may cancel to far below the sum
+of its terms' magnitudes, which the dW bound's u * A term (tests/gpu_util.py)
+accounts for.
 """
 import numpy as np
 import pytest
@@ -30,7 +29,7 @@ def _shapes(n: int, seed: int = 20261202):
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
-        nh = int(rng.integers(2, 129))
+        nh = int(rng.integers(1, 129))
         if rng.random() < 0.6:  # d a multiple of 128: the tiled kernels
             d = int(rng.choice([128, 256, 384, 512, 640]))
             pe = 16 * int(rng.integers(0, min(d, 256) // 16 + 1))
@@ -57,11 +56,11 @@ def test_random_shape(sq, nh, nope, pe, off):
     dO_dx = gu.host_bits(dv.dx())
     ref_dO = oracle.bwd_dx(dv.dY, dv.W, dv.pos, c.theta, nope, pe)
     gu.check_bf16(dO_dx, ref_dO, f"{c.name} dO")
-    ref_dW = oracle.bwd_dw(dv.dY, dv.O, dv.pos, c.theta, nope, pe)
-    gu.check_dw(dv.dw().cpu().numpy(), ref_dW, f"{c.name} dW")
+    ref_dW, mag = gu.dw_refs(dv.dY, dv.O, dv.pos, c.theta, nope, pe)
+    gu.check_dw(dv.dw().cpu().numpy(), ref_dW, f"{c.name} dW", mag)
     dO, dW = dv.bwd()
     np.testing.assert_array_equal(gu.host_bits(dO), dO_dx)
-    gu.check_dw(dW.cpu().numpy(), ref_dW, f"{c.name} bwd dW")
+    gu.check_dw(dW.cpu().numpy(), ref_dW, f"{c.name} bwd dW", mag)
 
 
 def _large_shapes(n: int, seed: int = 20261203):
@@ -72,7 +71,7 @@ def _large_shapes(n: int, seed: int = 20261203):
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
-        nh = int(rng.integers(2, 129))
+        nh = int(rng.integers(1, 129))
         d = int(rng.choice([128, 256]))
         pe = int(rng.choice([0, 32, 64]))
         sq = int(rng.integers(1100, 1700)) if nh > 32 else int(rng.integers(2100, 4000))

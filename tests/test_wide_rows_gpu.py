@@ -9,14 +9,12 @@ checked against the oracle at sampled elements (every head row's pe channels
 among them), dW at sampled entries; the fused backward's dO is bitwise the
 separate dx's, and its dW is checked the same way.
 
-dW tolerance.  Each block accumulates its dW partial in one fp32 chain per
-element, one MFMA k-step (16 channels) at a time; here one block holds the
-one token, so a chain is n = d / 16 = 2^20 k-steps long.  Over random-sign
-terms the norm-wise relative error of such a chain grows like u * sqrt(n)
-(u = 2^-24, 6.1e-5 at n = 2^20), above the 1e-4 bar that production chains
-(about 2^10 k-steps) meet with wide margin; the test holds the norm-wise dW
-error to 4 u sqrt(n) and reports the largest entry error.  Measured: 7.7e-5
-(tiled and fused) and 1.05e-4 (general) norm-wise.
+dW.  A partial's fp32 accumulation chain is capped at 2^14 MFMA k-steps
+(16 channels each): the one token's 2^20 k-steps are split into 64 channel
+spans, each with its own partial, which the fixed-order reduction adds.
+Before the cap this case measured 1.05e-4 norm-wise (general kernel), above
+the 1e-4 bar; the sampled entries are now held to the bar norm-wise and
+each within 1e-4 of the largest sampled |entry|.
 """
 import numpy as np
 import pytest
@@ -74,11 +72,10 @@ def test_widest_rows_at_128_heads(nope, pe):
 
     widx = np.concatenate([[0, nh * nh - 1, 127, 127 * nh], rng.integers(0, nh * nh, 28)])
     ref = oracle.bwd_dw_at(dY_h, O_h, pos_h, THETA, nope, pe, widx)
-    tol = max(gu.DW_REL, 4 * 2.0 ** -24 * np.sqrt(d / 16))
     for label, m in (("dW", dW), ("fused dW", dW_f)):
         got = m.reshape(-1)[widx].astype(np.float64)
         rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
         worst = float(np.abs(got - ref).max() / np.abs(ref).max())
-        print(f"[case] {label}: sampled rel {rel:.3e}, max abs err / max abs {worst:.3e} (tol {tol:.2e})",
-              flush=True)
-        assert rel <= tol, f"{label} sampled rel {rel:.3e}"  # the bar is norm-wise; the max is reported
+        print(f"[case] {label}: sampled rel {rel:.3e}, max abs err / max abs {worst:.3e}", flush=True)
+        assert rel <= gu.DW_REL, f"{label} sampled rel {rel:.3e}"
+        assert worst <= gu.DW_REL, f"{label} max |err| / max |ref| {worst:.3e}"
