@@ -169,6 +169,30 @@ int postmix_bwd(const pm_bf16 *dY, const pm_bf16 *O, const pm_bf16 *W,
                 size_t workspace_bytes, void *stream);
 
 /*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * postmix_bwd without the workspace argument: the same computation, kernels
+ * and partition (dO and dW are bitwise postmix_bwd's), with the weight-
+ * gradient partials in a static device array of the library instead of a
+ * caller workspace.  Allocates, frees and synchronises nothing.
+ *   - The array is 32 MiB on each GPU the library runs on, held until the
+ *     process ends (the production shape needs 16 MiB, 128 heads at 8192 or
+ *     16384 tokens 32 MiB).  A shape whose partials need more
+ *     (postmix_bwd_dw_workspace_bytes > 32 MiB) is rejected with
+ *     PM_ERR_WORKSPACE before any device call; use postmix_bwd there.
+ *   - Every call on one GPU uses that GPU's array: calls that overlap on one
+ *     GPU (several streams, or several host threads) race and must be
+ *     serialised by the caller.  Each call overwrites every partial it reads,
+ *     so nothing carries over between calls.
+ *   Other arguments, errors and limits as postmix_bwd.
+ */
+int postmix_bwd_noalloc(const pm_bf16 *dY, const pm_bf16 *O, const pm_bf16 *W,
+                        const float *rope_cos, const float *rope_sin,
+                        int64_t table_rows, const int32_t *positions, int64_t sq,
+                        int32_t nh, int32_t nope, int32_t pe, pm_bf16 *dO,
+                        float *dW, void *stream);
+
+/*
  * RoPE tables from theta: row r (position r), column i < pe/2:
  *   cos_out[r, i] = cos(r * theta^(-2i/pe)),  sin_out likewise,
  * with the angle formed and evaluated in fp64, then rounded to fp32.

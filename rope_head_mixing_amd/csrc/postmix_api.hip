@@ -276,18 +276,53 @@ int postmix_bwd_dw(const pm_bf16* dY, const pm_bf16* O, const float* rope_cos,
     return ok();
 }
 
-int postmix_bwd(const pm_bf16* dY, const pm_bf16* O, const pm_bf16* W, const float* rope_cos,
-                const float* rope_sin, int64_t table_rows, const int32_t* positions, int64_t sq,
-                int32_t nh, int32_t nope, int32_t pe, pm_bf16* dO, float* dW, void* workspace,
-                size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// ---- the static scratch of postmix_bwd_noalloc -------------------------------
+// A file-scope device array: each GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address is looked up once per device (with
+// that device current) by hipGetSymbolAddress, and only that address is
+// passed to kernels.
+static constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (looked up on the first call on that device).
+int scratch_for_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PM_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(PM_ERR_DEVICE, "device index %d out of range", dev);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(PM_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return PM_OK;
+}
+
+// postmix_bwd, with the partials either in the caller's workspace or
+// (use_scratch) in the library's static scratch.
+int bwd_common(const pm_bf16* dY, const pm_bf16* O, const pm_bf16* W, const float* rope_cos,
+               const float* rope_sin, int64_t table_rows, const int32_t* positions, int64_t sq,
+               int32_t nh, int32_t nope, int32_t pe, pm_bf16* dO, float* dW, void* workspace,
+               size_t workspace_bytes, void* stream, bool use_scratch) {
     int rc = check_shape(sq, nh, nope, pe);
     if (rc) return rc;
     if (!dW) return fail(PM_ERR_NULL, "dW is NULL");
     if (((uintptr_t)dW & 3u) != 0) return fail(PM_ERR_ALIGN, "dW is not 4-byte aligned");
     if (sq == 0) {
-        // no tokens: dO is empty and dW is an empty sum
+        // no tokens: dO is empty and dW is an empty sum (no partials)
         return postmix_bwd_dw(dY, O, rope_cos, rope_sin, table_rows, positions, sq, nh, nope, pe, dW,
-                              workspace, workspace_bytes, stream);
+                              nullptr, 0, stream);
     }
     if (!dY) return fail(PM_ERR_NULL, "dY is NULL");
     if (!O) return fail(PM_ERR_NULL, "O is NULL");
@@ -300,14 +335,22 @@ int postmix_bwd(const pm_bf16* dY, const pm_bf16* O, const pm_bf16* W, const flo
     if (!aligned16(dO)) return fail(PM_ERR_ALIGN, "dO is not 16-byte aligned");
     if (((uintptr_t)W & 1u) != 0) return fail(PM_ERR_ALIGN, "W is not 2-byte aligned");
     const size_t need = postmix_bwd_dw_workspace_bytes(sq, nh, nope, pe);
-    if (need > 0 && !workspace) return fail(PM_ERR_NULL, "workspace is NULL (%zu bytes needed)", need);
-    if (workspace_bytes < need)
-        return fail(PM_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
-    if (!aligned16(workspace)) return fail(PM_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (use_scratch) {
+        if (need > kScratchBytes)
+            return fail(PM_ERR_WORKSPACE,
+                        "the weight-gradient partials of this shape need %zu bytes, more than the %zu "
+                        "bytes of postmix_bwd_noalloc's static scratch; call postmix_bwd with a workspace",
+                        need, kScratchBytes);
+    } else {
+        if (need > 0 && !workspace) return fail(PM_ERR_NULL, "workspace is NULL (%zu bytes needed)", need);
+        if (workspace_bytes < need)
+            return fail(PM_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+        if (!aligned16(workspace)) return fail(PM_ERR_ALIGN, "workspace is not 16-byte aligned");
+    }
     const size_t act = (size_t)sq * nh * (nope + pe) * sizeof(pm_bf16);
     const size_t tab = pe ? (size_t)table_rows * (pe / 2) * sizeof(float) : 0;
     const Range outs[3] = {{"dO", dO, act}, {"dW", dW, (size_t)nh * nh * sizeof(float)},
-                           {"workspace", workspace, need}};
+                           {"workspace", use_scratch ? nullptr : workspace, need}};
     const Range ins[6] = {{"dY", dY, act},
                           {"O", O, act},
                           {"W", W, (size_t)nh * nh * sizeof(pm_bf16)},
@@ -319,6 +362,10 @@ int postmix_bwd(const pm_bf16* dY, const pm_bf16* O, const pm_bf16* W, const flo
     int n_cu = 0;
     rc = check_device(&n_cu);
     if (rc) return rc;
+    if (use_scratch) {
+        rc = scratch_for_current_device(&workspace);
+        if (rc) return rc;
+    }
     pm::MixArgs mx;
     mx.X = dY;
     mx.W = W;
@@ -361,6 +408,25 @@ int postmix_bwd(const pm_bf16* dY, const pm_bf16* O, const pm_bf16* W, const flo
     }
     if (e != hipSuccess) return fail(PM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int postmix_bwd(const pm_bf16* dY, const pm_bf16* O, const pm_bf16* W, const float* rope_cos,
+                const float* rope_sin, int64_t table_rows, const int32_t* positions, int64_t sq,
+                int32_t nh, int32_t nope, int32_t pe, pm_bf16* dO, float* dW, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    return bwd_common(dY, O, W, rope_cos, rope_sin, table_rows, positions, sq, nh, nope, pe, dO, dW,
+                      workspace, workspace_bytes, stream, false);
+}
+
+int postmix_bwd_noalloc(const pm_bf16* dY, const pm_bf16* O, const pm_bf16* W, const float* rope_cos,
+                        const float* rope_sin, int64_t table_rows, const int32_t* positions, int64_t sq,
+                        int32_t nh, int32_t nope, int32_t pe, pm_bf16* dO, float* dW, void* stream) {
+    return bwd_common(dY, O, W, rope_cos, rope_sin, table_rows, positions, sq, nh, nope, pe, dO, dW,
+                      nullptr, 0, stream, true);
 }
 
 int postmix_rope_apply(const pm_bf16* X, const float* rope_cos, const float* rope_sin,

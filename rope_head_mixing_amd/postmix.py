@@ -11,6 +11,7 @@ Entry points keep the C names:
     postmix_bwd_dw(dY, O, rope_cos, rope_sin, positions, nope, pe, out=None, workspace=None)
     postmix_bwd_dw_workspace_bytes(sq, nh, nope, pe)
     postmix_bwd(dY, O, W, rope_cos, rope_sin, positions, nope, pe, ...)  -> (dO, dW)
+    postmix_bwd_noalloc(dY, O, W, rope_cos, rope_sin, positions, nope, pe, out_dO, out_dW)
     postmix_rope_table(theta, pe, table_rows, device=None)
     postmix_kv_index_remap(idx, sq, seqlen_kv, pad_value=-1, out=None)
     postmix_rope_apply(X, rope_cos, rope_sin, positions, nope, pe, direction, out=None)
@@ -68,6 +69,8 @@ def lib():
     L.postmix_bwd_dw.restype = ctypes.c_int
     L.postmix_bwd.argtypes = [P, P, P, P, P, I64, P, I64, I32, I32, I32, P, P, P, SZ, P]
     L.postmix_bwd.restype = ctypes.c_int
+    L.postmix_bwd_noalloc.argtypes = [P, P, P, P, P, I64, P, I64, I32, I32, I32, P, P, P]
+    L.postmix_bwd_noalloc.restype = ctypes.c_int
     L.postmix_rope_apply.argtypes = [P, P, P, I64, P, I64, I32, I32, I32, I32, P, P]
     L.postmix_rope_apply.restype = ctypes.c_int
     L.postmix_kv_index_remap.argtypes = [P, I64, I64, I64, I64, I32, P, P]
@@ -289,6 +292,31 @@ def postmix_bwd(dY, O, W, rope_cos, rope_sin, positions, nope: int, pe: int, out
         _check(lib().postmix_bwd(dY.data_ptr(), O.data_ptr(), W.data_ptr(), c, s, rows, p, sq, nh,
                                  nope, pe, dO.data_ptr(), dW.data_ptr(), workspace.data_ptr(),
                                  ws_bytes, _stream_handle(dev)))
+    return dO, dW
+
+
+def postmix_bwd_noalloc(dY, O, W, rope_cos, rope_sin, positions, nope: int, pe: int, out_dO=None,
+                        out_dW=None):
+    """postmix_bwd with the library's static scratch instead of a workspace
+    (the C entry point allocates nothing; outputs not given are allocated
+    here, by torch)."""
+    torch = _torch()
+    sq, nh = _act_dims(dY, "dY", nope, pe)
+    d = nope + pe
+    specs = [_Spec(dY, "dY", torch.bfloat16, (sq, nh, d)), _Spec(O, "O", torch.bfloat16, (sq, nh, d)),
+             _Spec(W, "W", torch.bfloat16, (nh, nh)),
+             *_rope_specs(rope_cos, rope_sin, positions, pe, sq)]
+    if out_dO is not None:
+        specs.append(_Spec(out_dO, "out_dO", torch.bfloat16, (sq, nh, d)))
+    if out_dW is not None:
+        specs.append(_Spec(out_dW, "out_dW", torch.float32, (nh, nh)))
+    dev = _validate(*specs)
+    c, s, rows, p = _rope_ptrs(rope_cos, rope_sin, positions, pe)
+    dO = torch.empty_like(dY) if out_dO is None else out_dO
+    dW = torch.empty((nh, nh), dtype=torch.float32, device=dev) if out_dW is None else out_dW
+    with _on_device(dev):
+        _check(lib().postmix_bwd_noalloc(dY.data_ptr(), O.data_ptr(), W.data_ptr(), c, s, rows, p, sq, nh,
+                                         nope, pe, dO.data_ptr(), dW.data_ptr(), _stream_handle(dev)))
     return dO, dW
 
 

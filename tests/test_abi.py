@@ -368,6 +368,49 @@ def test_fused_backward_argument_errors(kw, code, word):
     assert word in msg
 
 
+def bwd_noalloc(**kw):
+    sq, nh, nope, pe = kw.get("sq", 16), kw.get("nh", 64), kw.get("nope", 448), kw.get("pe", 64)
+    args = dict(dY=A, O=B, W=0x200000000, cos=C, sin=D, rows=32768, pos=E, sq=sq, nh=nh, nope=nope,
+                pe=pe, dO=F, dW=0x240000000)
+    args.update(kw)
+    L = pm.lib()
+    rc = L.postmix_bwd_noalloc(args["dY"], args["O"], args["W"], args["cos"], args["sin"], args["rows"],
+                               args["pos"], args["sq"], args["nh"], args["nope"], args["pe"], args["dO"],
+                               args["dW"], None)
+    return rc, L.postmix_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(dW=0), pm.PM_ERR_NULL, "dW"),
+    (dict(dO=0), pm.PM_ERR_NULL, "dO"),
+    (dict(W=0x200000000 + 1), pm.PM_ERR_ALIGN, "W"),
+    (dict(dO=A + 1024), pm.PM_ERR_OVERLAP, "dO"),
+    (dict(nh=129), pm.PM_ERR_SHAPE, "nh"),
+    # 2^20 tokens at 64 heads: 2048 partials of 16 KiB, 32 MiB, fit exactly;
+    # 2^21 tokens need 4096 (64 MiB), more than the static scratch
+    (dict(sq=1 << 21), pm.PM_ERR_WORKSPACE, "static scratch"),
+    # 16 tokens of 2^24 channels at 128 heads: 16 x 64 spans of 64 KiB
+    (dict(sq=16, nh=128, nope=(1 << 24) - 64), pm.PM_ERR_WORKSPACE, "static scratch"),
+])
+def test_noalloc_backward_argument_errors(kw, code, word):
+    """The no-allocation backward validates like postmix_bwd, and rejects
+    shapes whose partials exceed its 32 MiB static scratch before any device
+    call."""
+    rc, msg = bwd_noalloc(**kw)
+    assert rc == code, msg
+    assert word in msg
+
+
+def test_noalloc_scratch_covers_the_workloads():
+    """The production and sweep shapes fit the 32 MiB static scratch."""
+    L = pm.lib()
+    for args in [(16384, 64, 448, 64), (8192, 128, 448, 64), (16384, 128, 448, 64), (8192, 3, 448, 64),
+                 (1024, 64, 448, 64), (64, 4, 48, 16), (1 << 20, 64, 448, 64),
+                 (4, 128, (1 << 24) - 64, 64)]:
+        assert L.postmix_bwd_dw_workspace_bytes(*args) <= 32 << 20, args
+    assert L.postmix_bwd_dw_workspace_bytes(1 << 21, 64, 448, 64) > 32 << 20
+
+
 def remap(**kw):
     args = dict(idx=A, rows=8, sq=4, topk=16, seqlen_kv=1000, pad=-1, out=F)
     args.update(kw)
