@@ -25,25 +25,28 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every HIP source and link libpostmix.so next to this file."""
+def build(verbose: bool = False, extra_flags=None, out: str | None = None, link_flags=None) -> str:
+    """Compile every HIP source and link libpostmix.so next to this file (or
+    at `out`, e.g. a checker build with extra host flags)."""
+    lib = LIB if out is None else out
+    objdir = CSRC if out is None else os.path.dirname(os.path.abspath(out))
     objs = []
     for src in SOURCES:
-        obj = os.path.join(CSRC, src.replace(".hip", ".o"))
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
         cmd = [HIPCC, *FLAGS, *(extra_flags or []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.check_call(cmd)
         objs.append(obj)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *(link_flags or []), "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     for obj in objs:
         os.remove(obj)
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":
