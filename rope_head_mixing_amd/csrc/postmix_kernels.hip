@@ -1347,8 +1347,16 @@ struct BwdCfg {
     // fragments), in one shared array.  Against one dW tile and one dx block
     // on every wave with W read from LDS per use, the compute phase reads
     // ~40% less LDS.  Only pe rotated in registers.
-    static constexpr bool SPLIT = NH == 128;
+    // 64 rows on 16 waves split the same way: waves 0 .. 7 each own the two
+    // tiles of one h-block (g-blocks 0 and 1) over one of four k-sets, so one
+    // O fragment (and one rotated pe operand) serves two MFMAs; waves 8 .. 15
+    // each own one dx M-block for both N-blocks, so its transposed dY
+    // fragments are read once for two MFMAs.  Against a tile and a dx block on
+    // every wave, the compute phase reads a third less LDS per chunk.
+    static constexpr bool SPLIT = NH == 128 || (NH == 64 && WAVES == 16);
     static constexpr int NB = NH / 32, KB = NH / 16;
+    // SPLIT: k-sets of the dW waves (1 at 128 rows: each tile is one wave's)
+    static constexpr int DW_KSETS = SPLIT ? (WAVES / 2) / (NB * NB / 2) : 1;
     static constexpr int PITCH = CH + 8;
     static constexpr int WPITCH = NH + 8;
     static constexpr int VPR = CH / 8;
@@ -1422,17 +1430,25 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     // derived indices (tile, k-set, blocks), which otherwise spill
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile = wave % C::NTILE, kset = wave / C::NTILE;
-    // SPLIT: dw_role waves own dW tiles (gb, hb), (gb + 1, hb); the others
-    // dx M-blocks mb, mb + 1 of N-block nb
+    // SPLIT: dw_role waves own dW tiles (gb, hb), (gb + 1, hb) over k-set
+    // dkset; the others dx M-blocks mb, mb + 1 of N-block nb (128 rows) or
+    // M-block mb of both N-blocks (64 rows)
     const bool dw_role = !C::SPLIT || wave < WAVES / 2;
     const int vs = wave % (WAVES / 2);
-    const int gb = C::SPLIT ? 2 * (vs / C::NB) : tile / C::NB, hb = C::SPLIT ? vs % C::NB : tile % C::NB;
-    const int mb = C::SPLIT ? 2 * (vs / C::NB) : wave % C::MBC, nb = C::SPLIT ? vs % C::NB : wave / C::MBC;
+    const int gb = C::SPLIT ? 2 * ((vs / C::NB) % (C::NB / 2)) : tile / C::NB;
+    const int hb = C::SPLIT ? vs % C::NB : tile % C::NB;
+    const int dkset = C::SPLIT ? vs / (C::NB * (C::NB / 2)) : 0;
+    const int mb = C::SPLIT ? (C::NB == 2 ? vs : 2 * (vs / C::NB)) : wave % C::MBC;
+    const int nb = C::SPLIT ? (C::NB == 2 ? 0 : vs % C::NB) : wave / C::MBC;
     // offsets into a chunk's cos/sin rows of the tokens of this lane's dW row
-    // (32*hb + lane%32) and dx row (32*nb + lane%32); padding rows take any
+    // (32*hb + lane%32) and dx row (32*nbx + lane%32); padding rows take any
     // staged token's
-    int ph = PAD ? (32 * hb + (lane & 31)) / nh : 0, pr = PAD ? (32 * nb + (lane & 31)) / nh : 0;
-    const int ph_off = (ph < tp ? ph : tp - 1) * pe, pr_off = (pr < tp ? pr : tp - 1) * pe;
+    const int ph = PAD ? (32 * hb + (lane & 31)) / nh : 0;
+    const int ph_off = (ph < tp ? ph : tp - 1) * pe;
+    auto pr_off_of = [&](int nbx) {
+        const int pr = PAD ? (32 * nbx + (lane & 31)) / nh : 0;
+        return (pr < tp ? pr : tp - 1) * pe;
+    };
 
     // token block tb of B = gridDim.x / spans holds the token groups (tp
     // tokens each, one chunk's rows) [tb*G/B, (tb+1)*G/B) of the G = ngroups
@@ -1551,9 +1567,12 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) wf[kb] = tr_frag(wl + (16 * kb) * C::WPITCH + 32 * nb, C::WPITCH, lane);
     } else if (!dw_role) {
+        // 128 rows: the eight fragments of N-block nb (fragment kb in
+        // keep[kb / 4]); 64 rows: the four of each N-block (N-block n in keep[n])
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-            const u32x4 f = *reinterpret_cast<const u32x4*>(wl + (32 * nb + (lane & 31)) * C::WPITCH + 16 * kb +
+        for (int kb = 0; kb < 2 * 4; ++kb) {
+            const int n = C::NB == 2 ? kb >> 2 : nb, k = C::NB == 2 ? kb & 3 : kb;
+            const u32x4 f = *reinterpret_cast<const u32x4*>(wl + (32 * n + (lane & 31)) * C::WPITCH + 16 * k +
                                                             8 * (lane >> 5));
 #pragma unroll
             for (int e = 0; e < 4; ++e) keep[kb >> 2][4 * (kb & 3) + e] = __uint_as_float(f[e]);
@@ -1663,10 +1682,19 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         };
 
         if (C::SPLIT && dw_role) {
-            // ---- weight gradient: tiles (gb, hb) and (gb + 1, hb), every k-step
+            // ---- weight gradient: tiles (gb, hb) and (gb + 1, hb), k-steps
+            // t = dkset, dkset + DW_KSETS, ... (every k-step at 128 rows).
+            // The lane's channel offset is made opaque per chunk: otherwise
+            // the compiler keeps one precomputed offset per k-step live across
+            // the chunk loop, they spill, and their reloads in the pe k-steps
+            // wait for the chunk prefetch (scratch and global loads share a
+            // counter).  Recomputing an offset is one add.
+            int h8 = 8 * half;
+            asm volatile("" : "+v"(h8));
 #pragma unroll
-            for (int t = 0; t < C::KS; ++t) {
-                const int c = 16 * t + 8 * half;
+            for (int j = 0; j < C::KS / C::DW_KSETS; ++j) {
+                const int t = dkset + C::DW_KSETS * j;
+                const int c = 16 * t + h8;
                 const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(dyl + (32 * gb + (lane & 31)) * C::PITCH + c);
                 const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(dyl + (32 * gb + 32 + (lane & 31)) * C::PITCH + c);
                 const int h = 32 * hb + (lane & 31);
@@ -1702,17 +1730,49 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             }
         }
 
-        // ---- input gradient: M-block m (channels), N-block nb (heads); bfrag(kb)
+        // ---- input gradient: M-block m (channels), N-block n (heads); bfrag(kb)
         // gives the lane's W fragment of k-block kb
         const bool paired = chunk_pe && pe_pairs_in_blocks(nope, pe);
         const int L = nope - c_base;  // local index of the first pe channel (chunks with pe)
+        // the results of block (m, n): paired pe blocks rotated in registers,
+        // other pe channels to the fp32 scratch, nope channels rounded to bf16
+        auto dx_store = [&](const f32x16& acc, int m, int n) {
+            const bool pb = paired && 32 * m >= L;  // a paired pe block (wave-uniform)
+            const int q = m - (L >> 5);
+            const int hrow = 32 * n + (lane & 31);
+            if (pb) {
+                const int pr_off = pr_off_of(n);
+                rotate_paired_block(acc, dol, C::PITCH, hrow, L, h2, q, Q, csl + pr_off, snl + pr_off, -1.0f);
+            }
+#pragma unroll
+            for (int a = 0; a < 4 && !pb; ++a) {
+                const int cl = 32 * m + 8 * a + 4 * Q;
+                const int cg = c_base + cl;
+                if (cg < nope) {
+                    uint2 o;
+                    o.x = pack_bf16(acc[4 * a], acc[4 * a + 1]);
+                    o.y = pack_bf16(acc[4 * a + 2], acc[4 * a + 3]);
+                    *reinterpret_cast<uint2*>(dol + hrow * C::PITCH + cl) = o;
+                } else {
+                    f32x4 o = {acc[4 * a], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]};
+                    *reinterpret_cast<f32x4*>(pes + hrow * pes_pitch + (cg - nope)) = o;
+                }
+            }
+        };
+        // the lane's A fragment columns of M-block m (a paired pe block takes
+        // 16 first-half channels and their 16 partners)
+        auto a_cols = [&](int m, int& clo, int& chi) {
+            const bool pb = paired && 32 * m >= L;
+            const int q = m - (L >> 5);
+            clo = pb ? L + 16 * q : 32 * m;
+            chi = pb ? L + h2 + 16 * q : 32 * m + 16;
+        };
         auto dx_block = [&](int m, auto&& bfrag) {
             f32x16 acc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-            const bool pb = paired && 32 * m >= L;  // a paired pe block (wave-uniform)
-            const int q = m - (L >> 5);
-            const int clo = pb ? L + 16 * q : 32 * m, chi = pb ? L + h2 + 16 * q : 32 * m + 16;
+            int clo, chi;
+            a_cols(m, clo, chi);
             if constexpr (C::SPLIT) {  // A fragments one k-block ahead (registers)
                 bf16x8 a = tr_frag2(dyl, clo, chi, C::PITCH, lane);
 #pragma unroll
@@ -1731,32 +1791,36 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
                 for (int kb = 0; kb < C::KB; ++kb)
                     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], bfrag(kb), acc, 0, 0, 0);
             }
-            const int hrow = 32 * nb + (lane & 31);
-            if (pb) rotate_paired_block(acc, dol, C::PITCH, hrow, L, h2, q, Q, csl + pr_off, snl + pr_off, -1.0f);
+            dx_store(acc, m, nb);
+        };
+        auto kept = [&](int kb) {
+            u32x4 f;
 #pragma unroll
-            for (int a = 0; a < 4 && !pb; ++a) {
-                const int cl = 32 * m + 8 * a + 4 * Q;
-                const int cg = c_base + cl;
-                if (cg < nope) {
-                    uint2 o;
-                    o.x = pack_bf16(acc[4 * a], acc[4 * a + 1]);
-                    o.y = pack_bf16(acc[4 * a + 2], acc[4 * a + 3]);
-                    *reinterpret_cast<uint2*>(dol + hrow * C::PITCH + cl) = o;
-                } else {
-                    f32x4 o = {acc[4 * a], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]};
-                    *reinterpret_cast<f32x4*>(pes + hrow * pes_pitch + (cg - nope)) = o;
-                }
-            }
+            for (int e = 0; e < 4; ++e) f[e] = __float_as_uint(keep[kb >> 2][4 * (kb & 3) + e]);
+            return as_bf16x8(f);
         };
         if (!C::SPLIT) {
             dx_block(mb, [&](int kb) { return wf[C::SPLIT ? 0 : kb]; });
-        } else if (!dw_role) {
-            auto kept = [&](int kb) {
-                u32x4 f;
+        } else if (!dw_role && C::NB == 2) {
+            // 64 rows: M-block mb for both N-blocks from one read of its A
+            // fragments; each block's MFMA inputs and k order are the
+            // token-part kernel's, so dO keeps its bits
+            int clo, chi;
+            a_cols(mb, clo, chi);
+            bf16x8 af[C::KB];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) f[e] = __float_as_uint(keep[kb >> 2][4 * (kb & 3) + e]);
-                return as_bf16x8(f);
-            };
+            for (int kb = 0; kb < C::KB; ++kb) af[kb] = tr_frag2(dyl + (16 * kb) * C::PITCH, clo, chi, C::PITCH, lane);
+            f32x16 acc0, acc1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < C::KB; ++kb) {
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], kept(kb), acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], kept(4 + kb), acc1, 0, 0, 0);
+            }
+            dx_store(acc0, mb, 0);
+            dx_store(acc1, mb, 1);
+        } else if (!dw_role) {
             dx_block(mb, kept);
             dx_block(mb + 1, kept);
         }
@@ -1814,43 +1878,69 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     }
 
     // ---- dW partial: the k-sets of each tile summed in k-set order (fixed);
-    // SPLIT: each tile is one wave's (all k-steps)
+    // SPLIT: each wave owns two tiles over its k-set (at 128 rows every k-step)
     float* red = reinterpret_cast<float*>(smem);
+    constexpr int NPAIR = C::NB * (C::NB / 2);  // SPLIT: dW waves of one k-set
+    const int pair = vs % NPAIR;
+    auto red_slot = [&](int k, int j, int r) -> float& {
+        return red[((((k - 1) * NPAIR + pair) * 2 + j) * 16 + r) * 64 + lane];
+    };
     if (!C::SPLIT && kset != 0) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) red[(((kset - 1) * C::NTILE + tile) * 16 + r) * 64 + lane] = acc_w[r];
     }
+    if (C::SPLIT && C::DW_KSETS > 1 && dw_role && dkset != 0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red_slot(dkset, j, r) = keep[j][r];
+    }
     __syncthreads();
-    if constexpr (C::SPLIT && PAD) {
-        // the [NH, NH] tile sums to LDS, then the partial's nh x nh corner
-        // (tp = 1 at 128 rows)
-        float* m = red;
-        static_assert(NH * (NH + 1) * 4 <= 3 * NH * C::PITCH * 2, "partial area");
-        if (dw_role) {
+    if constexpr (C::SPLIT) {
+        const bool owner = dw_role && dkset == 0;
+        if (C::DW_KSETS > 1 && owner) {
+#pragma unroll
+            for (int k = 1; k < C::DW_KSETS; ++k)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) keep[j][r] += red_slot(k, j, r);
+        }
+        if constexpr (PAD) {
+            // the [NH, NH] tile sums to LDS (after the k-set area), then the
+            // partial is the sum of the tp diagonal [nh, nh] blocks, p = 0, 1,
+            // .. in order (tp = 1 at 128 rows: the block itself)
+            constexpr int RED = (C::DW_KSETS - 1) * NPAIR * 2 * 16 * 64;
+            static_assert((RED + NH * (NH + 1)) * 4 <= 3 * NH * C::PITCH * 2, "partial area");
+            float* m = red + RED;
+            if (owner) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        m[(32 * (gb + j) + 8 * (r >> 2) + 4 * half + (r & 3)) * (NH + 1) + 32 * hb + (lane & 31)] =
+                            keep[j][r];
+            }
+            __syncthreads();
+            float* part_out = partials + (int64_t)blockIdx.x * nh * nh;
+            for (int idx = tid; idx < nh * nh; idx += C::NT) {
+                const int g = idx / nh, h = idx - g * nh;
+                float sum = m[g * (NH + 1) + h];
+                for (int p = 1; p < tp; ++p) sum += m[(p * nh + g) * (NH + 1) + p * nh + h];
+                part_out[idx] = sum;
+            }
+            return;
+        } else {
+            if (!owner) return;
+            float* part_out = partials + (int64_t)blockIdx.x * nh * nh;
+            const int h = 32 * hb + (lane & 31);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    m[(32 * (gb + j) + 8 * (r >> 2) + 4 * half + (r & 3)) * (NH + 1) + 32 * hb + (lane & 31)] =
-                        keep[j][r];
+                    part_out[(32 * (gb + j) + 8 * (r >> 2) + 4 * half + (r & 3)) * nh + h] = keep[j][r];
+            return;
         }
-        __syncthreads();
-        float* part_out = partials + (int64_t)blockIdx.x * nh * nh;
-        for (int idx = tid; idx < nh * nh; idx += C::NT) {
-            const int g = idx / nh, h = idx - g * nh;
-            part_out[idx] = m[g * (NH + 1) + h];
-        }
-        return;
-    } else if constexpr (C::SPLIT) {
-        if (!dw_role) return;
-        float* part_out = partials + (int64_t)blockIdx.x * nh * nh;
-        const int h = 32 * hb + (lane & 31);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                part_out[(32 * (gb + j) + 8 * (r >> 2) + 4 * half + (r & 3)) * nh + h] = keep[j][r];
-        return;
     } else if constexpr (PAD) {
         // the full [NH, NH] sum goes to LDS (after the k-set area), then the
         // partial is the sum of the tp diagonal [nh, nh] blocks, p = 0, 1, ..
