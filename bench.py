@@ -90,32 +90,51 @@ def measured_traffic(kernel_key: str):
 
 def cpu_baseline(case, O, W, dY, pos, target_s: float):
     """The oracle, untouched, on the first S tokens of the workload (S sized
-    from a short calibration so the timed run is about target_s seconds)."""
+    from a short calibration so the timed run is about target_s seconds).
+    The step's algorithmic bytes scale with the tokens, so the sample's rate is
+    the full workload's; per op: the oracle's time extrapolated to the full
+    workload, its GB/s over the op's algorithmic bytes and its GFLOP/s."""
     import oracle
     threads = oracle.default_threads()
+    calls = {
+        "fwd": lambda S: oracle.fwd(O[:S], W, pos[:S], case.theta, case.nope, case.pe, nthreads=threads),
+        "bwd_dx": lambda S: oracle.bwd_dx(dY[:S], W, pos[:S], case.theta, case.nope, case.pe, nthreads=threads),
+        "bwd_dw": lambda S: oracle.bwd_dw(dY[:S], O[:S], pos[:S], case.theta, case.nope, case.pe,
+                                          nthreads=threads),
+    }
 
     def one_pass(S):
-        t0 = time.perf_counter()
-        oracle.fwd(O[:S], W, pos[:S], case.theta, case.nope, case.pe, nthreads=threads)
-        oracle.bwd_dx(dY[:S], W, pos[:S], case.theta, case.nope, case.pe, nthreads=threads)
-        oracle.bwd_dw(dY[:S], O[:S], pos[:S], case.theta, case.nope, case.pe, nthreads=threads)
-        return time.perf_counter() - t0
+        secs = {}
+        for op, fn in calls.items():
+            t0 = time.perf_counter()
+            fn(S)
+            secs[op] = time.perf_counter() - t0
+        return secs
 
     cal = min(case.sq, 256)
-    t_cal = one_pass(cal)
+    t_cal = sum(one_pass(cal).values())
     S = int(min(case.sq, max(cal, round(target_s / max(t_cal, 1e-6) * cal / 64) * 64)))
-    t = one_pass(S)
+    secs = one_pass(S)
+    t = sum(secs.values())
     frac = S / case.sq
+    # the step (fwd + the single-call backward) moves these bytes; the oracle
+    # computes the same outputs with its three functions
     alg = sum(case.algorithmic_bytes(op) for op in STEP_OPS) * frac
+    per_op = {}
+    for op, s in secs.items():
+        per_op[op] = {"us_full_workload": round(s / frac * 1e6, 1),
+                      "GBps": round(case.algorithmic_bytes(op) * frac / s / 1e9, 3),
+                      "GFLOPs": round(case.flops() * frac / s / 1e9, 2)}
     return {
         "value": round(alg / t / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"fwd, dx and dW on the first {S} of {case.sq} tokens "
-                  f"({t:.2f} s; full step extrapolates to {t / frac * 1e6:.0f} us)",
+                  f"({t:.2f} s; the full step extrapolates to {t / frac * 1e6:.0f} us)",
         "seconds": round(t, 3),
         "us_per_full_step_extrapolated": round(t / frac * 1e6, 1),
+        "ops": per_op,
     }
 
 
@@ -298,9 +317,10 @@ def summarize_counters(pmc_dir, command_note, out_prefix, kernels=None, n_cu=256
 
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
-        # bench.py --summarize-counters PMC_DIR NAME COMMAND_NOTE_FILE
+        # bench.py --summarize-counters PMC_DIR NAME COMMAND_NOTE_FILE [WORKLOAD]
         pmc_dir, name, note_file = sys.argv[2:5]
-        summarize_counters(pmc_dir, open(note_file).read(), name)
+        workload = sys.argv[5] if len(sys.argv) > 5 else "prod"
+        summarize_counters(pmc_dir, open(note_file).read(), name, kernels=KERNELS_BY_WORKLOAD[workload])
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
         # bench.py --summarize-profiles TRACE_DIR FETCH_DIR WRITE_DIR NAME COMMAND_NOTE_FILE [WORKLOAD]
@@ -315,7 +335,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=30)  # ~35 ms: lets the clocks settle
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prod",
                     help="prod (default) or another key of synthetic.CASES")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -364,6 +384,8 @@ def main():
                                             workspace=ws),
     }
 
+    dist = [{}]  # op -> (median ms, min ms) of the timed passes
+
     def timed_loop(ops):
         """Warm up, then time args.steps passes of `ops`; events between calls."""
         for _ in range(args.warmup):
@@ -381,8 +403,10 @@ def main():
                 ev[k][i + 1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        ms = {op: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
-              for i, op in enumerate(ops)}
+        samples = {op: [ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]
+                   for i, op in enumerate(ops)}
+        ms = {op: float(np.mean(v)) for op, v in samples.items()}
+        dist[0].update({op: (float(np.median(v)), float(np.min(v))) for op, v in samples.items()})
         return wall, ms
 
     # the unfused route (materialised inv_rope(O); rebuilt in the backward) and
@@ -411,8 +435,10 @@ def main():
     op_report = {}
     for op in ops:
         gbps = alg[op] / (per_op_ms[op] * 1e-3) / 1e9
+        med, mn = dist[0][op]
         op_report[op] = {"us": round(per_op_ms[op] * 1e3, 1), "GBps": round(gbps, 1),
                          "pct_peak": round(100 * gbps / PEAK_GBPS, 1),
+                         "us_median": round(med * 1e3, 1), "us_min": round(mn * 1e3, 1),
                          "algorithmic_bytes": alg[op], "in_step": op in STEP_OPS}
 
     # device-to-device copy of the same 1 GiB, for an achievable-bandwidth reference
