@@ -1588,11 +1588,63 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     // done with them (barrier), chunk k+1 (already in registers) is staged
     // there and chunk k+2 is requested, and only then are chunk k's dO rows
     // stored (they live in separate buffers).  Two barriers per chunk.
+    // ---- PS: the rotated pe operand of chunk kk, once per chunk.  A task is
+    // a row and 4 channels i .. i+3 of the first half with their partners
+    // i+h2 ..: both halves are read and written by the same thread (4
+    // channels, not 8: this pass sets the kernel's register peak).  hi goes in
+    // place of the staged O, lo to lol.  It runs in the staging phase, right
+    // after the next chunk's loads are issued (the memory wait hides it), by
+    // every wave, instead of in the compute phase, where the dW waves set the
+    // pace.  Each row takes the cos/sin row of its token (one token per chunk
+    // at 128 rows).  vh (tasks per row) is a power of two (checked at launch):
+    // a shift and a mask split the task index.  A division there made the
+    // compiler keep a 64-bit value across the chunk loop, spilled, and its
+    // reload waited for the chunk prefetch (nh = 96: 65 us of 760).
+    auto chunk_has_pe = [&](int kk) { return pe > 0 && (p0 + kk % cps) * CH + CH > nope; };
+    auto pe_pass = [&](int kk) {
+        static_assert(!PS || C::SPLIT, "the pe pass is compiled for waves split by gradient only");
+        const int c_base = (p0 + kk % cps) * CH;
+        const int tok = (kk / cps) * tp;
+        const float* csl = rope_g + ((C::NBUF == 2 ? (tok / rgt) & 1 : 0) * rgt + tok % rgt) * pe;
+        uint16_t* const lol = reinterpret_cast<uint16_t*>(rope_g + C::NBUF * rgt * pe);  // [NH][pe + 8]
+        const int L0 = nope - c_base;  // local first pe channel (the whole pe range is in this chunk)
+        const int vh = h2 >> 2;
+        const int lvh = __builtin_ctz((unsigned)vh);
+        for (int task = tid; task < (NH << lvh); task += C::NT) {
+            const int row = task >> lvh, i = 4 * (task & (vh - 1));
+            uint16_t* const o1 = ol + row * C::PITCH + L0 + i;
+            uint16_t* const o2 = o1 + h2;
+            const uint2 a = *reinterpret_cast<const uint2*>(o1), b = *reinterpret_cast<const uint2*>(o2);
+            int rt = PAD && NH == 64 ? row / nh : 0;  // the row's token (padding rows: any staged one)
+            rt = rt < tp ? rt : tp - 1;
+            const float* cr = csl + rt * pe + i;
+            const f32x4 c4 = *reinterpret_cast<const f32x4*>(cr), s4 = *reinterpret_cast<const f32x4*>(cr + h2);
+            float cs[4], sp[4], sm[4];
+            uint32_t aw[2] = {a.x, a.y}, bw[2] = {b.x, b.y}, h1[2], l1[2], hh2[2], ll2[2];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                cs[e] = c4[e];
+                sp[e] = s4[e];
+                sm[e] = -s4[e];
+            }
+            rotate_split<2>(aw, bw, cs, sp, h1, l1);   // first half: a C + b S
+            rotate_split<2>(bw, aw, cs, sm, hh2, ll2);  // second half: b C - a S
+            *reinterpret_cast<uint2*>(o1) = uint2{h1[0], h1[1]};
+            *reinterpret_cast<uint2*>(o2) = uint2{hh2[0], hh2[1]};
+            *reinterpret_cast<uint2*>(lol + row * lpitch + i) = uint2{l1[0], l1[1]};
+            *reinterpret_cast<uint2*>(lol + row * lpitch + h2 + i) = uint2{ll2[0], ll2[1]};
+        }
+    };
+
     if (nchunks > 0) {
         stage_chunk(0);
         if (nchunks > 1) load_chunk(1);
     }
     __syncthreads();
+    if (PS && nchunks > 0 && chunk_has_pe(0)) {
+        pe_pass(0);
+        __syncthreads();
+    }
     for (int k = 0; k < nchunks; ++k) {
         const int64_t s = s_begin + (int64_t)(k / cps) * tp;  // first token of the chunk
         const int part = p0 + k % cps;
@@ -1603,46 +1655,6 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         const float* csl = rope_g + ((C::NBUF == 2 ? (tok / rgt) & 1 : 0) * rgt + tok % rgt) * pe;
         const float* snl = csl + (pe >> 1);
         uint16_t* const lol = reinterpret_cast<uint16_t*>(rope_g + C::NBUF * rgt * pe);  // [NH][pe + 8]
-
-        // ---- PS: the chunk's rotated pe operand, once.  A task is a row and
-        // 4 channels i .. i+3 of the first half with their partners i+h2 ..:
-        // both halves are read and written by the same thread (4 channels,
-        // not 8: this phase sets the kernel's register peak)
-        if (PS && chunk_pe) {
-            // 128 rows: one token per chunk, so every row takes the chunk's
-            // cos/sin row.  vh (tasks per row) is a power of two (pe = 32 or
-            // 64; checked at launch): a shift and a mask split the task index.
-            // A division there made the compiler keep a 64-bit value across
-            // the chunk loop, spilled, and its reload waited for the chunk
-            // prefetch (nh = 96: 65 us of 760).
-            static_assert(!PS || C::SPLIT, "the pe pass is compiled at 128 rows only");
-            const int L0 = nope - c_base;  // local first pe channel (the whole pe range is in this chunk)
-            const int vh = h2 >> 2;
-            const int lvh = __builtin_ctz((unsigned)vh);
-            for (int task = tid; task < (NH << lvh); task += C::NT) {
-                const int row = task >> lvh, i = 4 * (task & (vh - 1));
-                uint16_t* const o1 = ol + row * C::PITCH + L0 + i;
-                uint16_t* const o2 = o1 + h2;
-                const uint2 a = *reinterpret_cast<const uint2*>(o1), b = *reinterpret_cast<const uint2*>(o2);
-                const float* cr = csl + i;
-                const f32x4 c4 = *reinterpret_cast<const f32x4*>(cr), s4 = *reinterpret_cast<const f32x4*>(cr + h2);
-                float cs[4], sp[4], sm[4];
-                uint32_t aw[2] = {a.x, a.y}, bw[2] = {b.x, b.y}, h1[2], l1[2], hh2[2], ll2[2];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    cs[e] = c4[e];
-                    sp[e] = s4[e];
-                    sm[e] = -s4[e];
-                }
-                rotate_split<2>(aw, bw, cs, sp, h1, l1);   // first half: a C + b S
-                rotate_split<2>(bw, aw, cs, sm, hh2, ll2);  // second half: b C - a S
-                *reinterpret_cast<uint2*>(o1) = uint2{h1[0], h1[1]};
-                *reinterpret_cast<uint2*>(o2) = uint2{hh2[0], hh2[1]};
-                *reinterpret_cast<uint2*>(lol + row * lpitch + i) = uint2{l1[0], l1[1]};
-                *reinterpret_cast<uint2*>(lol + row * lpitch + h2 + i) = uint2{ll2[0], ll2[1]};
-            }
-            __syncthreads();
-        }
 
         // the weight gradient's B operand of a pe k-step: the rotated O rows
         // (h, channels c .. c+7), split into hi + lo; PS: hi formed in place
@@ -1834,6 +1846,10 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             if (pe > 0 && (k + 1) % cps == 0 && tok1 % rgt == 0) load_rope_group(s_begin + tok1, (tok1 / rgt) & 1);
             stage_chunk(k + 1);
             if (k + 2 < nchunks) load_chunk(k + 2);  // in flight during two compute phases
+            if (PS && chunk_has_pe(k + 1)) {
+                __syncthreads();  // chunk k+1 staged by every thread
+                pe_pass(k + 1);   // visible to its compute phase after the barrier below
+            }
         }
 
         // ---- dO rows of the chunk; pe pairs turned by +phi
@@ -2726,6 +2742,8 @@ static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int64_t
     // per chunk (rotation 70 us of 721 us at sq = 8192), and this takes the
     // backward from 732 to 712 us.  At NH = 64 its registers pushed spill
     // reloads into the chunk loop (535 -> 730 us), so it is not compiled there.
+    // 128 rows only: with 64 rows the dW waves rotating their own pe operand
+    // measured faster (the extra staging-phase barrier costs more there)
     constexpr bool PS_OK = NH == 128;
     const int vh = a.pe / 8;  // its tasks per row: a power of two
     const bool ps = PS_OK && a.pe > 0 && (vh & (vh - 1)) == 0 && C::lds_bytes(a.nope, a.pe, rgt, true) <= kMaxLds;
