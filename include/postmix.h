@@ -40,7 +40,11 @@
  *  - Limits: 1 <= nh <= 128; nope >= 0 with nope % 8 == 0; pe >= 0 with
  *    pe % 16 == 0; 0 < nope + pe <= 2^24; sq >= 0; sq * nh * (nope + pe)
  *    <= 2^40 elements, so any tensor that fits in device memory.  sq == 0 is
- *    a successful no-op.
+ *    a successful no-op.  The pages' shapes (nh = 3, 4, 64; 448 + 64 and
+ *    48 + 16 channels) and the head counts up to 128 lie inside.  Why: one
+ *    16-byte vector holds 8 channels, and each rotation half (pe/2 channels)
+ *    and the nope range are whole vectors; W's rows and its MFMA fragments
+ *    are staged for up to 128 heads; in-token offsets fit 31 bits.
  *  - Activation, table and workspace pointers must be 16-byte aligned; W must
  *    be 2-byte aligned (for nh of 32, 64 or 128 the tiled kernels read W in
  *    16-byte vectors and are used only when W is 16-byte aligned; other head
@@ -105,8 +109,13 @@ int postmix_bwd_dx(const pm_bf16 *dY, const pm_bf16 *W, const float *rope_cos,
 
 /*
  * Bytes of device workspace postmix_bwd_dw and postmix_bwd need for this
- * shape (a multiple of 256): one nh x nh fp32 partial per token block, for
- * the larger of the two block counts the calls may use.  Depends on
+ * shape (a multiple of 256).  Not on the pages: it serves this library's
+ * reading of their determinism requirement (backward reductions without
+ * atomics that repeat bit for bit, PaddleFleet PR #1776; the weight gradient
+ * dM[h,h'] = sum_{t,c} ... of PR #1772, description part 一).  Each token
+ * block (and, for very wide rows, each channel span of it) writes one nh x nh
+ * fp32 partial here, and a fixed-order tree adds them; the size is that of
+ * the larger of the two partitions the calls may use.  Depends on
  * (sq, nh, nope, pe) only.  Returns 0 for sq == 0 and for shapes outside the
  * limits.
  */
@@ -196,6 +205,13 @@ int postmix_bwd_noalloc(const pm_bf16 *dY, const pm_bf16 *O, const pm_bf16 *W,
  * RoPE tables from theta: row r (position r), column i < pe/2:
  *   cos_out[r, i] = cos(r * theta^(-2i/pe)),  sin_out likewise,
  * with the angle formed and evaluated in fp64, then rounded to fp32.
+ * The pages state the problem with RoPE on the trailing qk_pos_emb_head_dim
+ * channels (PR #1772 body item 1) but print neither its frequencies nor its
+ * precision; both are readings: the usual frequency ladder over the pe
+ * channels, and an fp64 angle (an fp32 position * frequency product is off
+ * by up to ~1.2e-3 rad at positions near 32767, which moves outputs past the
+ * forward tolerance).  The kernels take the tables, not theta, so callers
+ * with other frequencies pass their own.
  * cos_out, sin_out: [table_rows, pe/2] fp32 device buffers, written.
  */
 int postmix_rope_table(double theta, int32_t pe, int64_t table_rows,
