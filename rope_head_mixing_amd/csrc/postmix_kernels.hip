@@ -1357,7 +1357,13 @@ struct BwdCfg {
     static constexpr int NB = NH / 32, KB = NH / 16;
     // SPLIT: k-sets of the dW waves (1 at 128 rows: each tile is one wave's)
     static constexpr int DW_KSETS = SPLIT ? (WAVES / 2) / (NB * NB / 2) : 1;
-    static constexpr int PITCH = CH + 8;
+    // Row pitch (bf16).  The split kernels pad 48 B: rows 12 banks apart (of
+    // 64) keep the dW reads (16 rows of 16 B) free of bank conflicts and
+    // leave the dx transposed reads (4 rows of 32 + 32 B) 2-way, against
+    // 4-way at 16 B of padding (rows 4 banks apart), which measured 2.3x the
+    // cost of a conflict-free read.
+    static constexpr int PITCH = SPLIT ? CH + 24 : CH + 8;
+    static constexpr int DPITCH = CH + 8;  // dO rows (no transposed reads)
     static constexpr int WPITCH = NH + 8;
     static constexpr int VPR = CH / 8;
     static constexpr int VPO = NH * VPR;            // vectors per operand per chunk
@@ -1387,10 +1393,17 @@ struct BwdCfg {
     static constexpr int NBUF = NH == 128 ? 1 : 2;
     // dY chunk, O chunk, dO chunk, then W / pe scratch, then the buffers of
     // the cos and sin rows of rgt tokens, then (ps) the lo parts of the
-    // weight gradient's rotated pe operand, [NH][pe + 8] bf16
+    // weight gradient's rotated pe operand, [NH][pe + 8] bf16.  At NH = 128
+    // (pe rotated in registers or absent: no pe scratch) the cos/sin rows and
+    // the lo parts start where W was: W is only read at set-up, before the
+    // first cos/sin rows are fetched.
+    static constexpr bool AUX_OVERLAY = NH == 128;
+    __host__ __device__ static size_t rope_offset(int nope, int pe) { return AUX_OVERLAY ? 0 : aux_bytes(nope, pe); }
     __host__ __device__ static size_t lds_bytes(int nope, int pe, int rgt, bool ps) {
-        return (size_t)3 * NH * PITCH * 2 + aux_bytes(nope, pe) + (size_t)NBUF * rgt * pe * 4 +
-               (ps && pe > 0 ? (size_t)NH * (pe + 8) * 2 : 0);
+        const size_t tail = rope_offset(nope, pe) + (size_t)NBUF * rgt * pe * 4 +
+                            (ps && pe > 0 ? (size_t)NH * (pe + 8) * 2 : 0);
+        const size_t aux = aux_bytes(nope, pe);
+        return (size_t)2 * NH * PITCH * 2 + (size_t)NH * DPITCH * 2 + (tail > aux ? tail : aux);
     }
 };
 
@@ -1414,13 +1427,13 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint16_t* dyl = smem;                               // [NH][PITCH]
     uint16_t* ol = dyl + NH * C::PITCH;                 // [NH][PITCH]
-    uint16_t* dol = ol + NH * C::PITCH;                 // [NH][PITCH]
-    uint16_t* wl = dol + NH * C::PITCH;                 // [NH][WPITCH] bf16, then:
+    uint16_t* dol = ol + NH * C::PITCH;                 // [NH][DPITCH]
+    uint16_t* wl = dol + NH * C::DPITCH;                // [NH][WPITCH] bf16, then:
     float* pes = reinterpret_cast<float*>(wl);          // [NH][pe + 4] fp32, after set-up
     const int pes_pitch = pe + 4;
     // two buffers of the cos/sin rows of rgt consecutive tokens: [2][rgt][pe]
     // floats (cos then sin each); consecutive groups alternate
-    float* const rope_g = reinterpret_cast<float*>(reinterpret_cast<char*>(wl) + C::aux_bytes(nope, pe));
+    float* const rope_g = reinterpret_cast<float*>(reinterpret_cast<char*>(wl) + C::rope_offset(nope, pe));
 
     const int d = nope + pe, h2 = pe >> 1;
     const int lpitch = pe + 8;
@@ -1433,7 +1446,10 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     // SPLIT: dw_role waves own dW tiles (gb, hb), (gb + 1, hb) over k-set
     // dkset; the others dx M-blocks mb, mb + 1 of N-block nb (128 rows) or
     // M-block mb of both N-blocks (64 rows)
-    const bool dw_role = !C::SPLIT || wave < WAVES / 2;
+    // (at 64 rows the dx waves take the lower wave indices: the dx waves set
+    // the compute phase's length, and lower waves win the arbitration for the
+    // MFMA and LDS pipes; at 128 rows that order measured slower)
+    const bool dw_role = !C::SPLIT || (C::NB == 2 ? wave >= WAVES / 2 : wave < WAVES / 2);
     const int vs = wave % (WAVES / 2);
     const int gb = C::SPLIT ? 2 * ((vs / C::NB) % (C::NB / 2)) : tile / C::NB;
     const int hb = C::SPLIT ? vs % C::NB : tile % C::NB;
@@ -1529,7 +1545,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         }
     };
     if (nchunks > 0) load_chunk(0);
-    if (pe > 0 && nchunks > 0) load_rope_group(s_begin, 0);
+    if (!C::AUX_OVERLAY && pe > 0 && nchunks > 0) load_rope_group(s_begin, 0);
 
     // W -> LDS -> this wave's dx B operand (B[k=g][n=h] = W[g][h], N-block nb).
     // SPLIT stages W transposed, [h][g]: a lane's B fragment (column h, 8
@@ -1578,7 +1594,8 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             for (int e = 0; e < 4; ++e) keep[kb >> 2][4 * (kb & 3) + e] = __uint_as_float(f[e]);
         }
     }
-    __syncthreads();  // W's LDS becomes the pe scratch
+    __syncthreads();  // W's LDS becomes the pe scratch (or the cos/sin rows)
+    if (C::AUX_OVERLAY && pe > 0 && nchunks > 0) load_rope_group(s_begin, 0);
 
     f32x16 acc_w;
 #pragma unroll
@@ -1754,7 +1771,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             const int hrow = 32 * n + (lane & 31);
             if (pb) {
                 const int pr_off = pr_off_of(n);
-                rotate_paired_block(acc, dol, C::PITCH, hrow, L, h2, q, Q, csl + pr_off, snl + pr_off, -1.0f);
+                rotate_paired_block(acc, dol, C::DPITCH, hrow, L, h2, q, Q, csl + pr_off, snl + pr_off, -1.0f);
             }
 #pragma unroll
             for (int a = 0; a < 4 && !pb; ++a) {
@@ -1764,7 +1781,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
                     uint2 o;
                     o.x = pack_bf16(acc[4 * a], acc[4 * a + 1]);
                     o.y = pack_bf16(acc[4 * a + 2], acc[4 * a + 3]);
-                    *reinterpret_cast<uint2*>(dol + hrow * C::PITCH + cl) = o;
+                    *reinterpret_cast<uint2*>(dol + hrow * C::DPITCH + cl) = o;
                 } else {
                     f32x4 o = {acc[4 * a], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]};
                     *reinterpret_cast<f32x4*>(pes + hrow * pes_pitch + (cg - nope)) = o;
@@ -1863,7 +1880,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             const int cl = 8 * c8, cg = c_base + cl;
             u32x4 o;
             if (cg < nope || paired) {
-                o = *reinterpret_cast<const u32x4*>(dol + row * C::PITCH + cl);
+                o = *reinterpret_cast<const u32x4*>(dol + row * C::DPITCH + cl);
             } else {
                 const int i = cg - nope;
                 const bool first = i < h2;
