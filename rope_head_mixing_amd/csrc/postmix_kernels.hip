@@ -625,7 +625,12 @@ struct PartCfg {
     static constexpr int KB = NH / 16, NB = NH / 32, NT = 64 * WAVES;
     // NS > 1: wave w computes N-blocks (w % NS)*NBW .. +NBW of M-blocks w/NS, +MSTEP, ...
     static constexpr int NBW = NB / NS, MSTEP = WAVES / NS;
-    static constexpr int PITCH = CP + 8;                 // bf16 elements per LDS tile row
+    // bf16 elements per LDS tile row.  128 rows pad 48 B (rows 12 of 64 banks
+    // apart: the transposing A-fragment reads 2-way instead of 4-way): the
+    // forward at nh = 128, sq = 8192 went 385 -> 373 us in the benchmark's
+    // regime.  Other heights keep 16 B (no gain at 64 rows; at 96 rows the
+    // wider rows would cost a workgroup per CU).
+    static constexpr int PITCH = NH == 128 ? CP + 24 : CP + 8;
     static constexpr int WPITCH = NH + 8;                // bf16 elements per LDS row of W
     static constexpr int VPR = CP / 8;                   // 16-byte vectors per tile row
     static constexpr int VPT = NH * VPR / NT;            // vectors per thread
@@ -1353,10 +1358,17 @@ struct BwdCfg {
     // each own one dx M-block for both N-blocks, so its transposed dY
     // fragments are read once for two MFMAs.  Against a tile and a dx block on
     // every wave, the compute phase reads a third less LDS per chunk.
-    static constexpr bool SPLIT = NH == 128 || (NH == 64 && WAVES == 16);
+    // 96 rows on 12 waves (one workgroup per CU, 168 registers a wave) split
+    // the same way: waves 0 .. 5 each own the three tiles of one h-block
+    // (g-blocks 0, 1, 2) over one of two k-sets; waves 6 .. 11 each own four
+    // dx M-blocks of one N-block, with its six W fragments in registers.
+    static constexpr bool SPLIT = NH == 128 || NH == 96 || (NH == 64 && WAVES == 16);
     static constexpr int NB = NH / 32, KB = NH / 16;
-    // SPLIT: k-sets of the dW waves (1 at 128 rows: each tile is one wave's)
-    static constexpr int DW_KSETS = SPLIT ? (WAVES / 2) / (NB * NB / 2) : 1;
+    // SPLIT: g-blocks (dW tiles) per dW wave, dW waves per k-set, k-sets
+    // (1 at 128 rows: each tile is one wave's), dx M-blocks per dx wave
+    static constexpr int DWG = NB == 3 ? 3 : 2;
+    static constexpr int DW_PER_KSET = NB == 3 ? 3 : NB * (NB / 2);
+    static constexpr int DW_KSETS = SPLIT ? (WAVES / 2) / DW_PER_KSET : 1;
     // Row pitch (bf16).  The split kernels pad 48 B: rows 12 banks apart (of
     // 64) keep the dW reads (16 rows of 16 B) free of bank conflicts and
     // leave the dx transposed reads (4 rows of 32 + 32 B) 2-way, against
@@ -1372,13 +1384,20 @@ struct BwdCfg {
     static constexpr int KS = CH / 16;              // k-steps of the weight gradient per chunk
     static constexpr int MBC = CH / 32;             // M-blocks of the head mix per chunk
     static constexpr int NTILE = NB * NB;           // dW output tiles
-    static constexpr int KSET = WAVES / NTILE;      // waves per dW tile
-    static_assert((NH == 64 || NH == 128) && MBC * NB == WAVES && KSET >= 1 && KS % KSET == 0 &&
-                  VPO % NT == 0, "fused shape");
+    static constexpr int KSET = WAVES / NTILE;      // waves per dW tile (not SPLIT)
+    static constexpr int DXM = SPLIT ? (NB == 2 ? 1 : MBC * NB / (WAVES / 2)) : 1;
+    static_assert(SPLIT ? ((WAVES / 2) % DW_PER_KSET == 0 && KS % DW_KSETS == 0 &&
+                           (NB == 2 ? MBC == WAVES / 2 : MBC * NB == DXM * (WAVES / 2)) && DXM % (NB == 2 ? 1 : 2) == 0)
+                        : ((NH == 64 || NH == 128) && MBC * NB == WAVES && KSET >= 1 && KS % KSET == 0),
+                  "fused shape");
+    static_assert(VPO % NT == 0, "whole vectors per thread");
+    // 96 rows stage W at set-up in the dO buffer (free until the first
+    // compute phase), so the chunk buffers at CH = 256 fit the LDS
+    static constexpr bool W_IN_DOL = NH == 96;
     // W and the fp32 pe scratch, overlapped (W is consumed at set-up); the
     // scratch is not needed for pe rotated in registers
     __host__ __device__ static size_t aux_bytes(int nope, int pe) {
-        const size_t w = (size_t)NH * WPITCH * 2;
+        const size_t w = W_IN_DOL ? 0 : (size_t)NH * WPITCH * 2;
         const size_t p = pe_pairs_in_blocks(nope, pe) ? 0 : (size_t)NH * (pe + 4) * 4;
         return w > p ? w : p;
     }
@@ -1388,9 +1407,9 @@ struct BwdCfg {
     static constexpr int RG_MAX = 32;
     // buffers of staged cos/sin groups: two (the next group is fetched while
     // the store phase of the current chunk may still read its rows); one at
-    // NH = 128, whose pe is always rotated in registers, so its store phase
-    // reads none
-    static constexpr int NBUF = NH == 128 ? 1 : 2;
+    // NH = 96 and 128, whose pe is always rotated in registers, so their
+    // store phase reads none
+    static constexpr int NBUF = NH >= 96 ? 1 : 2;
     // dY chunk, O chunk, dO chunk, then W / pe scratch, then the buffers of
     // the cos and sin rows of rgt tokens, then (ps) the lo parts of the
     // weight gradient's rotated pe operand, [NH][pe + 8] bf16.  At NH = 128
@@ -1408,7 +1427,7 @@ struct BwdCfg {
 };
 
 template <int NH, int CH, int WAVES, bool PAD, bool PS>
-__global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
+__global__ __launch_bounds__(64 * WAVES, WAVES == 12 ? 3 : 4) void bwd_fused_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ O, const uint16_t* __restrict__ W,
     const float* __restrict__ rcos, const float* __restrict__ rsin, int64_t table_rows,
     const int32_t* __restrict__ positions, int64_t sq, int nh, int nope, int pe,
@@ -1428,12 +1447,13 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     uint16_t* dyl = smem;                               // [NH][PITCH]
     uint16_t* ol = dyl + NH * C::PITCH;                 // [NH][PITCH]
     uint16_t* dol = ol + NH * C::PITCH;                 // [NH][DPITCH]
-    uint16_t* wl = dol + NH * C::DPITCH;                // [NH][WPITCH] bf16, then:
-    float* pes = reinterpret_cast<float*>(wl);          // [NH][pe + 4] fp32, after set-up
+    uint16_t* const auxp = dol + NH * C::DPITCH;
+    uint16_t* wl = C::W_IN_DOL ? dol : auxp;            // [NH][WPITCH] bf16 at set-up
+    float* pes = reinterpret_cast<float*>(auxp);        // [NH][pe + 4] fp32, after set-up
     const int pes_pitch = pe + 4;
     // two buffers of the cos/sin rows of rgt consecutive tokens: [2][rgt][pe]
     // floats (cos then sin each); consecutive groups alternate
-    float* const rope_g = reinterpret_cast<float*>(reinterpret_cast<char*>(wl) + C::rope_offset(nope, pe));
+    float* const rope_g = reinterpret_cast<float*>(reinterpret_cast<char*>(auxp) + C::rope_offset(nope, pe));
 
     const int d = nope + pe, h2 = pe >> 1;
     const int lpitch = pe + 8;
@@ -1443,9 +1463,9 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     // derived indices (tile, k-set, blocks), which otherwise spill
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile = wave % C::NTILE, kset = wave / C::NTILE;
-    // SPLIT: dw_role waves own dW tiles (gb, hb), (gb + 1, hb) over k-set
-    // dkset; the others dx M-blocks mb, mb + 1 of N-block nb (128 rows) or
-    // M-block mb of both N-blocks (64 rows)
+    // SPLIT: dw_role waves own dW tiles (gb + j, hb), j < DWG, over k-set
+    // dkset; the others dx M-blocks mb .. mb + DXM - 1 of N-block nb (96 and
+    // 128 rows) or M-block mb of both N-blocks (64 rows)
     // (at 64 rows the dx waves take the lower wave indices: the dx waves set
     // the compute phase's length, and lower waves win the arbitration for the
     // MFMA and LDS pipes; at 128 rows that order measured slower)
@@ -1453,8 +1473,8 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     const int vs = wave % (WAVES / 2);
     const int gb = C::SPLIT ? 2 * ((vs / C::NB) % (C::NB / 2)) : tile / C::NB;
     const int hb = C::SPLIT ? vs % C::NB : tile % C::NB;
-    const int dkset = C::SPLIT ? vs / (C::NB * (C::NB / 2)) : 0;
-    const int mb = C::SPLIT ? (C::NB == 2 ? vs : 2 * (vs / C::NB)) : wave % C::MBC;
+    const int dkset = C::SPLIT ? vs / C::DW_PER_KSET : 0;
+    const int mb = C::SPLIT ? (C::NB == 2 ? vs : C::DXM * (vs / C::NB)) : wave % C::MBC;
     const int nb = C::SPLIT ? (C::NB == 2 ? 0 : vs % C::NB) : wave / C::MBC;
     // offsets into a chunk's cos/sin rows of the tokens of this lane's dW row
     // (32*hb + lane%32) and dx row (32*nbx + lane%32); padding rows take any
@@ -1520,9 +1540,15 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         const int64_t rowbase = s * nh * (int64_t)d + part * CH;
         const uint16_t* const dyb = dY + rowbase;
         const uint16_t* const ob = O + rowbase;
+        // 96 rows: the thread index is made opaque here, so the per-vector
+        // offsets are recomputed per chunk (a few adds) instead of kept across
+        // the chunk loop, where eight 64-bit offsets were spilled and their
+        // reloads serialised the prefetch
+        int lt = tid;
+        if (C::W_IN_DOL) asm volatile("" : "+v"(lt));
 #pragma unroll
         for (int j = 0; j < C::VPT; ++j) {
-            const int q = j * C::NT + tid;
+            const int q = j * C::NT + lt;
             const int op = q / C::VPO;               // 0: dY, 1: O (compile-time per j)
             const int rem = q % C::VPO;
             int row = rem / C::VPR;
@@ -1534,9 +1560,11 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     };
     auto stage_chunk = [&](int k) {  // registers of chunk k -> LDS (padding rows as zeros)
         const int rows = chunk_rows(k);
+        int lt = tid;  // opaque at 96 rows, as in load_chunk
+        if (C::W_IN_DOL) asm volatile("" : "+v"(lt));
 #pragma unroll
         for (int j = 0; j < C::VPT; ++j) {
-            const int q = j * C::NT + tid;
+            const int q = j * C::NT + lt;
             const int op = q / C::VPO;
             const int rem = q % C::VPO;
             const int row = rem / C::VPR, c8 = rem % C::VPR;
@@ -1574,19 +1602,21 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     }
     __syncthreads();
     bf16x8 wf[C::SPLIT ? 1 : C::KB];  // W fragments in registers (not SPLIT)
-    // SPLIT: a dW wave's two accumulators, or a dx wave's eight W fragments
-    // (fragment kb in keep[kb / 4], elements 4(kb % 4) ..)
-    f32x16 keep[2];
+    // SPLIT: a dW wave's DWG accumulators, or a dx wave's W fragments (eight;
+    // six at 96 rows; fragment kb in keep[kb / 4], elements 4(kb % 4) ..)
+    f32x16 keep[C::DWG];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) keep[0][r] = keep[1][r] = 0.0f;
+    for (int j = 0; j < C::DWG; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) keep[j][r] = 0.0f;
     if (!C::SPLIT) {
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) wf[kb] = tr_frag(wl + (16 * kb) * C::WPITCH + 32 * nb, C::WPITCH, lane);
     } else if (!dw_role) {
-        // 128 rows: the eight fragments of N-block nb (fragment kb in
-        // keep[kb / 4]); 64 rows: the four of each N-block (N-block n in keep[n])
+        // 96 and 128 rows: the six or eight fragments of N-block nb (fragment
+        // kb in keep[kb / 4]); 64 rows: the four of each N-block (N-block n in keep[n])
 #pragma unroll
-        for (int kb = 0; kb < 2 * 4; ++kb) {
+        for (int kb = 0; kb < (C::NB == 2 ? 8 : C::KB); ++kb) {
             const int n = C::NB == 2 ? kb >> 2 : nb, k = C::NB == 2 ? kb & 3 : kb;
             const u32x4 f = *reinterpret_cast<const u32x4*>(wl + (32 * n + (lane & 31)) * C::WPITCH + 16 * k +
                                                             8 * (lane >> 5));
@@ -1594,7 +1624,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             for (int e = 0; e < 4; ++e) keep[kb >> 2][4 * (kb & 3) + e] = __uint_as_float(f[e]);
         }
     }
-    __syncthreads();  // W's LDS becomes the pe scratch (or the cos/sin rows)
+    __syncthreads();  // W's LDS becomes the pe scratch (or the cos/sin rows, or dO)
     if (C::AUX_OVERLAY && pe > 0 && nchunks > 0) load_rope_group(s_begin, 0);
 
     f32x16 acc_w;
@@ -1711,7 +1741,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         };
 
         if (C::SPLIT && dw_role) {
-            // ---- weight gradient: tiles (gb, hb) and (gb + 1, hb), k-steps
+            // ---- weight gradient: tiles (gb + j, hb), j < DWG, k-steps
             // t = dkset, dkset + DW_KSETS, ... (every k-step at 128 rows).
             // The lane's channel offset is made opaque per chunk: otherwise
             // the compiler keeps one precomputed offset per k-step live across
@@ -1724,8 +1754,10 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             for (int j = 0; j < C::KS / C::DW_KSETS; ++j) {
                 const int t = dkset + C::DW_KSETS * j;
                 const int c = 16 * t + h8;
-                const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(dyl + (32 * gb + (lane & 31)) * C::PITCH + c);
-                const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(dyl + (32 * gb + 32 + (lane & 31)) * C::PITCH + c);
+                bf16x8 a[C::DWG];
+#pragma unroll
+                for (int g = 0; g < C::DWG; ++g)
+                    a[g] = *reinterpret_cast<const bf16x8*>(dyl + (32 * (gb + g) + (lane & 31)) * C::PITCH + c);
                 const int h = 32 * hb + (lane & 31);
                 const u32x4 own = *reinterpret_cast<const u32x4*>(ol + h * C::PITCH + c);
                 const bool step_pe = chunk_pe && c_base + 16 * t + 16 > nope;  // wave-uniform
@@ -1733,10 +1765,11 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
                 // each accumulator a second register copy at the join
                 u32x4 hi = own, lo = {0u, 0u, 0u, 0u};
                 if (step_pe) pe_operand(c, c_base + c, h, own, hi, lo);
-                keep[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, as_bf16x8(hi), keep[0], 0, 0, 0);
-                if (step_pe) keep[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, as_bf16x8(lo), keep[0], 0, 0, 0);
-                keep[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, as_bf16x8(hi), keep[1], 0, 0, 0);
-                if (step_pe) keep[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, as_bf16x8(lo), keep[1], 0, 0, 0);
+#pragma unroll
+                for (int g = 0; g < C::DWG; ++g) {
+                    keep[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[g], as_bf16x8(hi), keep[g], 0, 0, 0);
+                    if (step_pe) keep[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[g], as_bf16x8(lo), keep[g], 0, 0, 0);
+                }
             }
         } else if (!C::SPLIT) {
             // ---- weight gradient: tile (gb, hb), k-steps t = kset, kset + KSET, ...
@@ -1849,9 +1882,34 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             }
             dx_store(acc0, mb, 0);
             dx_store(acc1, mb, 1);
+        } else if (!dw_role && C::NB == 3) {
+            // 96 rows: the next M-block's six A fragments are read while this
+            // block's MFMAs run (the registers allow it at 12 waves); one
+            // fragment ahead left the dx waves waiting on LDS latency in each
+            // k-step.  MFMA inputs and k order are those of dx_block.
+            bf16x8 af[C::KB], an[C::KB];
+            auto read_frags = [&](int m, bf16x8* f) {
+                int clo, chi;
+                a_cols(m, clo, chi);
+#pragma unroll
+                for (int kb = 0; kb < C::KB; ++kb) f[kb] = tr_frag2(dyl + (16 * kb) * C::PITCH, clo, chi, C::PITCH, lane);
+            };
+            read_frags(mb, af);
+#pragma unroll
+            for (int i = 0; i < C::DXM; ++i) {
+                if (i + 1 < C::DXM) read_frags(mb + i + 1, an);
+                f32x16 acc;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+                for (int kb = 0; kb < C::KB; ++kb) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb], kept(kb), acc, 0, 0, 0);
+                dx_store(acc, mb + i, nb);
+#pragma unroll
+                for (int kb = 0; kb < C::KB; ++kb) af[kb] = an[kb];
+            }
         } else if (!dw_role) {
-            dx_block(mb, kept);
-            dx_block(mb + 1, kept);
+#pragma unroll
+            for (int i = 0; i < C::DXM; ++i) dx_block(mb + i, kept);
         }
         __syncthreads();  // dY/O buffers free; dO and the pe scratch complete
         if (k + 1 < nchunks) {
@@ -1872,9 +1930,11 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         // ---- dO rows of the chunk; pe pairs turned by +phi
         uint16_t* outs = dO + s * nh * (int64_t)d + c_base;
         const int rows_k = chunk_rows(k);
+        int lt = tid;  // opaque at 96 rows, as in load_chunk
+        if (C::W_IN_DOL) asm volatile("" : "+v"(lt));
 #pragma unroll
         for (int j = 0; j < C::OPT; ++j) {
-            const int q = j * C::NT + tid;
+            const int q = j * C::NT + lt;
             const int row = q / C::VPR, c8 = q % C::VPR;
             if (PAD && row >= rows_k) continue;  // padding rows
             const int cl = 8 * c8, cg = c_base + cl;
@@ -1911,20 +1971,22 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
     }
 
     // ---- dW partial: the k-sets of each tile summed in k-set order (fixed);
-    // SPLIT: each wave owns two tiles over its k-set (at 128 rows every k-step)
+    // SPLIT: each wave owns DWG tiles over its k-set (at 128 rows every k-step)
     float* red = reinterpret_cast<float*>(smem);
-    constexpr int NPAIR = C::NB * (C::NB / 2);  // SPLIT: dW waves of one k-set
+    constexpr int NPAIR = C::DW_PER_KSET;  // SPLIT: dW waves of one k-set
     const int pair = vs % NPAIR;
     auto red_slot = [&](int k, int j, int r) -> float& {
-        return red[((((k - 1) * NPAIR + pair) * 2 + j) * 16 + r) * 64 + lane];
+        return red[((((k - 1) * NPAIR + pair) * C::DWG + j) * 16 + r) * 64 + lane];
     };
+    // LDS left for the reduction and the partial (chunk buffers and dO)
+    constexpr int RED_LDS = 2 * NH * C::PITCH * 2 + NH * C::DPITCH * 2;
     if (!C::SPLIT && kset != 0) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) red[(((kset - 1) * C::NTILE + tile) * 16 + r) * 64 + lane] = acc_w[r];
     }
     if (C::SPLIT && C::DW_KSETS > 1 && dw_role && dkset != 0) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < C::DWG; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) red_slot(dkset, j, r) = keep[j][r];
     }
@@ -1935,7 +1997,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
 #pragma unroll
             for (int k = 1; k < C::DW_KSETS; ++k)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < C::DWG; ++j)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) keep[j][r] += red_slot(k, j, r);
         }
@@ -1943,12 +2005,12 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             // the [NH, NH] tile sums to LDS (after the k-set area), then the
             // partial is the sum of the tp diagonal [nh, nh] blocks, p = 0, 1,
             // .. in order (tp = 1 at 128 rows: the block itself)
-            constexpr int RED = (C::DW_KSETS - 1) * NPAIR * 2 * 16 * 64;
-            static_assert((RED + NH * (NH + 1)) * 4 <= 3 * NH * C::PITCH * 2, "partial area");
+            constexpr int RED = (C::DW_KSETS - 1) * NPAIR * C::DWG * 16 * 64;
+            static_assert((RED + NH * (NH + 1)) * 4 <= RED_LDS, "partial area");
             float* m = red + RED;
             if (owner) {
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < C::DWG; ++j)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         m[(32 * (gb + j) + 8 * (r >> 2) + 4 * half + (r & 3)) * (NH + 1) + 32 * hb + (lane & 31)] =
@@ -1968,7 +2030,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
             float* part_out = partials + (int64_t)blockIdx.x * nh * nh;
             const int h = 32 * hb + (lane & 31);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < C::DWG; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     part_out[(32 * (gb + j) + 8 * (r >> 2) + 4 * half + (r & 3)) * nh + h] = keep[j][r];
@@ -1979,7 +2041,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void bwd_fused_kernel(
         // partial is the sum of the tp diagonal [nh, nh] blocks, p = 0, 1, ..
         // in order (tp = 1: the block itself)
         constexpr int RED = (C::KSET - 1) * C::NTILE * 16 * 64;  // floats of the k-set area
-        static_assert((RED + NH * (NH + 1)) * 4 <= 3 * NH * C::PITCH * 2, "diagonal-block area");
+        static_assert((RED + NH * (NH + 1)) * 4 <= RED_LDS, "diagonal-block area");
         float* m = red + RED;
         if (kset == 0) {
 #pragma unroll
@@ -2606,6 +2668,18 @@ DwPlan dw_plan(int64_t sq, int nh, int nope, int pe) {
 // chunk width of the fused backward: 256 channels (16 waves) where d allows
 static int bwd_fused_chunk(int d) { return d % 256 == 0 ? 256 : 128; }
 
+// Head rows of the fused backward's chunks: 64 (several tokens per chunk
+// below 33 heads, padded rows above), 96 for 64 < nh <= 96 where d is a
+// multiple of 256 and the 256-channel chunks fit the LDS (pe rotated in
+// registers or absent), else 128 (128-channel chunks; their rows are 256 B
+// segments, which stream slower than the 512 B of 256-channel chunks).
+static bool bwd_fused96_fits(int nope, int pe);
+static int bwd_fused_rows(int nh, int nope, int pe) {
+    if (nh <= 64) return 64;
+    if (nh <= 96 && (nope + pe) % 256 == 0 && bwd_fused96_fits(nope, pe)) return 96;
+    return 128;
+}
+
 // Tokens per chunk of the fused backward: nh <= 32 packs the tokens of the
 // dx tile (the token-part kernel's 64-row tile with parts as wide as the
 // chunks), so the two compute dO identically; otherwise one.
@@ -2727,6 +2801,11 @@ static hipError_t launch_dw_t(const DwArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+static bool bwd_fused96_fits(int nope, int pe) {
+    return (pe == 0 || pe_pairs_in_blocks(nope, pe)) &&
+           BwdCfg<96, 256, 12>::lds_bytes(nope, pe, BwdCfg<96, 256, 12>::rope_group(1), false) <= kMaxLds;
+}
+
 // fused backward (dx + dW partials in one pass), then the fixed-order reduce
 bool bwd_fused_applies(int nh, int nope, int pe) {
     const int d = nope + pe;
@@ -2743,6 +2822,7 @@ bool bwd_fused_applies(int nh, int nope, int pe) {
                                         : BwdCfg<64, 128, 8>::lds_bytes(nope, pe, rgt, false);
     } else {
         if (!(pe == 0 || pe_pairs_in_blocks(nope, pe))) return false;
+        if (bwd_fused_rows(nh, nope, pe) == 96) return true;
         lds = BwdCfg<128, 128, 16>::lds_bytes(nope, pe, BwdCfg<128, 128, 16>::rope_group(1), false);
     }
     return lds <= kMaxLds;
@@ -2788,7 +2868,8 @@ hipError_t launch_bwd_fused(const MixArgs& mx, const DwArgs& a, hipStream_t stre
     const int64_t ngroups = (a.sq + tp - 1) / tp;
     hipError_t err;
     if (a.nh > 64)
-        err = launch_bwd_fused_t<128, 128, 16>(mx, a, ngroups, pl, 1, stream);
+        err = bwd_fused_rows(a.nh, a.nope, a.pe) == 96 ? launch_bwd_fused_t<96, 256, 12>(mx, a, ngroups, pl, 1, stream)
+                                                       : launch_bwd_fused_t<128, 128, 16>(mx, a, ngroups, pl, 1, stream);
     else
         err = bwd_fused_chunk(a.nope + a.pe) == 256 ? launch_bwd_fused_t<64, 256, 16>(mx, a, ngroups, pl, tp, stream)
                                                     : launch_bwd_fused_t<64, 128, 8>(mx, a, ngroups, pl, tp, stream);

@@ -213,7 +213,14 @@ def test_tiled_and_general_kernels_agree(sq, nh, nope, pe):
     (5, 128, 432, 80, 2),       # not fused (nh = 128 with pe = 80): separate kernels
     (11, 48, 448, 64, 3),       # fused path, nh = 48 (head rows padded to 64)
     (9, 33, 192, 64, 1),        # fused path, nh = 33, d = 256
-    (7, 96, 448, 64, 5),        # fused path, nh = 96 (head rows padded to 128)
+    (7, 96, 448, 64, 5),        # fused path, nh = 96: 96-row chunks of 256 channels on 12 waves
+    (9, 72, 448, 64, 3),        # fused path, nh = 72: 96-row chunks, rows 72..95 padding
+    (11, 65, 192, 64, 2),       # fused path, nh = 65, d = 256: 96-row chunks, one real row in the last N-block
+    (8, 80, 224, 32, 4),        # fused path, nh = 80, pe = 32 (one paired pe block), 96-row chunks
+    (6, 96, 256, 0, 1),         # fused path, nh = 96, no pe
+    (5, 96, 384, 128, 7),       # fused path, nh = 96, pe = 128: the 96-row LDS does not fit, 128-row chunks
+    (7, 90, 320, 64, 1),        # fused path, nh = 90, d = 384 (not a multiple of 256): 128-row chunks
+    (520, 72, 448, 64, 9),      # fused path, nh = 72: 260 blocks of 2 tokens -> 256 blocks
     (6, 100, 432, 80, 9),       # not fused (padded to 128 with pe = 80): separate kernels
     (21, 32, 448, 64, 5),       # fused path, nh = 32: two tokens per 64-row chunk
     (9, 3, 448, 64, 0),         # fused path, nh = 3: one partial chunk of 9 of 21 tokens
@@ -228,7 +235,7 @@ def test_tiled_and_general_kernels_agree(sq, nh, nope, pe):
     # block counts rounded to a multiple of 256, token groups spread evenly
     (2400, 8, 192, 64, 3),      # 300 blocks of one 8-token chunk -> 256 blocks of 1 or 2 chunks
     (4800, 64, 192, 64, 11),    # 600 blocks of 8 tokens -> 512 blocks of 9 or 10
-    (1200, 96, 192, 64, 5),     # 300 blocks of 4 tokens -> 256 blocks of 4 or 5 (rows padded to 128);
+    (1200, 96, 192, 64, 5),     # 300 blocks of 4 tokens -> 256 blocks of 4 or 5 (96-row chunks);
                                 # the separate weight gradient's 300 blocks -> 256 as well
 ])
 def test_fused_backward_matches_oracle_and_separate_calls(sq, nh, nope, pe, off):
