@@ -54,8 +54,21 @@ KERNELS_NH128 = {
     "bwd_dx": "mix_part_kernel<128, 256, 8, true, 4, false>",
     "bwd_dw": "dw_chunk_kernel<128, 128, false> + dw_reduce_kernel",
 }
+# nh=96 and nh=72 (96-row tiles and chunks; 72 with padding rows)
+KERNELS_NH96 = {
+    "fwd": "mix_part_kernel<96, 256, 6, false, 3, false>",
+    "bwd": "bwd_fused_kernel<96, 256, 12, false, false> + dw_reduce_kernel",
+    "bwd_dx": "mix_part_kernel<96, 256, 6, true, 3, false>",
+    "bwd_dw": "dw_chunk_kernel<128, 128, true> + dw_reduce_kernel",
+}
+KERNELS_NH72 = {
+    "fwd": "mix_part_kernel<96, 256, 6, false, 3, true>",
+    "bwd": "bwd_fused_kernel<96, 256, 12, true, false> + dw_reduce_kernel",
+    "bwd_dx": "mix_part_kernel<96, 256, 6, true, 3, true>",
+    "bwd_dw": "dw_chunk_kernel<128, 128, true> + dw_reduce_kernel",
+}
 KERNELS_BY_WORKLOAD = {"prod": KERNELS_NH64, "fwd_1k": KERNELS_NH64, "sweep_nh3": KERNELS_NH3,
-                       "sweep_nh128": KERNELS_NH128}
+                       "sweep_nh128": KERNELS_NH128, "sweep_nh96": KERNELS_NH96, "sweep_nh72": KERNELS_NH72}
 STEP_OPS = ("fwd", "bwd")          # the timed step
 EXTRA_OPS = ("bwd_dx", "bwd_dw")   # the separate backward entry points, timed after
 # The pages' own figures for this workload (another GPU; context only).

@@ -107,13 +107,17 @@ class Case:
 
 
 # The five workloads (tiny, forward-only, production forward, production
-# backward, head-count sweep) with the seeds used throughout.
+# backward, head-count sweep) with the seeds used throughout, and two more
+# head counts for the 96-row kernels.
 CASES = {
     "tiny": Case("tiny", 64, 4, 48, 16, 0, (1001, 1002, 1003)),
     "fwd_1k": Case("fwd_1k", 1024, 64, 448, 64, 0, (2001, 2002, None)),
     "prod": Case("prod", 16384, 64, 448, 64, 16384, (3001, 3002, 3003)),
     "sweep_nh3": Case("sweep_nh3", 8192, 3, 448, 64, 0, (5001, 5002, 5003)),
     "sweep_nh128": Case("sweep_nh128", 8192, 128, 448, 64, 0, (5011, 5012, 5013)),
+    # head counts between 64 and 128 (96-row tiles and chunks), same recipe
+    "sweep_nh96": Case("sweep_nh96", 8192, 96, 448, 64, 0, (5021, 5022, 5023)),
+    "sweep_nh72": Case("sweep_nh72", 8192, 72, 448, 64, 0, (5031, 5032, 5033)),
 }
 
 

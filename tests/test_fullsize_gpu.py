@@ -6,6 +6,8 @@ The workloads (rope_head_mixing_amd.synthetic.CASES):
     16384..32767 (one context-parallel shard of a 64K sequence, PaddleFleet
     PR #1772 body item 1), forward and backward;
   - sweep_nh128: [8192, 128, 448+64];
+  - sweep_nh96 and sweep_nh72: [8192, 96 or 72, 448+64] (96-row tiles and
+    chunks, 72 with padding rows);
   - a 20500-token production-width case whose single-call backward blocks
     hold 24 tokens (the staged cos/sin rows are refilled inside a block).
 (The forward-only [1024, 64, 448+64] and the nh = 3 sweep are checked the
@@ -86,6 +88,13 @@ def test_production_forward_and_backward_every_element():
 def test_sweep_nh128_every_element():
     """sq=8192, nh=128, 448+64, positions 0..8191."""
     full_size_check(synthetic.CASES["sweep_nh128"])
+
+
+@pytest.mark.parametrize("name", ["sweep_nh96", "sweep_nh72"])
+def test_sweep_96_row_kernels_every_element(name):
+    """sq=8192, nh=96 and 72, 448+64: the 96-row forward/dx tiles and the
+    96-row chunks of the single-call backward (rows 72..95 padding at 72)."""
+    full_size_check(synthetic.CASES[name], repeat=3)
 
 
 def test_fused_backward_long_blocks_every_element():
