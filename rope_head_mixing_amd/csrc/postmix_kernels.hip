@@ -620,17 +620,18 @@ __host__ __device__ __forceinline__ bool pe_pairs_in_blocks(int nope, int pe) {
     return pe > 0 && pe % 32 == 0 && nope % 32 == 0;
 }
 
-template <int NH, int CP, int WAVES, int NS = 1>
+template <int NH, int CP, int WAVES, int NS = 1, bool PADDED = false>
 struct PartCfg {
     static constexpr int KB = NH / 16, NB = NH / 32, NT = 64 * WAVES;
     // NS > 1: wave w computes N-blocks (w % NS)*NBW .. +NBW of M-blocks w/NS, +MSTEP, ...
     static constexpr int NBW = NB / NS, MSTEP = WAVES / NS;
-    // bf16 elements per LDS tile row.  128 rows pad 48 B (rows 12 of 64 banks
-    // apart: the transposing A-fragment reads 2-way instead of 4-way): the
-    // forward at nh = 128, sq = 8192 went 385 -> 373 us in the benchmark's
-    // regime.  Other heights keep 16 B (no gain at 64 rows; at 96 rows the
-    // wider rows would cost a workgroup per CU).
-    static constexpr int PITCH = NH == 128 ? CP + 24 : CP + 8;
+    // bf16 elements per LDS tile row.  128 rows and unpadded 96-row tiles pad
+    // 48 B (rows 12 of 64 banks apart: the transposing A-fragment reads 2-way
+    // instead of 4-way): in the benchmark's regime the forward at sq = 8192
+    // went 385 -> 373 us at nh = 128 and 312 -> 293 us at nh = 96.  Other
+    // tiles keep 16 B: no gain at 64 rows, and padded 96-row tiles (nh = 72)
+    // measured 10% slower with the wider rows at the same occupancy.
+    static constexpr int PITCH = (NH == 128 || (NH == 96 && !PADDED)) ? CP + 24 : CP + 8;
     static constexpr int WPITCH = NH + 8;                // bf16 elements per LDS row of W
     static constexpr int VPR = CP / 8;                   // 16-byte vectors per tile row
     static constexpr int VPT = NH * VPR / NT;            // vectors per thread
@@ -733,7 +734,7 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
     // zero padding, never loaded from or stored to HBM.  Otherwise nh == NH
     // and ptok == 1.
     const int tp = PAD ? ptok : 1;
-    using C = PartCfg<NH, CP, WAVES, NS>;
+    using C = PartCfg<NH, CP, WAVES, NS, PAD>;
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint16_t* tile = smem;                                   // [NH][PITCH] bf16
     uint16_t* wl = smem;                                     // [NH][WPITCH] bf16 first, in the tile's place
@@ -2502,16 +2503,18 @@ static hipError_t launch_mix_t(const MixArgs& a, hipStream_t stream) {
 template <int NH, int CP, int WAVES, bool DX, int NS = 1>
 static hipError_t launch_part_t(const MixArgs& a, hipStream_t stream) {
     using C = PartCfg<NH, CP, WAVES, NS>;
+    using CP_ = PartCfg<NH, CP, WAVES, NS, true>;  // padded tiles (their own row pitch)
     const int d = a.nope + a.pe;
     const int cpt = d / CP;
     const bool pad = a.nh != NH;
     const int tp = pad ? C::tokens_per_tile(a.nh, a.pe) : 1;
     const int64_t n_tiles = (a.sq + tp - 1) / tp * cpt;
-    const size_t lds = C::lds_bytes(a.nope, a.pe, tp);
+    const size_t lds = pad ? CP_::lds_bytes(a.nope, a.pe, tp) : C::lds_bytes(a.nope, a.pe, tp);
     auto kern = pad ? mix_part_kernel<NH, CP, WAVES, DX, NS, true> : mix_part_kernel<NH, CP, WAVES, DX, NS, false>;
     static AttrPerDevice attr[2];
     const hipError_t ae = attr[pad].ensure([&] {
-        size_t lds_max = C::lds_bytes(8, CP) + (size_t)C::NT * 16;  // largest: pe = CP with the scratch
+        // largest: pe = CP with the scratch
+        size_t lds_max = (pad ? CP_::lds_bytes(8, CP) : C::lds_bytes(8, CP)) + (size_t)C::NT * 16;
         if (lds_max > kMaxLds) lds_max = kMaxLds;  // shapes beyond it are not routed here
         if (lds_max <= 65536) return hipSuccess;
         return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
