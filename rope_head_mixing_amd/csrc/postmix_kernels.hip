@@ -1479,9 +1479,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 12 ? 3 : 4) void bwd_fused_ker
     const int gb = C::SPLIT ? 2 * ((vs / C::NB) % (C::NB / 2)) : tile / C::NB;
     const int hb = C::SPLIT ? vs % C::NB : tile % C::NB;
     const int dkset = C::SPLIT ? vs / C::DW_PER_KSET : 0;
-    // DST (64 rows): the dx waves own M-block pairs (mb, mb + 1) of one
-    // N-block instead, and store their own dO rows (below)
-    static_assert(!DST || (C::SPLIT && C::NB == 2), "direct dO stores: 64 rows split by gradient");
+    // DST: the dx waves store their own dO rows (below); at 64 rows they
+    // then own M-block pairs (mb, mb + 1) of one N-block
+    static_assert(!DST || C::SPLIT, "direct dO stores: waves split by gradient");
+    constexpr int DXW = C::NB == 2 ? 2 : C::DXM;  // DST: M-blocks per dx wave
     const int mb = C::SPLIT ? (C::NB == 2 ? (DST ? 2 * (vs >> 1) : vs) : C::DXM * (vs / C::NB)) : wave % C::MBC;
     const int nb = C::SPLIT ? (C::NB == 2 ? (DST ? (vs & 1) : 0) : vs % C::NB) : wave / C::MBC;
     // offsets into a chunk's cos/sin rows of the tokens of this lane's dW row
@@ -1869,30 +1870,36 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 12 ? 3 : 4) void bwd_fused_ker
             for (int e = 0; e < 4; ++e) f[e] = __float_as_uint(keep[kb >> 2][4 * (kb & 3) + e]);
             return as_bf16x8(f);
         };
-        if (!C::SPLIT) {
-            dx_block(mb, [&](int kb) { return wf[C::SPLIT ? 0 : kb]; });
-        } else if (!dw_role && C::NB == 2 && DST) {
-            // 64 rows, direct stores: M-blocks mb, mb + 1 of N-block nb, then
-            // this wave's own dO rows (32 rows x 64 channels: whole 128-byte
-            // lines that no other wave writes) from its dO buffer columns to
-            // HBM, here in the compute phase, where the dx waves would
-            // otherwise wait for the dW waves; no store phase.  Each lane
-            // reads back what lanes of this wave wrote: LDS accesses of one
-            // wave complete in order, and the fence keeps the compiler from
-            // moving them.
-            dx_block(mb, kept);
-            dx_block(mb + 1, kept);
+        // DST: this dx wave's own dO rows (32 rows of N-block nb x the 32*DXW
+        // channels of its M-blocks: whole lines that no other wave writes)
+        // from its dO buffer columns to HBM, here in the compute phase, where
+        // the dx waves would otherwise wait for the dW waves; no store phase.
+        // Each lane reads back what lanes of this wave wrote: LDS accesses of
+        // one wave complete in order, and the fences keep the compiler from
+        // moving them.
+        auto store_own_dO = [&]() {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            constexpr int LPR = 4 * DXW, RPI = 64 / LPR;  // lanes per row, rows per instruction
             const int rows_k = chunk_rows(k);
             uint16_t* const outs = dO + s * nh * (int64_t)d + c_base;
+            int ln = lane;  // opaque at 96 rows, as in load_chunk
+            if (C::W_IN_DOL) asm volatile("" : "+v"(ln));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 32 * nb + 8 * j + (lane >> 3), cl = 32 * mb + 8 * (lane & 7);
+            for (int j = 0; j < 32 / RPI; ++j) {
+                const int row = 32 * nb + RPI * j + ln / LPR, cl = 32 * mb + 8 * (ln % LPR);
                 if (PAD && row >= rows_k) continue;  // padding rows
                 const u32x4 o = *reinterpret_cast<const u32x4*>(dol + row * C::DPITCH + cl);
                 __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(outs + row * (int64_t)d + cl));
             }
+        };
+        if (!C::SPLIT) {
+            dx_block(mb, [&](int kb) { return wf[C::SPLIT ? 0 : kb]; });
+        } else if (!dw_role && C::NB == 2 && DST) {
+            // 64 rows, direct stores: M-blocks mb, mb + 1 of N-block nb
+            dx_block(mb, kept);
+            dx_block(mb + 1, kept);
+            store_own_dO();
         } else if (!dw_role && C::NB == 2) {
             // 64 rows: M-block mb for both N-blocks from one read of its A
             // fragments; each block's MFMA inputs and k order are the
@@ -1937,9 +1944,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 12 ? 3 : 4) void bwd_fused_ker
 #pragma unroll
                 for (int kb = 0; kb < C::KB; ++kb) af[kb] = an[kb];
             }
+            if (DST) store_own_dO();
         } else if (!dw_role) {
 #pragma unroll
             for (int i = 0; i < C::DXM; ++i) dx_block(mb + i, kept);
+            if (DST) store_own_dO();
         }
         __syncthreads();  // dY/O buffers free; dO and the pe scratch complete
         if (k + 1 < nchunks) {
@@ -2877,21 +2886,28 @@ static hipError_t launch_bwd_fused_t(const MixArgs& mx, const DwArgs& a, int64_t
     constexpr bool PS_OK = NH == 128;
     const int vh = a.pe / 8;  // its tasks per row: a power of two
     const bool ps = PS_OK && a.pe > 0 && (vh & (vh - 1)) == 0 && C::lds_bytes(a.nope, a.pe, rgt, true) <= kMaxLds;
-    // Direct dO stores (64 rows split by gradient): the dx waves' dO rows are a
+    // Direct dO stores (waves split by gradient): the dx waves' dO rows are a
     // plain copy (pe rotated in registers or absent) and every paired pe
-    // block's partner columns lie in the same wave's 64 channels
-    constexpr bool DST_OK = NH == 64 && C::SPLIT;
+    // block's partner columns lie in the same wave's channels.  Against the
+    // store phase, in the benchmark's regime (settled): 64 rows 549-552 ->
+    // 533-534 us (510 -> 516), 96 rows at nh = 96, sq = 8192 522-528 ->
+    // 518-521 us (477 -> 456), 128 rows at nh = 128, sq = 8192 651-654 ->
+    // 619-624 us (593 -> 582).
+    constexpr bool DST_OK = C::SPLIT;
+    constexpr int DXW = C::NB == 2 ? 2 : C::DXM;  // M-blocks per dx wave with direct stores
+    const int L32 = (a.nope % CH) / 32;            // first pe M-block of its chunk
     const bool dst = DST_OK && (a.pe == 0 || (pe_pairs_in_blocks(a.nope, a.pe) &&
-                                              (a.pe == 32 || (a.pe == 64 && a.nope % 64 == 0))));
-    const int mode = ps ? 1 : dst ? 2 : 0;
-    auto kern = pad ? (ps    ? bwd_fused_kernel<NH, CH, WAVES, true, PS_OK, false>
-                       : dst ? bwd_fused_kernel<NH, CH, WAVES, true, false, DST_OK>
-                             : bwd_fused_kernel<NH, CH, WAVES, true, false, false>)
-                    : (ps    ? bwd_fused_kernel<NH, CH, WAVES, false, PS_OK, false>
-                       : dst ? bwd_fused_kernel<NH, CH, WAVES, false, false, DST_OK>
-                             : bwd_fused_kernel<NH, CH, WAVES, false, false, false>);
-    static AttrPerDevice attr[2][3];
-    const hipError_t ae = attr[pad][mode].ensure([&] {
+                                              L32 / DXW == (L32 + a.pe / 32 - 1) / DXW));
+    auto kern = pad ? (ps ? (dst ? bwd_fused_kernel<NH, CH, WAVES, true, PS_OK, DST_OK>
+                                 : bwd_fused_kernel<NH, CH, WAVES, true, PS_OK, false>)
+                          : (dst ? bwd_fused_kernel<NH, CH, WAVES, true, false, DST_OK>
+                                 : bwd_fused_kernel<NH, CH, WAVES, true, false, false>))
+                    : (ps ? (dst ? bwd_fused_kernel<NH, CH, WAVES, false, PS_OK, DST_OK>
+                                 : bwd_fused_kernel<NH, CH, WAVES, false, PS_OK, false>)
+                          : (dst ? bwd_fused_kernel<NH, CH, WAVES, false, false, DST_OK>
+                                 : bwd_fused_kernel<NH, CH, WAVES, false, false, false>));
+    static AttrPerDevice attr[2][2][2];
+    const hipError_t ae = attr[pad][ps][dst].ensure([&] {
         size_t lds_max = C::lds_bytes(8, 128, C::RG_MAX, true);  // largest: pe = 128 with the scratch
         if (lds_max > kMaxLds) lds_max = kMaxLds;
         return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
