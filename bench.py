@@ -36,34 +36,34 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # kernels behind each op at nh=64, d=512 (tiled path)
 KERNELS_NH64 = {
     "fwd": "mix_part_kernel<64, 256, 8, false, 1, false>",
-    "bwd": "bwd_fused_kernel<64, 256, 16, false, false> + dw_reduce_kernel",
+    "bwd": "bwd_fused_kernel<64, 256, 16, false, false, true> + dw_reduce_kernel",
     "bwd_dx": "mix_part_kernel<64, 256, 8, true, 1, false>",
     "bwd_dw": "dw_chunk_kernel<64, 128, false> + dw_reduce_kernel",
 }
 # the same at nh=3, d=512 (head-count sweep workload: 21 tokens per 64-row tile)
 KERNELS_NH3 = {
     "fwd": "mix_part_kernel<64, 256, 8, false, 1, true>",
-    "bwd": "bwd_fused_kernel<64, 256, 16, true, false> + dw_reduce_kernel",
+    "bwd": "bwd_fused_kernel<64, 256, 16, true, false, true> + dw_reduce_kernel",
     "bwd_dx": "mix_part_kernel<64, 256, 8, true, 1, true>",
     "bwd_dw": "dw_chunk_kernel<64, 128, true> + dw_reduce_kernel",
 }
 # the same at nh=128, d=512 (head-count sweep workload)
 KERNELS_NH128 = {
     "fwd": "mix_part_kernel<128, 256, 8, false, 4, false>",
-    "bwd": "bwd_fused_kernel<128, 128, 16, false, true> + dw_reduce_kernel",
+    "bwd": "bwd_fused_kernel<128, 128, 16, false, true, true> + dw_reduce_kernel",
     "bwd_dx": "mix_part_kernel<128, 256, 8, true, 4, false>",
     "bwd_dw": "dw_chunk_kernel<128, 128, false> + dw_reduce_kernel",
 }
 # nh=96 and nh=72 (96-row tiles and chunks; 72 with padding rows)
 KERNELS_NH96 = {
     "fwd": "mix_part_kernel<96, 256, 6, false, 3, false>",
-    "bwd": "bwd_fused_kernel<96, 256, 12, false, false> + dw_reduce_kernel",
+    "bwd": "bwd_fused_kernel<96, 256, 12, false, false, true> + dw_reduce_kernel",
     "bwd_dx": "mix_part_kernel<96, 256, 6, true, 3, false>",
     "bwd_dw": "dw_chunk_kernel<128, 128, true> + dw_reduce_kernel",
 }
 KERNELS_NH72 = {
     "fwd": "mix_part_kernel<96, 256, 6, false, 3, true>",
-    "bwd": "bwd_fused_kernel<96, 256, 12, true, false> + dw_reduce_kernel",
+    "bwd": "bwd_fused_kernel<96, 256, 12, true, false, true> + dw_reduce_kernel",
     "bwd_dx": "mix_part_kernel<96, 256, 6, true, 3, true>",
     "bwd_dw": "dw_chunk_kernel<128, 128, true> + dw_reduce_kernel",
 }
