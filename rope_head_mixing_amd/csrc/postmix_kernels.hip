@@ -1321,9 +1321,12 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
 //
 // One read of dY and O serves both gradients: fixed token blocks (a function
 // of the shape only), one fp32 weight-gradient partial each, and every
-// (token, CH-channel) chunk of dY and O is staged in LDS once.  CH = 256 with
-// 16 waves (one workgroup per CU) where d allows, else CH = 128 with 8 waves.
-// At 64 head rows, with KSET = WAVES/4 waves per dW output tile:
+// (token, CH-channel) chunk of dY and O is staged in LDS once.  Three
+// configurations split the waves by gradient (BwdCfg::SPLIT): 64 rows with
+// CH = 256 on 16 waves, 96 rows with CH = 256 on 12 waves, and 128 rows
+// with CH = 128 on 16 waves.  d not a multiple of 256 at 64 rows uses CH =
+// 128 on 8 waves with both gradients on every wave; there, with KSET =
+// WAVES/4 waves per dW output tile:
 //   - dW:  wave w owns output tile w%4 (g-block tile/2, h-block tile%2) over
 //          the k-steps t = w/4 (mod KSET); at the end of the block the KSET
 //          waves of a tile are added in k-set order (fixed);
@@ -1334,12 +1337,15 @@ __global__ __launch_bounds__((DwCfg<NH, CH>::NT)) void dw_chunk_kernel(
 //          results to an LDS output chunk (other pe layouts: an fp32 scratch,
 //          rotated in the store phase); the store phase writes dO rows with
 //          non-temporal stores.
+// The split configurations are described at BwdCfg.  With direct stores
+// (DST) their dx waves write their own dO rows to HBM in the compute phase
+// and there is no store phase.
 // The dx arithmetic (MFMA inputs, k order, rotation expression, tokens per
 // tile) is that of the token-part kernel, so dO is bitwise the same as
 // postmix_bwd_dx's.  64 head rows (nh <= 32: several tokens per chunk; up to
-// 64: padded), or 128 with pe rotated in registers (16 waves split by
-// gradient, BwdCfg::SPLIT); d a multiple of 128, pe <= 128 (all pe channels
-// in a token's last chunk).
+// 64: padded), 96 or 128 (padded above nh) with pe rotated in registers or
+// absent; d a multiple of 128, pe <= 128 (all pe channels in a token's last
+// chunk).
 // ---------------------------------------------------------------------------
 
 template <int NH, int CH, int WAVES>
@@ -1353,12 +1359,13 @@ struct BwdCfg {
     // fragments), in one shared array.  Against one dW tile and one dx block
     // on every wave with W read from LDS per use, the compute phase reads
     // ~40% less LDS.  Only pe rotated in registers.
-    // 64 rows on 16 waves split the same way: waves 0 .. 7 each own the two
+    // 64 rows on 16 waves split the same way: waves 8 .. 15 each own the two
     // tiles of one h-block (g-blocks 0 and 1) over one of four k-sets, so one
-    // O fragment (and one rotated pe operand) serves two MFMAs; waves 8 .. 15
+    // O fragment (and one rotated pe operand) serves two MFMAs; waves 0 .. 7
     // each own one dx M-block for both N-blocks, so its transposed dY
-    // fragments are read once for two MFMAs.  Against a tile and a dx block on
-    // every wave, the compute phase reads a third less LDS per chunk.
+    // fragments are read once for two MFMAs, or, with direct dO stores, an
+    // M-block pair of one N-block.  Against a tile and a dx block on every
+    // wave, the compute phase reads a third less LDS per chunk.
     // 96 rows on 12 waves (one workgroup per CU, 168 registers a wave) split
     // the same way: waves 0 .. 5 each own the three tiles of one h-block
     // (g-blocks 0, 1, 2) over one of two k-sets; waves 6 .. 11 each own four
