@@ -1514,23 +1514,36 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 12 ? 3 : 4) void bwd_fused_ker
     int64_t s_end = (tb + 1) * ngroups / nbt * tp;
     if (s_end > sq) s_end = sq;
     const int p0 = (int)((int64_t)y * cpt / spans), cps = (int)((int64_t)(y + 1) * cpt / spans) - p0;
-    const int nchunks = (int)((s_end - s_begin + tp - 1) / tp) * cps;
+    // At 96 and 128 rows token block tb takes the groups tb, tb + B, tb + 2B,
+    // ... instead (about the same count), so the blocks running at once work
+    // on neighbouring tokens: nh = 128, sq = 8192 585 -> 569 us settled
+    // (621 -> 618 in the benchmark's regime), nh = 96 460 -> 456 us.  At 64
+    // rows contiguous ranges measured faster (517 against 523 us settled).
+    constexpr bool kStridedTokens = NH >= 96;
+    const int ngr = kStridedTokens ? (tb < ngroups ? (int)((ngroups - 1 - tb) / nbt + 1) : 0)
+                                   : (int)((s_end - s_begin + tp - 1) / tp);
+    auto group_tok = [&](int j) -> int64_t {  // first token of the block's j-th group
+        return kStridedTokens ? (tb + nbt * (int64_t)j) * tp : s_begin + (int64_t)j * tp;
+    };
+    const int64_t s_lim = kStridedTokens ? sq : s_end;  // tokens of a group end below this
+    const int nchunks = ngr * cps;
 
     u32x4 v[C::VPT];
-    // cos and sin rows of tokens s0 .. s0+rgt-1 (within the block) -> LDS
-    // buffer `buf`; read once per rgt tokens instead of once per chunk.  Rows
-    // past the last token are zeros: the padding rows of a partial chunk
-    // rotate zeros with them, and their products must stay exact zeros.
-    auto load_rope_group = [&](int64_t s0, int buf) {
+    // cos and sin rows of the rgt tokens of groups j0, j0 + 1, .. of the
+    // block -> LDS buffer `buf`; read once per rgt tokens instead of once per
+    // chunk.  Rows past the last token are zeros: the padding rows of a
+    // partial chunk rotate zeros with them, and their products must stay
+    // exact zeros.
+    auto load_rope_group = [&](int j0, int buf) {
         float* const rg = rope_g + (C::NBUF == 2 ? buf : 0) * rgt * pe;
-        int64_t n = s_end - s0;
-        if (n > rgt) n = rgt;
         const int q4 = pe >> 2, half4 = pe >> 3;  // f32x4 per token row (cos + sin), per table row
         for (int idx = tid; idx < rgt * q4; idx += C::NT) {
             const int t = idx / q4, q = idx - t * q4;
+            const int jt = j0 + t / tp;                 // the row's group
+            const int64_t st = group_tok(jt) + t % tp;  // and token
             f32x4 x = {0.f, 0.f, 0.f, 0.f};
-            if (t < n) {
-                const int64_t prow = table_row(positions, s0 + t, table_rows);
+            if (jt < ngr && st < s_lim) {
+                const int64_t prow = table_row(positions, st, table_rows);
                 const float* tab = q < half4 ? rcos : rsin;
                 const int qq = q < half4 ? q : q - half4;
                 x = reinterpret_cast<const f32x4*>(tab + prow * h2)[qq];
@@ -1538,10 +1551,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 12 ? 3 : 4) void bwd_fused_ker
             reinterpret_cast<f32x4*>(rg + t * pe)[q] = x;
         }
     };
-    // head rows of chunk k backed by tokens < s_end
+    // head rows of chunk k backed by tokens below s_lim
     auto chunk_rows = [&](int k) -> int {
         if (!PAD) return NH;
-        const int64_t left = s_end - (s_begin + (int64_t)(k / cps) * tp);
+        const int64_t left = s_lim - group_tok(k / cps);
         return (int)(left < tp ? left : tp) * nh;
     };
     // The loads are unconditional: padding rows re-read the chunk's last row
@@ -1550,7 +1563,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 12 ? 3 : 4) void bwd_fused_ker
     // for every load in flight (scratch and global loads share one counter),
     // which serialises the prefetch.  In-chunk offsets fit 32 bits (d <= 2^24).
     auto load_chunk = [&](int k) {
-        const int64_t s = s_begin + (int64_t)(k / cps) * tp;  // first token of the chunk
+        const int64_t s = group_tok(k / cps);  // first token of the chunk
         const int part = p0 + k % cps;
         const int rows = chunk_rows(k);
         const int64_t rowbase = s * nh * (int64_t)d + part * CH;
@@ -1589,7 +1602,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 12 ? 3 : 4) void bwd_fused_ker
         }
     };
     if (nchunks > 0) load_chunk(0);
-    if (!C::AUX_OVERLAY && pe > 0 && nchunks > 0) load_rope_group(s_begin, 0);
+    if (!C::AUX_OVERLAY && pe > 0 && nchunks > 0) load_rope_group(0, 0);
 
     // W -> LDS -> this wave's dx B operand (B[k=g][n=h] = W[g][h], N-block nb).
     // SPLIT stages W transposed, [h][g]: a lane's B fragment (column h, 8
@@ -1641,7 +1654,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 12 ? 3 : 4) void bwd_fused_ker
         }
     }
     __syncthreads();  // W's LDS becomes the pe scratch (or the cos/sin rows, or dO)
-    if (C::AUX_OVERLAY && pe > 0 && nchunks > 0) load_rope_group(s_begin, 0);
+    if (C::AUX_OVERLAY && pe > 0 && nchunks > 0) load_rope_group(0, 0);
 
     f32x16 acc_w;
 #pragma unroll
@@ -1709,7 +1722,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 12 ? 3 : 4) void bwd_fused_ker
         __syncthreads();
     }
     for (int k = 0; k < nchunks; ++k) {
-        const int64_t s = s_begin + (int64_t)(k / cps) * tp;  // first token of the chunk
+        const int64_t s = group_tok(k / cps);  // first token of the chunk
         const int part = p0 + k % cps;
         const int c_base = part * CH;
         const bool chunk_pe = pe > 0 && c_base + CH > nope;
@@ -1964,7 +1977,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 12 ? 3 : 4) void bwd_fused_ker
             // waiting for the table rows waits for nothing else in flight
             // but chunk k+1, which the staging needs anyway
             const int tok1 = ((k + 1) / cps) * tp;
-            if (pe > 0 && (k + 1) % cps == 0 && tok1 % rgt == 0) load_rope_group(s_begin + tok1, (tok1 / rgt) & 1);
+            if (pe > 0 && (k + 1) % cps == 0 && tok1 % rgt == 0) load_rope_group(tok1 / tp, (tok1 / rgt) & 1);
             stage_chunk(k + 1);
             if (k + 2 < nchunks) load_chunk(k + 2);  // in flight during two compute phases
             if (PS && chunk_has_pe(k + 1)) {
