@@ -779,6 +779,17 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
                 v[j] = u32x4{0u, 0u, 0u, 0u};
         }
     };
+    // W's loads go out before the tile's: loads complete in issue order, so
+    // W issued behind the tile made the W setup (LDS writes, two barriers,
+    // fragment reads) wait for the whole tile instead of overlapping it
+    u32x4 wv[PAD ? 1 : C::WVPT];
+    if (!PAD) {
+#pragma unroll
+        for (int j = 0; j < C::WVPT; ++j) {
+            const int q = j * C::NT + tid;
+            if (q < NH * C::WVPR) wv[j] = reinterpret_cast<const u32x4*>(W)[q];
+        }
+    }
     if (t < n_tiles) load_tile(t);  // the tile's loads overlap the W setup
 
     // setup: W -> LDS -> B operand in registers
@@ -788,7 +799,7 @@ __global__ __launch_bounds__(64 * WAVES) void mix_part_kernel(
             const int q = j * C::NT + tid;
             if (q < NH * C::WVPR) {
                 const int row = q / C::WVPR, c8 = q % C::WVPR;
-                *reinterpret_cast<u32x4*>(wl + row * C::WPITCH + 8 * c8) = reinterpret_cast<const u32x4*>(W)[q];
+                *reinterpret_cast<u32x4*>(wl + row * C::WPITCH + 8 * c8) = wv[j];
             }
         }
     } else {  // zero the padded rows, then scatter W's nh*nh elements (16-byte loads when aligned)
