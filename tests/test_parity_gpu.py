@@ -237,6 +237,13 @@ def test_tiled_and_general_kernels_agree(sq, nh, nope, pe):
     (4800, 64, 192, 64, 11),    # 600 blocks of 8 tokens -> 512 blocks of 9 or 10
     (1200, 96, 192, 64, 5),     # 300 blocks of 4 tokens -> 256 blocks of 4 or 5 (96-row chunks);
                                 # the separate weight gradient's 300 blocks -> 256 as well
+    # several rounds of blocks per CU, with fewer tokens per block than a
+    # cos/sin group (one partial group per block)
+    (4096, 64, 448, 64, 3),     # 1024 blocks of 4 tokens: four rounds
+    (3840, 64, 448, 64, 5),     # 960 blocks of 4 tokens: the last round three quarters full
+    (8192, 64, 192, 64, 1),     # 1024 blocks of 8 tokens, d = 256
+    (2048, 128, 448, 64, 3),    # nh = 128: 512 blocks of 4 strided tokens
+    (4096, 128, 192, 64, 7),    # nh = 128, d = 256: 512 blocks of 8 strided tokens
 ])
 def test_fused_backward_matches_oracle_and_separate_calls(sq, nh, nope, pe, off):
     c = synthetic.case(sq, nh, nope, pe, seed=4000 + sq, pos_offset=off)
