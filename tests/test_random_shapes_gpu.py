@@ -6,7 +6,8 @@ draws head counts from 1 to 128 (padded rows, several tokens per tile, 96- and
 128-row tiles), channel splits with and without d a multiple of 128 (tiled and
 general kernels), pe from 0 to 256 and short ragged token counts, and eight
 more with 1100 to 4000 tokens, where the token blocks are rounded to whole
-rounds and spread evenly.  Each shape
+rounds and spread evenly, and forty more drawn per head-count band with
+rows up to 1280 channels.  Each shape
 runs the forward, dx, dW and the single-call backward, each checked against
 the oracle, and the single-call dO must equal postmix_bwd_dx's bit for bit.
 Head counts start at one: a single dW entry may cancel to far below the sum
@@ -81,4 +82,28 @@ def _large_shapes(n: int, seed: int = 20261203):
 
 @pytest.mark.parametrize("sq,nh,nope,pe,off", _large_shapes(8))
 def test_random_shape_many_blocks(sq, nh, nope, pe, off):
+    test_random_shape(sq, nh, nope, pe, off)
+
+
+def _banded_shapes(per_band: int = 8, seed: int = 20261204):
+    """Eight shapes in each head-count band ([1, 4] fp32 small-head kernels,
+    [5, 32] token-packed tiles, [33, 64], [65, 96], [97, 128]), with rows up
+    to 1280 channels: nope a multiple of 8 in [0, 1024], pe a multiple of 16
+    in [0, 256] (nope + pe > 0), sq in [1, 64], positions offset by [0, 40000)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for lo, hi in [(1, 4), (5, 32), (33, 64), (65, 96), (97, 128)]:
+        for _ in range(per_band):
+            nh = int(rng.integers(lo, hi + 1))
+            while True:
+                nope = 8 * int(rng.integers(0, 129))
+                pe = 16 * int(rng.integers(0, 17))
+                if nope + pe > 0:
+                    break
+            out.append((int(rng.integers(1, 65)), nh, nope, pe, int(rng.integers(0, 40000))))
+    return out
+
+
+@pytest.mark.parametrize("sq,nh,nope,pe,off", _banded_shapes())
+def test_banded_random_shape(sq, nh, nope, pe, off):
     test_random_shape(sq, nh, nope, pe, off)
