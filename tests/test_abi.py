@@ -454,7 +454,20 @@ def test_benchmark_kernel_names_exist_in_the_library():
     if shutil.which("nm") is None:
         pytest.skip("nm not available")
     out = subprocess.run(["nm", "-C", pm.LIB_PATH], capture_output=True, text=True, check=True).stdout
-    for table in (bench.KERNELS_NH64, bench.KERNELS_NH3, bench.KERNELS_NH128):
+    for workload, table in bench.KERNELS_BY_WORKLOAD.items():
         for op, names in table.items():
             for name in (n.strip() for n in names.split("+")):
-                assert f"pm::{name}(" in out, f"{op}: kernel {name!r} not in {pm.LIB_PATH}"
+                assert f"pm::{name}(" in out, f"{workload} {op}: kernel {name!r} not in {pm.LIB_PATH}"
+
+
+def test_benchmark_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU; asked for more it says so and exits non-zero
+    before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert r.stdout == ""
+    assert "exactly one GPU" in r.stderr
